@@ -1,0 +1,142 @@
+/*
+ * kda.h -- C ABI of libkda, the MI355X (gfx950) chunked forward of Kimi Delta
+ * Attention.
+ *
+ * Source of the operation: FlashKDA pages. "Core Kernel API / flash_kda.fwd"
+ * (ccm-staging.vinena.studio, FlashKDA Delta Attention skill) gives the call
+ *   fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+ *       initial_state=None, final_state=None, cu_seqlens=None);
+ * "Kernel API and Constraints" (trend.ondo.sh, MoonshotAI/FlashKDA) fixes
+ * K = V = 128, cu_seqlens only with B = 1, and initial/final states that are
+ * bf16 or fp32 or absent and of one dtype; the summary paragraph of the
+ * ccm-staging page fixes bf16 activations and describes varlen packing.
+ *
+ * The pages print no formula. libkda computes, per sequence n and head h, the
+ * gated delta rule with per-channel decay along the key axis:
+ *   q^ = q / sqrt(|q|^2 + 1e-6),  k^ = k / sqrt(|k|^2 + 1e-6)
+ *   log a_c = max(-exp(A_log[h]) * softplus(g_c + dt_bias[h,c]), lower_bound)
+ *   S_t = (I - beta_t k^ k^T) Diag(a_t) S_{t-1} + beta_t k^ v_t^T   (S is K x V)
+ *   out_t = scale * S_t^T q^
+ * evaluated chunkwise (64 tokens per chunk) on the GPU.
+ *
+ * Conventions for every entry point:
+ *  - Device pointers unless stated otherwise; all buffers belong to the caller.
+ *    libkda never allocates, frees or retains device memory.
+ *  - Activations are row-major contiguous:
+ *      q, k, g : bf16 [B, T, H, 128]      v, out : bf16 [B, T, H, 128]
+ *      beta    : bf16 [B, T, H]           A_log  : fp32 [H]
+ *      dt_bias : fp32 [H, 128]
+ *      initial_state, final_state : [N, H, 128(K), 128(V)], bf16 or fp32,
+ *                                   S[n][h][k][v] with o = S^T q over k.
+ *    With cu_seqlens (int32 [N+1], device, sorted, cu[0] = 0, cu[N] = T) the
+ *    batch is B = 1 and sequence n owns tokens [cu[n], cu[n+1]); otherwise
+ *    N = B and sequence n is batch row n.
+ *  - Calls are asynchronous on `stream`; nothing synchronises the host and
+ *    cu_seqlens is never read on the host (its validity is a precondition).
+ *  - Errors are detected before anything is enqueued and returned as a
+ *    kda_status; on KDA_ERR_HIP the contents of out/final_state are undefined.
+ *  - The library is stateless apart from the optional profiling switch and is
+ *    safe to call from several host threads on different streams.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef KDA_API
+#define KDA_API __attribute__((visibility("default")))
+#endif
+
+/* Status codes returned by kda_fwd. */
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    KDA_ERR_HEAD_DIM = 2,    /* K != 128 or V != 128                               */
+    KDA_ERR_SHAPE = 3,       /* B, T, H <= 0, num_seqs <= 0 with cu_seqlens, or
+                                B != 1 with cu_seqlens                             */
+    KDA_ERR_STATE_DTYPE = 4, /* state_dtype inconsistent with the state pointers   */
+    KDA_ERR_ARG = 5,         /* scale or lower_bound non-finite, lower_bound > 0, or
+                                lower_bound < KDA_LOWER_BOUND_MIN                 */
+    KDA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than kda_fwd_workspace_size */
+    KDA_ERR_ALIAS = 7,       /* out overlaps an input, or the states overlap only
+                                partially                                          */
+    KDA_ERR_HIP = 8          /* a HIP launch/runtime error after validation         */
+} kda_status;
+
+/* dtype of initial_state / final_state (one dtype for both). */
+typedef enum {
+    KDA_STATE_NONE = 0,      /* both state pointers NULL                            */
+    KDA_STATE_BF16 = 1,
+    KDA_STATE_FP32 = 2
+} kda_state_dtype;
+
+/* Most negative lower_bound the chunked kernels evaluate exactly. Inside one
+ * 16-token sub-chunk the decay factors are anchored at its middle token, so the
+ * largest factor is exp(8 * |lower_bound|); -10 keeps it below the bf16/fp32
+ * range (exp(88.7)). Smaller bounds are rejected with KDA_ERR_ARG. */
+#define KDA_LOWER_BOUND_MIN (-10.0f)
+
+/*
+ * kda_fwd -- chunked KDA forward (the flash_kda.fwd call of the pages).
+ *
+ *  q, k, v, g, beta : bf16 inputs, layouts above; must not overlap `out`.
+ *  scale            : multiplies the output only (finite).
+ *  out              : bf16 [B, T, H, 128], written in full (round to nearest even).
+ *  A_log, dt_bias   : fp32 gate parameters.
+ *  lower_bound      : clamp of log a in natural-log units, in
+ *                     [KDA_LOWER_BOUND_MIN, 0]; 0 means no decay.
+ *  initial_state    : NULL (zero state) or [N, H, 128, 128] of state_dtype.
+ *  final_state      : NULL (not returned) or [N, H, 128, 128] of state_dtype;
+ *                     receives S after the last token of each sequence (bf16 is
+ *                     rounded to nearest even from the fp32 state). It may be
+ *                     the same pointer as initial_state (in-place update) but
+ *                     may not overlap it otherwise.
+ *  state_dtype      : KDA_STATE_NONE iff both state pointers are NULL.
+ *  cu_seqlens       : NULL, or int32 [num_seqs + 1] on the device (B must be 1).
+ *  num_seqs         : number of packed sequences when cu_seqlens != NULL, else
+ *                     ignored (N = B).
+ *  B, T, H, K, V    : sizes; K and V must be 128. T counts packed tokens when
+ *                     cu_seqlens is given.
+ *  workspace        : device scratch of at least kda_fwd_workspace_size(...)
+ *                     bytes, 256-byte aligned; contents on entry are ignored and
+ *                     on return hold per-chunk intermediates (internal format).
+ *  stream           : hipStream_t (as void*) the kernels are enqueued on; NULL
+ *                     means the default stream.
+ */
+KDA_API int kda_fwd(const void *q, const void *k, const void *v, const void *g,
+            const void *beta, float scale, void *out, const float *A_log,
+            const float *dt_bias, float lower_bound, const void *initial_state,
+            void *final_state, int state_dtype, const int32_t *cu_seqlens,
+            int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
+            int64_t V, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_fwd_workspace_size -- bytes of workspace kda_fwd needs (host only).
+ *  num_seqs = 0 means no cu_seqlens (N = B); otherwise B must be 1 and T is the
+ *  packed token count. Returns 0 for invalid sizes.
+ */
+KDA_API size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t num_seqs);
+
+/* Static, NUL-terminated description of a kda_status code (host only). */
+KDA_API const char *kda_status_string(int status);
+
+/*
+ * Kernel-level timing for measurement tools (host only, not thread-safe).
+ *  kda_profile_enable(1) makes later kda_fwd calls bracket each kernel they
+ *  enqueue with hipEvents on the call's stream; kda_profile_enable(0) stops it.
+ *  kda_profile_read synchronises on the recorded events of the most recent
+ *  profiled call and writes up to `cap` kernel names and durations in ms;
+ *  it returns the number of kernels (or -1 if nothing was recorded).
+ */
+KDA_API int kda_profile_enable(int on);
+KDA_API int kda_profile_read(const char **names, float *ms, int cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -1,0 +1,191 @@
+"""MI355X-native chunked forward of Kimi Delta Attention (libkda).
+
+``fwd`` mirrors the ``flash_kda.fwd`` call named on the FlashKDA pages
+("Core Kernel API / flash_kda.fwd", ccm-staging page; constraints in
+"Kernel API and Constraints", trend.ondo.sh page): q, k, v, g, beta, scale, out,
+A_log, dt_bias, lower_bound, initial_state, final_state, cu_seqlens. It writes
+``out`` (and ``final_state``) in place.
+
+This module only marshals arguments: torch supplies device memory and the
+current stream, and every step of the computation runs in the HIP kernels of
+``libkda.so`` (built in-tree by ``build.py``). There is no fallback: if the
+library is missing, or no GPU is present, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["fwd", "workspace_size", "status_string", "library_path", "load_library",
+           "profile_enable", "profile_read", "KDA_LOWER_BOUND_MIN", "KdaError"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+_lib = None
+
+KDA_STATE_NONE, KDA_STATE_BF16, KDA_STATE_FP32 = 0, 1, 2
+KDA_LOWER_BOUND_MIN = -10.0
+EXPORTED = ("kda_fwd", "kda_fwd_workspace_size", "kda_status_string",
+            "kda_profile_enable", "kda_profile_read")
+
+
+class KdaError(RuntimeError):
+    """A HIP launch/runtime error reported by libkda (status KDA_ERR_HIP)."""
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("libkda.so is not built: run `python -c \"import __graft_entry__ as e; e.build()\"` "
+                           "or `python kimi_delta_attention_fwd_amd/build.py`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_float, P, P,
+                            ctypes.c_int, P, I64, I64, I64, I64, I64, I64, P, ctypes.c_size_t, P]
+    lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.kda_fwd_workspace_size.argtypes = [I64, I64, I64, I64]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_profile_enable.restype = ctypes.c_int
+    lib.kda_profile_enable.argtypes = [ctypes.c_int]
+    lib.kda_profile_read.restype = ctypes.c_int
+    lib.kda_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
+                                     ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return load_library().kda_status_string(int(code)).decode()
+
+
+def workspace_size(B: int, T: int, H: int, num_seqs: int = 0) -> int:
+    """Bytes of device workspace ``fwd`` needs (num_seqs = 0: no cu_seqlens)."""
+    return int(load_library().kda_fwd_workspace_size(int(B), int(T), int(H), int(num_seqs)))
+
+
+def profile_enable(on: bool = True) -> None:
+    rc = load_library().kda_profile_enable(1 if on else 0)
+    if rc != 0:
+        raise KdaError(status_string(rc))
+
+
+def profile_read(cap: int = 8):
+    """[(kernel name, ms)] of the most recent profiled ``fwd`` call (synchronises)."""
+    lib = load_library()
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = lib.kda_profile_read(names, ms, cap)
+    if n < 0:
+        return []
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]
+
+
+_ws_cache = {}
+
+
+def _workspace(nbytes, device):
+    import torch
+    key = (str(device), )
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+        initial_state=None, final_state=None, cu_seqlens=None, workspace=None):
+    """Chunked KDA forward on the current torch (ROCm) stream; fills ``out``.
+
+    q, k, g: bf16 [B, T, H, 128]; v, out: bf16 [B, T, H, 128]; beta: bf16
+    [B, T, H]; A_log: fp32 [H]; dt_bias: fp32 [H, 128]; lower_bound in
+    [KDA_LOWER_BOUND_MIN, 0]; initial_state / final_state: None or
+    [N, H, 128, 128] of one dtype (bf16 or fp32), final_state may be the same
+    tensor as initial_state; cu_seqlens: None or int32 [N + 1] on the device
+    (B must be 1). ``workspace`` (optional) is a uint8 device tensor of at least
+    ``workspace_size`` bytes; by default a cached buffer is used.
+    Raises ValueError for invalid arguments and KdaError for HIP failures.
+    """
+    import torch
+    lib = load_library()
+    bf16 = torch.bfloat16
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("out", out)):
+        if t.dtype != bf16:
+            raise ValueError("%s must be bfloat16 (got %s)" % (name, t.dtype))
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        if t.dtype != torch.float32:
+            raise ValueError("%s must be float32 (got %s)" % (name, t.dtype))
+    tensors = [q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens, workspace]
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, K]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    for name, t in (("k", k), ("g", g)):
+        if tuple(t.shape) != (B, T, H, K):
+            raise ValueError("%s must have the shape of q" % name)
+    if tuple(v.shape) != (B, T, H, V) or tuple(out.shape) != (B, T, H, V):
+        raise ValueError("v and out must be [B, T, H, V]")
+    if tuple(beta.shape) != (B, T, H):
+        raise ValueError("beta must be [B, T, H]")
+    if A_log.numel() != H or dt_bias.numel() != H * K:
+        raise ValueError("A_log must have H elements and dt_bias H*K")
+    num_seqs = 0
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise ValueError("cu_seqlens must be int32")
+        num_seqs = cu_seqlens.numel() - 1
+        if num_seqs <= 0:
+            raise ValueError("cu_seqlens must have at least 2 entries")
+    sd = KDA_STATE_NONE
+    states = [s for s in (initial_state, final_state) if s is not None]
+    if states:
+        dts = {s.dtype for s in states}
+        if len(dts) != 1:
+            raise ValueError("initial_state and final_state must have the same dtype")
+        dt = dts.pop()
+        if dt == torch.float32:
+            sd = KDA_STATE_FP32
+        elif dt == bf16:
+            sd = KDA_STATE_BF16
+        else:
+            raise ValueError("states must be bfloat16 or float32")
+        N = num_seqs if cu_seqlens is not None else B
+        for s in states:
+            if tuple(s.shape) != (N, H, K, V):
+                raise ValueError("states must be [N, H, K, V] = %s" % ((N, H, K, V),))
+    need = lib.kda_fwd_workspace_size(B, T, H, num_seqs)
+    if workspace is None:
+        ws = _workspace(need, q.device)
+    else:
+        ws = workspace
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+                     _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                     _ptr(final_state), sd, _ptr(cu_seqlens), num_seqs, B, T, H, K, V,
+                     _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
+    if rc == 0:
+        return out
+    msg = lib.kda_status_string(rc).decode()
+    if rc == 8:
+        raise KdaError(msg)
+    raise ValueError(msg)

@@ -1,0 +1,201 @@
+/*
+ * kda_api.cpp -- C ABI of libkda (declared in include/kda.h): argument
+ * validation, workspace carving and kernel launches on the caller's stream.
+ *
+ * The checks mirror the constraints the FlashKDA pages state for
+ * flash_kda.fwd ("Kernel API and Constraints", trend.ondo.sh page: K = V = 128,
+ * cu_seqlens only with B = 1, initial and final states bf16/fp32/None of one
+ * dtype; "Core Kernel API / flash_kda.fwd", ccm-staging page: the argument
+ * list). Everything is checked on the host before any HIP call, so every error
+ * path can be exercised without a GPU.
+ */
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+extern "C" hipError_t kda_launch_chunk_map(const int32_t *cu, int64_t nseq, int32_t *chunk_off, hipStream_t st);
+extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *v, const void *g,
+                                      const void *beta, const float *A_log, const float *dt_bias,
+                                      float scale, float lower_bound, const int32_t *cu,
+                                      const int32_t *chunk_off, int64_t nseq, int64_t T, int64_t H,
+                                      int64_t nslots, void *records, hipStream_t st);
+extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
+                                      int64_t nseq, int64_t T, int64_t H, void *out,
+                                      const void *init_state, void *final_state, int state_fp32,
+                                      hipStream_t st);
+
+namespace {
+
+struct Range {
+    uintptr_t lo, hi; /* [lo, hi) */
+};
+
+Range rng(const void *p, size_t bytes)
+{
+    const uintptr_t a = (uintptr_t)p;
+    return Range{a, a + bytes};
+}
+
+bool overlap(const Range &a, const Range &b)
+{
+    return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi;
+}
+
+/* ---- optional kernel timing ---- */
+constexpr int kMaxProf = 8;
+bool g_prof_on = false;
+int g_prof_n = -1;
+const char *g_prof_names[kMaxProf];
+hipEvent_t g_ev[kMaxProf][2];
+bool g_ev_made = false;
+
+struct ProfScope {
+    int idx;
+    hipStream_t st;
+    ProfScope(const char *name, hipStream_t s) : idx(-1), st(s)
+    {
+        if (!g_prof_on || g_prof_n >= kMaxProf) return;
+        idx = g_prof_n++;
+        g_prof_names[idx] = name;
+        hipEventRecord(g_ev[idx][0], st);
+    }
+    ~ProfScope()
+    {
+        if (idx >= 0) hipEventRecord(g_ev[idx][1], st);
+    }
+};
+
+} // namespace
+
+extern "C" const char *kda_status_string(int status)
+{
+    switch (status) {
+    case KDA_OK: return "KDA_OK: success";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+    case KDA_ERR_HEAD_DIM: return "KDA_ERR_HEAD_DIM: K and V must both be 128";
+    case KDA_ERR_SHAPE:
+        return "KDA_ERR_SHAPE: B, T, H must be positive; with cu_seqlens B must be 1 and num_seqs positive";
+    case KDA_ERR_STATE_DTYPE:
+        return "KDA_ERR_STATE_DTYPE: state_dtype must be NONE exactly when no state is given, else BF16 or FP32";
+    case KDA_ERR_ARG:
+        return "KDA_ERR_ARG: scale and lower_bound must be finite with -10 <= lower_bound <= 0";
+    case KDA_ERR_WORKSPACE:
+        return "KDA_ERR_WORKSPACE: workspace is NULL, not 256-byte aligned, or smaller than kda_fwd_workspace_size";
+    case KDA_ERR_ALIAS:
+        return "KDA_ERR_ALIAS: out/final_state/workspace overlap an input, or the states overlap partially";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch or runtime error occurred";
+    default: return "unknown kda status";
+    }
+}
+
+extern "C" size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t num_seqs)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || num_seqs < 0) return 0;
+    if (num_seqs > 0 && B != 1) return 0;
+    const int64_t nslots = kda_max_chunks(B, T, num_seqs);
+    return kda_chunk_map_bytes(num_seqs) + (size_t)nslots * (size_t)H * KDA_REC_BYTES;
+}
+
+extern "C" int kda_profile_enable(int on)
+{
+    if (on && !g_ev_made) {
+        for (int i = 0; i < kMaxProf; i++)
+            for (int j = 0; j < 2; j++)
+                if (hipEventCreate(&g_ev[i][j]) != hipSuccess) return KDA_ERR_HIP;
+        g_ev_made = true;
+    }
+    g_prof_on = on != 0;
+    return KDA_OK;
+}
+
+extern "C" int kda_profile_read(const char **names, float *ms, int cap)
+{
+    if (g_prof_n < 0) return -1;
+    for (int i = 0; i < g_prof_n && i < cap; i++) {
+        if (hipEventSynchronize(g_ev[i][1]) != hipSuccess) return -1;
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, g_ev[i][0], g_ev[i][1]) != hipSuccess) return -1;
+        if (names) names[i] = g_prof_names[i];
+        if (ms) ms[i] = t;
+    }
+    return g_prof_n;
+}
+
+extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                       float scale, void *out, const float *A_log, const float *dt_bias,
+                       float lower_bound, const void *initial_state, void *final_state,
+                       int state_dtype, const int32_t *cu_seqlens, int64_t num_seqs, int64_t B,
+                       int64_t T, int64_t H, int64_t K, int64_t V, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    /* ---- validation (host only, nothing enqueued yet) ---- */
+    if (K != KDA_DK || V != KDA_DV) return KDA_ERR_HEAD_DIM;
+    if (B <= 0 || T <= 0 || H <= 0) return KDA_ERR_SHAPE;
+    if (cu_seqlens && (B != 1 || num_seqs <= 0)) return KDA_ERR_SHAPE;
+    if (!q || !k || !v || !g || !beta || !out || !A_log || !dt_bias) return KDA_ERR_NULL;
+    if (state_dtype == KDA_STATE_NONE) {
+        if (initial_state || final_state) return KDA_ERR_STATE_DTYPE;
+    } else if (state_dtype == KDA_STATE_BF16 || state_dtype == KDA_STATE_FP32) {
+        if (!initial_state && !final_state) return KDA_ERR_STATE_DTYPE;
+    } else {
+        return KDA_ERR_STATE_DTYPE;
+    }
+    if (!std::isfinite(scale) || !std::isfinite(lower_bound) || lower_bound > 0.f ||
+        lower_bound < KDA_LOWER_BOUND_MIN)
+        return KDA_ERR_ARG;
+    const int64_t nseq_arg = cu_seqlens ? num_seqs : 0;
+    const size_t need = kda_fwd_workspace_size(B, T, H, nseq_arg);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return KDA_ERR_WORKSPACE;
+
+    const int64_t N = cu_seqlens ? num_seqs : B;
+    const size_t act = (size_t)B * T * H * KDA_DK * 2;
+    const size_t sbytes = (size_t)N * H * KDA_DK * KDA_DV * (state_dtype == KDA_STATE_FP32 ? 4 : 2);
+    const Range r_out = rng(out, act);
+    const Range inputs[] = {rng(q, act), rng(k, act), rng(v, act), rng(g, act),
+                            rng(beta, (size_t)B * T * H * 2), rng(A_log, (size_t)H * 4),
+                            rng(dt_bias, (size_t)H * KDA_DK * 4),
+                            rng(cu_seqlens, cu_seqlens ? (size_t)(num_seqs + 1) * 4 : 0),
+                            rng(initial_state, initial_state ? sbytes : 0)};
+    const Range r_fin = rng(final_state, final_state ? sbytes : 0);
+    const Range r_ws = rng(workspace, need);
+    for (const Range &in : inputs) {
+        if (overlap(r_out, in)) return KDA_ERR_ALIAS;
+        if (overlap(r_ws, in)) return KDA_ERR_ALIAS;
+        if (&in != &inputs[8] && overlap(r_fin, in)) return KDA_ERR_ALIAS;
+    }
+    if (overlap(r_out, r_fin) || overlap(r_out, r_ws) || overlap(r_fin, r_ws)) return KDA_ERR_ALIAS;
+    if (initial_state && final_state && initial_state != final_state && overlap(inputs[8], r_fin))
+        return KDA_ERR_ALIAS;
+
+    /* ---- launches ---- */
+    hipStream_t st = (hipStream_t)stream;
+    if (g_prof_on) g_prof_n = 0;
+    unsigned char *ws = (unsigned char *)workspace;
+    int32_t *chunk_off = nullptr;
+    if (cu_seqlens) {
+        chunk_off = (int32_t *)ws;
+        ProfScope ps("kda_chunk_map", st);
+        if (kda_launch_chunk_map(cu_seqlens, num_seqs, chunk_off, st) != hipSuccess) return KDA_ERR_HIP;
+    }
+    void *records = ws + kda_chunk_map_bytes(nseq_arg);
+    const int64_t nslots = kda_max_chunks(B, T, nseq_arg);
+    {
+        ProfScope ps("kda_prep", st);
+        if (kda_launch_prep(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound, cu_seqlens, chunk_off,
+                            N, T, H, nslots, records, st) != hipSuccess)
+            return KDA_ERR_HIP;
+    }
+    {
+        ProfScope ps("kda_scan", st);
+        if (kda_launch_scan(records, cu_seqlens, chunk_off, N, T, H, out,
+                            state_dtype == KDA_STATE_NONE ? nullptr : initial_state, final_state,
+                            state_dtype == KDA_STATE_FP32 ? 1 : 0, st) != hipSuccess)
+            return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}

@@ -1,0 +1,65 @@
+/*
+ * kda_internal.h -- layouts shared by the libkda kernels and host launcher.
+ * Not installed; the public interface is include/kda.h.
+ *
+ * Chunked evaluation (derived from the gated delta rule; the FlashKDA pages
+ * describe a chunked kernel for it without formulas). Per sequence and head,
+ * tokens are cut into chunks of 64 that restart at every sequence start. For a
+ * chunk of L <= 64 tokens with state S entering it and G = inclusive cumsum of
+ * log a over the chunk (per key channel):
+ *   A_rj = beta_r sum_c k^_r k^_j e^{G_r - G_j}   (j < r),   T = (I + A)^-1
+ *   W = T diag(beta) (K^ o e^G),   U = T diag(beta) V,   D = U - W S
+ *   P_rj = scale sum_c q^_r k^_j e^{G_r - G_j}   (j <= r)
+ *   Q' = scale (Q^ o e^G) - P W
+ *   out = Q' S + P U                  (= scale [(Q^ o e^G) S + P_unscaled D])
+ *   S  <- diag(e^{G_L}) S + (K^ o e^{G_L - G})^T D
+ * A "prep" kernel forms everything that does not depend on S for all chunks in
+ * parallel and stores it as a per-(chunk, head) record; a "scan" kernel walks
+ * the chunks of each (sequence, head) in order, keeping S in registers.
+ *
+ * Record operands are stored in the exact register layout of the gfx950
+ * v_mfma_f32_16x16x32_bf16 operands the scan issues, so every scan load is a
+ * contiguous 16-byte (or 32-byte) read per lane:
+ *   "fragment" = 64 lanes x 8 bf16 = 1 KiB. Lane l covers row (l % 16) of a
+ *   16-row tile; its 8 values cover the 32-wide contraction block in the order
+ *   kperm(g, i) = i < 4 ? 4g + i : 16 + 4g + (i - 4),  g = l / 16,
+ *   which is the order in which a pair of 16x16 fp32 accumulator tiles holds
+ *   rows (4g + e) -- so an accumulator pair converts to an operand in place.
+ */
+#ifndef KDA_INTERNAL_H
+#define KDA_INTERNAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#define KDA_CHUNK 64
+#define KDA_DK 128
+#define KDA_DV 128
+
+/* byte offsets inside one (chunk, head) record */
+#define KDA_REC_W 0          /* -W   : 16 fragments, index mt*4 + kb (mt: token tile, kb: key block) */
+#define KDA_REC_Q 16384      /* Q'   : 16 fragments, index mt*4 + kb                                  */
+#define KDA_REC_KT 32768     /* Kt^T : 16 fragments, index ct*2 + jb (ct: key tile, jb: token block) */
+#define KDA_REC_P 49152      /* P    : 6 fragments (lower triangle), index kda_pidx(mt, jb)           */
+#define KDA_REC_U 55296      /* U    : [8 value tiles][64 lanes][4 token tiles][4] bf16              */
+#define KDA_REC_GL 71680     /* e^{G_L}: 128 fp32, key-channel order                               */
+#define KDA_REC_BYTES 72192
+
+/* fragment index of P(mt, jb); only jb <= mt / 2 exists */
+#define KDA_PIDX(mt, jb) ((mt) < 2 ? (mt) : 2 + 2 * ((mt) - 2) + (jb))
+
+/* workspace = [chunk_off int32[N + 1], padded to 256 B][records] */
+static inline size_t kda_chunk_map_bytes(int64_t num_seqs)
+{
+    return num_seqs > 0 ? (size_t)(((num_seqs + 1) * 4 + 255) / 256 * 256) : 0;
+}
+
+/* upper bound on the number of chunks: exact without cu_seqlens */
+static inline int64_t kda_max_chunks(int64_t B, int64_t T, int64_t num_seqs)
+{
+    if (num_seqs > 0)
+        return T / KDA_CHUNK + num_seqs;
+    return B * ((T + KDA_CHUNK - 1) / KDA_CHUNK);
+}
+
+#endif

@@ -1,0 +1,679 @@
+/*
+ * kda_kernels.hip -- gfx950 kernels of the chunked Kimi Delta Attention forward.
+ *
+ *   kda_chunk_map_kernel : varlen chunk table (prefix sum of ceil(len / 64)).
+ *   kda_prep_kernel      : one workgroup per (chunk, head); gate, q/k L2 norm,
+ *                          in-chunk cumsum, tril A and P, T = (I + A)^-1 by
+ *                          forward substitution in LDS, W, U, Q', K~^T.
+ *   kda_scan_kernel      : one wave per (sequence, head, 16 value columns);
+ *                          the sequential chunk loop with the 128 x 16 slice of
+ *                          the fp32 state held in MFMA accumulators.
+ *
+ * The operation is the gated delta rule of the FlashKDA pages (ccm-staging
+ * page, "Core Kernel API / flash_kda.fwd"; trend.ondo.sh page, "Kernel API and
+ * Constraints"); the chunk algebra and the record layout are described in
+ * kda_internal.h.
+ *
+ * Decay factors never overflow: inside a 16-token sub-chunk both sides of the
+ * pairwise factor e^{G_r - G_j} are anchored at the sub-chunk's 8th token
+ * (|exponent| <= 8 |lower_bound|); across sub-chunks the query side is anchored
+ * at the start of its sub-chunk, the key side at the end of its own, and a
+ * per-channel bridge e^{B_i - B_{b+1}} <= 1 joins them, so every factor there
+ * is <= 1. Exponentials are taken base 2 (v_exp_f32) on log2-scaled sums.
+ */
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_internal.h"
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define LOG2E_F 1.4426950408889634f
+#define LN2_F 0.6931471805599453f
+
+namespace {
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+/* position inside a 32-wide contraction block of operand slot i of lane group g */
+__device__ __forceinline__ int kperm(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f2bf_bits(float x)
+{
+    __bf16 b = (__bf16)x; /* round to nearest even */
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x4 &a, const f32x4 &b)
+{
+    bf16x8 r;
+    r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
+    r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 pack8f(const float *x)
+{
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; i++) r[i] = (__bf16)x[i];
+    return r;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+/* inclusive prefix sum over the 16 lanes of a DPP row */
+__device__ __forceinline__ float row_scan16(float x)
+{
+    int v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true));
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true));
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true));
+    v = __float_as_int(x);
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true));
+    return x;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+/* sequence / chunk of a chunk slot; returns false for slots past the end */
+__device__ __forceinline__ bool locate_chunk(int64_t slot, const int32_t *cu, const int32_t *chunk_off,
+                                             int64_t nseq, int64_t T, int64_t &t0, int &L, int64_t &seq)
+{
+    if (cu == nullptr) {
+        const int64_t cps = (T + KDA_CHUNK - 1) / KDA_CHUNK;
+        seq = slot / cps;
+        const int64_t c = slot - seq * cps;
+        t0 = seq * T + c * KDA_CHUNK;
+        const int64_t rem = T - c * KDA_CHUNK;
+        L = (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
+        return true;
+    }
+    if (slot >= chunk_off[nseq]) return false;
+    int64_t lo = 0, hi = nseq - 1; /* largest n with chunk_off[n] <= slot */
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (chunk_off[mid] <= slot) lo = mid; else hi = mid - 1;
+    }
+    seq = lo;
+    const int64_t c = slot - chunk_off[lo];
+    t0 = cu[lo] + c * KDA_CHUNK;
+    const int64_t rem = cu[lo + 1] - t0;
+    L = (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
+    return true;
+}
+
+} // namespace
+
+/* ------------------------------------------------------------------------- */
+/* varlen chunk table: chunk_off[n] = sum_{m < n} ceil(len_m / 64)            */
+/* ------------------------------------------------------------------------- */
+extern "C" __global__ void __launch_bounds__(1024)
+kda_chunk_map_kernel(const int32_t *__restrict__ cu, int64_t nseq, int32_t *__restrict__ chunk_off)
+{
+    __shared__ int32_t s_wave[16];
+    __shared__ int32_t s_carry;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) { s_carry = 0; chunk_off[0] = 0; }
+    __syncthreads();
+    for (int64_t base = 0; base < nseq; base += 1024) {
+        const int64_t n = base + tid;
+        int32_t x = 0;
+        if (n < nseq) {
+            const int32_t len = cu[n + 1] - cu[n];
+            x = (len + KDA_CHUNK - 1) / KDA_CHUNK;
+        }
+        for (int d = 1; d < 64; d <<= 1) {
+            const int32_t y = __shfl_up(x, d);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) s_wave[wave] = x;
+        __syncthreads();
+        int32_t add = s_carry;
+        for (int w = 0; w < wave; w++) add += s_wave[w];
+        if (n < nseq) chunk_off[n + 1] = add + x;
+        __syncthreads();
+        if (tid == 1023) s_carry = add + x;
+        __syncthreads();
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* prep: one workgroup of 4 waves per (chunk slot, head)                       */
+/* ------------------------------------------------------------------------- */
+struct PrepShared {
+    float tot[4][KDA_DK];     /* in-sub-chunk inclusive cumsum at row 15 (log2 units) */
+    float mid[4][KDA_DK];     /* ... at row 7 (the anchor)                            */
+    float f_cm[4][KDA_DK];    /* 2^{mid}                                              */
+    float f_zt[4][KDA_DK];    /* 2^{tot - mid}                                        */
+    float f_b[4][KDA_DK];     /* 2^{B_w}, B_w = G before sub-chunk w                  */
+    float f_k[4][KDA_DK];     /* 2^{G_L - B_w - tot_w}                                */
+    float f_t[4][KDA_DK];     /* 2^{tot_w} (bridge factors)                           */
+    bf16x8 z[4][4][64];       /* key side of off-diagonal blocks, per sub-chunk       */
+    bf16x8 rt[8][2][64];      /* R = beta K^ e^G, transposed fragments (key tile, token block) */
+    bf16x8 vt[8][2][64];      /* beta V, transposed fragments (value tile, token block)        */
+    float a[KDA_CHUNK][KDA_CHUNK]; /* A (strictly lower)                              */
+    float t[KDA_CHUNK][KDA_CHUNK]; /* T = (I + A)^-1                                  */
+    float m[4][16][16];       /* per-wave 16x16 scratch                               */
+};
+
+extern "C" __global__ void __launch_bounds__(256)
+kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                const uint16_t *__restrict__ v, const uint16_t *__restrict__ gt,
+                const uint16_t *__restrict__ beta, const float *__restrict__ A_log,
+                const float *__restrict__ dt_bias, float scale, float lower_bound,
+                const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
+                int64_t nseq, int64_t T, int H, unsigned char *__restrict__ rec_base)
+{
+    __shared__ PrepShared sh;
+    const int64_t slot = blockIdx.x / H;
+    const int h = (int)(blockIdx.x - slot * H);
+    int64_t t0, seq;
+    int L;
+    if (!locate_chunk(slot, cu, chunk_off, nseq, T, t0, L, seq)) return;
+    unsigned char *rec = rec_base + ((size_t)slot * H + h) * KDA_REC_BYTES;
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, r16 = l & 15;
+    const int r = 16 * w + r16;
+    const bool valid = r < L;
+    const size_t row = (size_t)(t0 + (valid ? r : 0)) * H + h;
+
+    /* zero T (upper blocks stay zero) */
+    for (int i = tid; i < KDA_CHUNK * KDA_CHUNK; i += 256) (&sh.t[0][0])[i] = 0.f;
+
+    /* ---- load this lane's token row: 32 key channels kb*32 + kperm(g, i) ---- */
+    float qf[32], kf[32], la[32], vf[32];
+    const float bt = valid ? bf2f(beta[row]) : 0.f;
+    const float decay_rate = __expf(A_log[h]);
+    const float lb2 = lower_bound * LOG2E_F;
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) {
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            const int ch0 = 32 * kb + 16 * half + 4 * g;
+            const int j0 = kb * 8 + half * 4;
+            uint2 uq = make_uint2(0, 0), uk = uq, ug = uq, uv = uq;
+            if (valid) {
+                uq = *(const uint2 *)(q + row * KDA_DK + ch0);
+                uk = *(const uint2 *)(k + row * KDA_DK + ch0);
+                ug = *(const uint2 *)(gt + row * KDA_DK + ch0);
+                uv = *(const uint2 *)(v + row * KDA_DV + ch0);
+            }
+            const float4 db = *(const float4 *)(dt_bias + (size_t)h * KDA_DK + ch0);
+            const uint32_t wq[2] = {uq.x, uq.y}, wk[2] = {uk.x, uk.y}, wg[2] = {ug.x, ug.y}, wv[2] = {uv.x, uv.y};
+            const float dbs[4] = {db.x, db.y, db.z, db.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int sh16 = (e & 1) * 16;
+                qf[j0 + e] = bf2f((uint16_t)(wq[e >> 1] >> sh16));
+                kf[j0 + e] = bf2f((uint16_t)(wk[e >> 1] >> sh16));
+                vf[j0 + e] = bf2f((uint16_t)(wv[e >> 1] >> sh16));
+                const float x = bf2f((uint16_t)(wg[e >> 1] >> sh16)) + dbs[e];
+                /* softplus(x) = max(x, 0) + ln(1 + e^{-|x|}) */
+                const float sp = fmaxf(x, 0.f) + log2_fast(1.f + exp2_fast(-fabsf(x) * LOG2E_F)) * LN2_F;
+                const float l2 = fmaxf(-decay_rate * sp * LOG2E_F, lb2);
+                la[j0 + e] = valid ? l2 : 0.f; /* padded rows: no decay */
+            }
+        }
+    }
+    /* ---- L2 normalisation (scale folded into q) ---- */
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; j++) { sq += qf[j] * qf[j]; sk += kf[j] * kf[j]; }
+    sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
+    sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
+    const float iq = scale / sqrtf(sq + 1e-6f), ik = 1.f / sqrtf(sk + 1e-6f);
+#pragma unroll
+    for (int j = 0; j < 32; j++) { qf[j] *= iq; kf[j] *= ik; vf[j] *= bt; }
+
+    /* ---- in-sub-chunk inclusive cumsum of log2 a over the 16 tokens ---- */
+#pragma unroll
+    for (int j = 0; j < 32; j++) la[j] = row_scan16(la[j]);
+#pragma unroll
+    for (int j = 0; j < 32; j++) {
+        const int ch = 32 * (j >> 3) + kperm(g, j & 7);
+        if (r16 == 15) sh.tot[w][ch] = la[j];
+        if (r16 == 7) sh.mid[w][ch] = la[j];
+    }
+    __syncthreads();
+    /* ---- per (sub-chunk, channel) factors ---- */
+    for (int p = tid; p < 4 * KDA_DK; p += 256) {
+        const int ww = p >> 7, ch = p & 127;
+        float B = 0.f, GL = 0.f;
+        for (int m = 0; m < 4; m++) {
+            const float tm = sh.tot[m][ch];
+            if (m < ww) B += tm;
+            GL += tm;
+        }
+        const float tot = sh.tot[ww][ch], mid = sh.mid[ww][ch];
+        sh.f_cm[ww][ch] = exp2_fast(mid);
+        sh.f_zt[ww][ch] = exp2_fast(tot - mid);
+        sh.f_b[ww][ch] = exp2_fast(B);
+        sh.f_k[ww][ch] = exp2_fast(GL - B - tot);
+        sh.f_t[ww][ch] = exp2_fast(tot);
+        if (ww == 0) ((float *)(rec + KDA_REC_GL))[ch] = exp2_fast(GL);
+    }
+    __syncthreads();
+
+    /* ---- decay-scaled operands of this lane (R-form: lane = token) ---- */
+    bf16x8 xdk[4], xdq[4], yd[4], qt[4];
+    float xok[32], xoq[32];
+    {
+        float tmp_z[32], tmp_r[32], tmp_kt[32];
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            const int ch = 32 * (j >> 3) + kperm(g, j & 7);
+            const float mid = sh.mid[w][ch];
+            const float e1 = exp2_fast(la[j] - mid); /* e^{G_r - G_m} */
+            const float e2 = exp2_fast(mid - la[j]); /* e^{G_m - G_r} */
+            const float fcm = sh.f_cm[w][ch], fzt = sh.f_zt[w][ch], fb = sh.f_b[w][ch], fk = sh.f_k[w][ch];
+            const float dk = kf[j] * e1, dq = qf[j] * e1, ykv = kf[j] * e2;
+            xok[j] = dk * fcm;       /* k^ e^{c_r}: anchored at the sub-chunk start */
+            xoq[j] = dq * fcm;
+            tmp_z[j] = ykv * fzt;    /* k^ e^{tot - c_r}: anchored at the sub-chunk end */
+            tmp_r[j] = bt * xok[j] * fb;     /* beta k^ e^{G_r} */
+            tmp_kt[j] = tmp_z[j] * fk;       /* k^ e^{G_L - G_r} */
+            xdk[j >> 3][j & 7] = (__bf16)dk;
+            xdq[j >> 3][j & 7] = (__bf16)dq;
+            yd[j >> 3][j & 7] = (__bf16)ykv;
+            qt[j >> 3][j & 7] = (__bf16)(xoq[j] * fb); /* scale Q^ e^{G_r} */
+        }
+        /* key side of off-diagonal blocks, for later sub-chunks */
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) sh.z[w][kb][l] = pack8f(&tmp_z[kb * 8]);
+
+        /* transposes via MFMA with a 0/1 selector: R-form tile -> C-form tile */
+        bf16x8 sel[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+            for (int i = 0; i < 8; i++) sel[hh][i] = (__bf16)(kperm(g, i) == 16 * hh + r16 ? 1.f : 0.f);
+        const int jb = w >> 1, jh = w & 1;
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
+            const bf16x8 fr = pack8f(&tmp_r[kb * 8]);
+            const bf16x8 fv = pack8f(&vf[kb * 8]);
+            const bf16x8 fk = pack8f(&tmp_kt[kb * 8]);
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++) {
+                const int ct = 2 * kb + hh;
+                const f32x4 dr = mfma(fr, sel[hh], zero4());
+                const f32x4 dv = mfma(fv, sel[hh], zero4());
+                const f32x4 dkt = mfma(fk, sel[hh], zero4());
+                uint16_t *pr = (uint16_t *)&sh.rt[ct][jb][l] + 4 * jh;
+                uint16_t *pv = (uint16_t *)&sh.vt[ct][jb][l] + 4 * jh;
+                uint2 ur, uv2, uk;
+                ur.x = f2bf_bits(dr[0]) | ((uint32_t)f2bf_bits(dr[1]) << 16);
+                ur.y = f2bf_bits(dr[2]) | ((uint32_t)f2bf_bits(dr[3]) << 16);
+                uv2.x = f2bf_bits(dv[0]) | ((uint32_t)f2bf_bits(dv[1]) << 16);
+                uv2.y = f2bf_bits(dv[2]) | ((uint32_t)f2bf_bits(dv[3]) << 16);
+                uk.x = f2bf_bits(dkt[0]) | ((uint32_t)f2bf_bits(dkt[1]) << 16);
+                uk.y = f2bf_bits(dkt[2]) | ((uint32_t)f2bf_bits(dkt[3]) << 16);
+                *(uint2 *)pr = ur;
+                *(uint2 *)pv = uv2;
+                *(uint2 *)(rec + KDA_REC_KT + ((size_t)(ct * 2 + jb) * 64 + l) * 16 + jh * 8) = uk;
+            }
+        }
+    }
+    __syncthreads(); /* z, rt, vt visible */
+
+    /* ---- tril A and P for row block w (outputs lane = token r, regs = j) ---- */
+    f32x4 at[4], pt[4];
+#pragma unroll
+    for (int b = 0; b < 4; b++) { at[b] = zero4(); pt[b] = zero4(); }
+    f32x4 ad = zero4(), pd = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) {
+        ad = mfma(yd[kb], xdk[kb], ad);
+        pd = mfma(yd[kb], xdq[kb], pd);
+    }
+    for (int b = w - 1; b >= 0; b--) {
+        if (b < w - 1) {
+            /* extend the bridge over sub-chunk b + 1 */
+#pragma unroll
+            for (int j = 0; j < 32; j++) {
+                const int ch = 32 * (j >> 3) + kperm(g, j & 7);
+                const float ft = sh.f_t[b + 1][ch];
+                xok[j] *= ft;
+                xoq[j] *= ft;
+            }
+        }
+        f32x4 ta = zero4(), tp = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
+            const bf16x8 zb = sh.z[b][kb][l];
+            ta = mfma(zb, pack8f(&xok[kb * 8]), ta);
+            tp = mfma(zb, pack8f(&xoq[kb * 8]), tp);
+        }
+        /* b < w is a compile-time unknown; write through a switch-free select */
+#pragma unroll
+        for (int bb = 0; bb < 4; bb++)
+            if (bb == b) { at[bb] = ta; pt[bb] = tp; }
+    }
+    /* masks (select, never multiply: the masked entries may be inf/nan) and beta */
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const int jj = 4 * g + e;
+        const float av = ad[e] * bt;
+        ad[e] = (jj < r16) ? av : 0.f;
+        pd[e] = (jj <= r16) ? pd[e] : 0.f;
+    }
+#pragma unroll
+    for (int bb = 0; bb < 4; bb++)
+        if (bb == w) { at[bb] = ad; pt[bb] = pd; }
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        if (b < w) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) at[b][e] *= bt;
+        }
+        *(float4 *)&sh.a[r][16 * b + 4 * g] = make_float4(at[b][0], at[b][1], at[b][2], at[b][3]);
+    }
+    /* P operand fragments (lane = token r, 8 regs over a 32-token block) */
+    bf16x8 pf[2];
+    pf[0] = pack8(pt[0], pt[1]);
+    pf[1] = pack8(pt[2], pt[3]);
+    {
+        bf16x8 *pdst = (bf16x8 *)(rec + KDA_REC_P);
+        if (w < 2) {
+            pdst[KDA_PIDX(w, 0) * 64 + l] = pf[0];
+        } else {
+            pdst[(2 + 2 * (w - 2)) * 64 + l] = pf[0];
+            pdst[(2 + 2 * (w - 2) + 1) * 64 + l] = pf[1];
+        }
+    }
+    __syncthreads(); /* A visible */
+
+    /* ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution ---- */
+    {
+        const int c = r16;
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; rr++) {
+            float acc = (rr == c) ? 1.f : 0.f;
+#pragma unroll
+            for (int jj = 0; jj < rr; jj++) acc -= sh.a[16 * w + rr][16 * w + jj] * x[jj];
+            x[rr] = acc;
+        }
+        if (g == 0) {
+#pragma unroll
+            for (int rr = 0; rr < 16; rr++) sh.t[16 * w + rr][16 * w + c] = x[rr];
+        }
+    }
+    __syncthreads();
+    /* off-diagonal blocks by block diagonals: T_wb = -T_ww sum_{m=b}^{w-1} A_wm T_mb */
+    {
+        const int rr = l >> 2, c4 = 4 * (l & 3);
+        for (int d = 1; d < 4; d++) {
+            const int b = w - d;
+            if (b >= 0) {
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int m = b; m < w; m++) {
+#pragma unroll
+                    for (int kk = 0; kk < 16; kk++) {
+                        const float a = sh.a[16 * w + rr][16 * m + kk];
+                        const float4 tv = *(const float4 *)&sh.t[16 * m + kk][16 * b + c4];
+                        acc[0] += a * tv.x; acc[1] += a * tv.y; acc[2] += a * tv.z; acc[3] += a * tv.w;
+                    }
+                }
+                *(float4 *)&sh.m[w][rr][c4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            }
+            __syncthreads();
+            if (b >= 0) {
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 16; kk++) {
+                    const float tw = sh.t[16 * w + rr][16 * w + kk];
+                    const float4 mv = *(const float4 *)&sh.m[w][kk][c4];
+                    acc[0] += tw * mv.x; acc[1] += tw * mv.y; acc[2] += tw * mv.z; acc[3] += tw * mv.w;
+                }
+                *(float4 *)&sh.t[16 * w + rr][16 * b + c4] = make_float4(-acc[0], -acc[1], -acc[2], -acc[3]);
+            }
+            __syncthreads();
+        }
+    }
+
+    /* ---- W, U, P T and Q' for row block w ---- */
+    const int nkb = (w >= 2) ? 2 : 1; /* token blocks holding j <= 16 w + 15 */
+    bf16x8 tf[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; jb++)
+#pragma unroll
+        for (int i = 0; i < 8; i++) tf[jb][i] = (__bf16)sh.t[r][32 * jb + kperm(g, i)];
+
+    /* W (stored negated), lane = token, regs = key channel */
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) {
+        f32x4 d0 = zero4(), d1 = zero4();
+#pragma unroll
+        for (int jb = 0; jb < 2; jb++)
+            if (jb < nkb) {
+                d0 = mfma(sh.rt[2 * kb][jb][l], tf[jb], d0);
+                d1 = mfma(sh.rt[2 * kb + 1][jb][l], tf[jb], d1);
+            }
+        ((bf16x8 *)(rec + KDA_REC_W))[(w * 4 + kb) * 64 + l] = pack8(-d0, -d1);
+    }
+    /* U, lane = value column, regs = token */
+#pragma unroll
+    for (int nt = 0; nt < 8; nt++) {
+        f32x4 d = zero4();
+#pragma unroll
+        for (int jb = 0; jb < 2; jb++)
+            if (jb < nkb) d = mfma(tf[jb], sh.vt[nt][jb][l], d);
+        uint2 u;
+        u.x = f2bf_bits(d[0]) | ((uint32_t)f2bf_bits(d[1]) << 16);
+        u.y = f2bf_bits(d[2]) | ((uint32_t)f2bf_bits(d[3]) << 16);
+        *(uint2 *)(rec + KDA_REC_U + ((size_t)(nt * 64 + l) * 16 + w * 4) * 2) = u;
+    }
+    /* P T, lane = token r, regs = j' */
+    f32x4 ptt[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; jt++) {
+        ptt[jt] = zero4();
+        if (jt <= w) {
+#pragma unroll
+            for (int jb = 0; jb < 2; jb++) {
+                if (jb >= nkb) continue;
+                bf16x8 tc;
+#pragma unroll
+                for (int i = 0; i < 8; i++) tc[i] = (__bf16)sh.t[32 * jb + kperm(g, i)][16 * jt + r16];
+                ptt[jt] = mfma(tc, pf[jb], ptt[jt]);
+            }
+        }
+    }
+    bf16x8 ptf[2];
+    ptf[0] = pack8(-ptt[0], -ptt[1]);
+    ptf[1] = pack8(-ptt[2], -ptt[3]);
+    /* Q' = Q~ - (P T) R, lane = token, regs = key channel */
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) {
+        f32x4 d0, d1;
+#pragma unroll
+        for (int e = 0; e < 4; e++) { d0[e] = (float)qt[kb][e]; d1[e] = (float)qt[kb][4 + e]; }
+#pragma unroll
+        for (int jb = 0; jb < 2; jb++)
+            if (jb < nkb) {
+                d0 = mfma(sh.rt[2 * kb][jb][l], ptf[jb], d0);
+                d1 = mfma(sh.rt[2 * kb + 1][jb][l], ptf[jb], d1);
+            }
+        ((bf16x8 *)(rec + KDA_REC_Q))[(w * 4 + kb) * 64 + l] = pack8(d0, d1);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* scan: one wave per (sequence, head, 16-column value tile)                   */
+/* ------------------------------------------------------------------------- */
+template <int WAVES>
+__global__ void __launch_bounds__(64 * WAVES)
+kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
+                const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H,
+                uint16_t *__restrict__ out, const void *__restrict__ init_state,
+                void *__restrict__ final_state, int state_fp32)
+{
+    const int l = threadIdx.x & 63, g = l >> 4, n16 = l & 15;
+    int64_t chain;
+    int nt;
+    if (WAVES == 1) {
+        /* the 8 value tiles of a chain run on one XCD (blockIdx % 8) and share L2 */
+        const int64_t b = blockIdx.x;
+        const int64_t xcd = b & 7, qd = b >> 3;
+        nt = (int)(qd & 7);
+        chain = (qd >> 3) * 8 + xcd;
+    } else {
+        chain = blockIdx.x;
+        nt = threadIdx.x >> 6;
+    }
+    const int64_t nchain = nseq * H;
+    if (chain >= nchain) return;
+    const int64_t seq = chain / H;
+    const int h = (int)(chain - seq * H);
+    const int vcol = 16 * nt + n16;
+
+    int64_t bos, eos, slot0;
+    if (cu == nullptr) {
+        bos = seq * T;
+        eos = bos + T;
+        slot0 = seq * ((T + KDA_CHUNK - 1) / KDA_CHUNK);
+    } else {
+        bos = cu[seq];
+        eos = cu[seq + 1];
+        slot0 = chunk_off[seq];
+    }
+
+    /* state slice: rows c = 16 mt + 4 g + e, column vcol */
+    f32x4 S[8];
+    const size_t sbase = (size_t)chain * KDA_DK * KDA_DV;
+#pragma unroll
+    for (int mt = 0; mt < 8; mt++) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const size_t idx = sbase + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
+            float s = 0.f;
+            if (init_state) s = state_fp32 ? ((const float *)init_state)[idx] : bf2f(((const uint16_t *)init_state)[idx]);
+            S[mt][e] = s;
+        }
+    }
+
+    const int64_t nchunk = (eos - bos + KDA_CHUNK - 1) / KDA_CHUNK;
+    for (int64_t c = 0; c < nchunk; c++) {
+        const int64_t t0 = bos + c * KDA_CHUNK;
+        const int L = (int)((eos - t0) < KDA_CHUNK ? (eos - t0) : KDA_CHUNK);
+        const unsigned char *rec = rec_base + ((size_t)(slot0 + c) * H + h) * KDA_REC_BYTES;
+        const bf16x8 *Wf = (const bf16x8 *)(rec + KDA_REC_W);
+        const bf16x8 *Qf = (const bf16x8 *)(rec + KDA_REC_Q);
+        const bf16x8 *Kf = (const bf16x8 *)(rec + KDA_REC_KT);
+        const bf16x8 *Pf = (const bf16x8 *)(rec + KDA_REC_P);
+        const bf16x8 *Uf = (const bf16x8 *)(rec + KDA_REC_U + (size_t)(nt * 64 + l) * 32);
+        const float4 *gLf = (const float4 *)(rec + KDA_REC_GL);
+
+        bf16x8 ub[2];
+        ub[0] = Uf[0];
+        ub[1] = Uf[1];
+        f32x4 D[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+            const bf16x8 &u = ub[mt >> 1];
+            const int o = (mt & 1) * 4;
+            D[mt] = f32x4{(float)u[o], (float)u[o + 1], (float)u[o + 2], (float)u[o + 3]};
+        }
+        bf16x8 sb[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+        /* D = U - W S */
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++) D[mt] = mfma(Wf[(mt * 4 + kb) * 64 + l], sb[kb], D[mt]);
+        /* out = Q' S + P U */
+        f32x4 O[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+            O[mt] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++) O[mt] = mfma(Qf[(mt * 4 + kb) * 64 + l], sb[kb], O[mt]);
+#pragma unroll
+            for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(Pf[KDA_PIDX(mt, jb) * 64 + l], ub[jb], O[mt]);
+        }
+        /* S <- diag(e^{G_L}) S + K~^T D */
+        bf16x8 db[2];
+        db[0] = pack8(D[0], D[1]);
+        db[1] = pack8(D[2], D[3]);
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++) {
+            const float4 gl = gLf[4 * mt + g];
+            S[mt][0] *= gl.x; S[mt][1] *= gl.y; S[mt][2] *= gl.z; S[mt][3] *= gl.w;
+#pragma unroll
+            for (int jb = 0; jb < 2; jb++) S[mt] = mfma(Kf[(mt * 2 + jb) * 64 + l], db[jb], S[mt]);
+        }
+        /* store out rows 16 mt + 4 g + e of this chunk */
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int rr = 16 * mt + 4 * g + e;
+                if (rr < L) out[((size_t)(t0 + rr) * H + h) * KDA_DV + vcol] = f2bf_bits(O[mt][e]);
+            }
+    }
+
+    if (final_state) {
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const size_t idx = sbase + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
+                if (state_fp32) ((float *)final_state)[idx] = S[mt][e];
+                else ((uint16_t *)final_state)[idx] = f2bf_bits(S[mt][e]);
+            }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
+/* launchers (called by kda_api.cpp after validation)                          */
+/* ------------------------------------------------------------------------- */
+extern "C" hipError_t kda_launch_chunk_map(const int32_t *cu, int64_t nseq, int32_t *chunk_off, hipStream_t st)
+{
+    hipLaunchKernelGGL(kda_chunk_map_kernel, dim3(1), dim3(1024), 0, st, cu, nseq, chunk_off);
+    return hipGetLastError();
+}
+
+extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *v, const void *g,
+                                      const void *beta, const float *A_log, const float *dt_bias,
+                                      float scale, float lower_bound, const int32_t *cu,
+                                      const int32_t *chunk_off, int64_t nseq, int64_t T, int64_t H,
+                                      int64_t nslots, void *records, hipStream_t st)
+{
+    const int64_t blocks = nslots * H;
+    hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
+                       (const uint16_t *)g, (const uint16_t *)beta, A_log, dt_bias, scale,
+                       lower_bound, cu, chunk_off, nseq, T, (int)H, (unsigned char *)records);
+    return hipGetLastError();
+}
+
+extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
+                                      int64_t nseq, int64_t T, int64_t H, void *out,
+                                      const void *init_state, void *final_state, int state_fp32,
+                                      hipStream_t st)
+{
+    const int64_t nchain = nseq * H;
+    if (nchain * 8 <= 4096) {
+        const int64_t blocks = (nchain + 7) / 8 * 64;
+        hipLaunchKernelGGL(kda_scan_kernel<1>, dim3((unsigned)blocks), dim3(64), 0, st,
+                           (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H,
+                           (uint16_t *)out, init_state, final_state, state_fp32);
+    } else {
+        hipLaunchKernelGGL(kda_scan_kernel<8>, dim3((unsigned)nchain), dim3(512), 0, st,
+                           (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H,
+                           (uint16_t *)out, init_state, final_state, state_fp32);
+    }
+    return hipGetLastError();
+}

@@ -1,0 +1,131 @@
+"""The C ABI library loads, exports what include/kda.h declares, and rejects
+invalid arguments before touching the GPU (CPU only: every call below fails
+validation, so nothing is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kimi_delta_attention_fwd_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    return sorted(set(re.findall(r"KDA_API\s+[\w\s\*]*?\b(kda_\w+)\s*\(", src)))
+
+
+def test_exports_match_header():
+    lib = kda.load_library()
+    names = _declared()
+    assert set(names) == set(kda.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code, tag in enumerate(["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_HEAD_DIM", "KDA_ERR_SHAPE",
+                                "KDA_ERR_STATE_DTYPE", "KDA_ERR_ARG", "KDA_ERR_WORKSPACE",
+                                "KDA_ERR_ALIAS", "KDA_ERR_HIP"]):
+        assert kda.status_string(code).startswith(tag)
+    assert "unknown" in kda.status_string(99)
+
+
+def test_workspace_size():
+    rec = 72192
+    assert kda.workspace_size(1, 65536, 32) == 1024 * 32 * rec
+    assert kda.workspace_size(4, 2048, 16) == 4 * 32 * 16 * rec
+    assert kda.workspace_size(1, 100, 2) == 2 * 2 * rec
+    assert kda.workspace_size(1, 66399, 32, 16) == 256 + (66399 // 64 + 16) * 32 * rec
+    assert kda.workspace_size(2, 100, 2, 3) == 0      # cu_seqlens requires B = 1
+    assert kda.workspace_size(0, 100, 2) == 0
+
+
+class FakeBufs:
+    """Distinct, non-overlapping fake device addresses (never dereferenced)."""
+
+    def __init__(self, B=1, T=64, H=2):
+        self.B, self.T, self.H = B, T, H
+        act = B * T * H * 128 * 2
+        base = 1 << 40
+        step = 1 << 32
+        self.addr = {name: base + i * step for i, name in enumerate(
+            ["q", "k", "v", "g", "beta", "out", "A_log", "dt_bias", "init", "fin", "cu", "ws"])}
+        self.act = act
+
+    def call(self, lib, **over):
+        a = dict(self.addr)
+        kw = dict(scale=0.088, lb=-5.0, sd=0, cu=None, nseq=0, B=self.B, T=self.T, H=self.H,
+                  K=128, V=128, wsb=kda.workspace_size(self.B, self.T, self.H), init=None, fin=None)
+        kw.update(over)
+        p = lambda name: ctypes.c_void_p(a[name]) if a.get(name) else None
+        ptr = {}
+        for name in ["q", "k", "v", "g", "beta", "out", "A_log", "dt_bias", "ws"]:
+            v = over.get("p_" + name, "default")
+            ptr[name] = p(name) if v == "default" else (None if v is None else ctypes.c_void_p(v))
+        init = ctypes.c_void_p(kw["init"]) if kw["init"] else None
+        fin = ctypes.c_void_p(kw["fin"]) if kw["fin"] else None
+        cu = ctypes.c_void_p(kw["cu"]) if kw["cu"] else None
+        return lib.kda_fwd(ptr["q"], ptr["k"], ptr["v"], ptr["g"], ptr["beta"], kw["scale"], ptr["out"],
+                           ptr["A_log"], ptr["dt_bias"], kw["lb"], init, fin, kw["sd"], cu, kw["nseq"],
+                           kw["B"], kw["T"], kw["H"], kw["K"], kw["V"], ptr["ws"], kw["wsb"], None)
+
+
+@pytest.fixture
+def fb():
+    return FakeBufs()
+
+
+def test_rejects_head_dims(fb):
+    lib = kda.load_library()
+    assert fb.call(lib, K=64) == 2
+    assert fb.call(lib, V=256) == 2
+
+
+def test_rejects_shapes(fb):
+    lib = kda.load_library()
+    assert fb.call(lib, B=0) == 3
+    assert fb.call(lib, T=0) == 3
+    assert fb.call(lib, H=-1) == 3
+    cu = fb.addr["cu"]
+    assert fb.call(lib, B=2, cu=cu, nseq=2) == 3          # cu_seqlens needs B = 1
+    assert fb.call(lib, cu=cu, nseq=0) == 3
+
+
+def test_rejects_null(fb):
+    lib = kda.load_library()
+    for name in ["q", "k", "v", "g", "beta", "out", "A_log", "dt_bias"]:
+        assert fb.call(lib, **{"p_" + name: None}) == 1, name
+
+
+def test_rejects_state_dtype(fb):
+    lib = kda.load_library()
+    assert fb.call(lib, sd=0, init=fb.addr["init"]) == 4   # state given with NONE
+    assert fb.call(lib, sd=1) == 4                         # BF16 without states
+    assert fb.call(lib, sd=7, init=fb.addr["init"]) == 4
+
+
+def test_rejects_args(fb):
+    lib = kda.load_library()
+    assert fb.call(lib, lb=0.5) == 5
+    assert fb.call(lib, lb=-10.5) == 5
+    assert fb.call(lib, lb=float("nan")) == 5
+    assert fb.call(lib, scale=float("inf")) == 5
+
+
+def test_rejects_workspace(fb):
+    lib = kda.load_library()
+    assert fb.call(lib, p_ws=None) == 6
+    assert fb.call(lib, wsb=100) == 6
+    assert fb.call(lib, p_ws=fb.addr["ws"] + 8) == 6       # not 256-byte aligned
+
+
+def test_rejects_aliasing(fb):
+    lib = kda.load_library()
+    assert fb.call(lib, p_out=fb.addr["v"] + 64) == 7      # out overlaps v
+    assert fb.call(lib, p_ws=fb.addr["q"]) == 7            # workspace overlaps q
+    st = fb.addr["init"]
+    assert fb.call(lib, sd=2, init=st, fin=st + 1024) == 7  # partial state overlap
+    assert fb.call(lib, sd=2, init=st, fin=fb.addr["k"]) == 7

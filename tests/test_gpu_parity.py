@@ -1,0 +1,265 @@
+"""GPU parity of libkda (through its C ABI) against the fp64 oracle.
+
+Bar (fixed before measuring): per tensor, relative L2 error <= 1e-2 and max
+absolute error <= 5e-2 for ``out`` and, where returned, ``final_state``; exact
+(bitwise) equality where the chunking makes two computations identical
+(varlen vs separate calls, batch vs separate calls, chained calls split at a
+multiple of 64 with an fp32 state, repeated calls).
+"""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import kda_inputs as ki
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 1e-2
+ABS_TOL = 5e-2
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests import gpu_util
+    return gpu_util
+
+
+def check(name, got, ref):
+    rel = oracle.rel_l2(got, ref)
+    mab = oracle.max_abs(got, ref)
+    print("%-28s rel_l2=%.3e max_abs=%.3e" % (name, rel, mab), flush=True)
+    assert np.all(np.isfinite(got)), name + ": non-finite values"
+    assert rel <= REL_TOL and mab <= ABS_TOL, (name, rel, mab)
+
+
+# ---------------------------------------------------------------- workloads
+# full-size workloads run on the GPU exactly as the bench launches them; the
+# oracle recomputes a sample of heads (chains are independent per head)
+SAMPLE_HEADS = {0: None, 1: None, 2: [0, 13, 31], 3: [0, 9, 31], 4: [0, 33, 63]}
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_workload_parity(cfg):
+    gu = _gpu()
+    print("workload %d" % cfg, flush=True)
+    d = ki.config_inputs(cfg)
+    o, f = gu.run_gpu(d)
+    heads = SAMPLE_HEADS[cfg]
+    ds = d if heads is None else gu.subset_heads(d, heads)
+    ro, rf = oracle.fwd_inputs(ds, want_final=d["final"])
+    og = o if heads is None else o[:, :, heads]
+    check("cfg%d out" % cfg, og, ro)
+    if d["final"]:
+        fg = f if heads is None else f[:, heads]
+        check("cfg%d final_state" % cfg, fg, rf)
+
+
+# ---------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 129, 200])
+def test_ragged_lengths(T):
+    gu = _gpu()
+    d = ki.make_inputs(2, T, 3, seed=T, state="fp32", initial=True, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("T=%d out" % T, o, ro)
+    check("T=%d final" % T, f, rf)
+
+
+@pytest.mark.parametrize("state", ["bf16", "fp32"])
+def test_varlen_with_empty_and_single(state):
+    gu = _gpu()
+    lens = [1, 0, 64, 65, 130, 3, 0, 200]
+    d = ki.make_inputs(1, sum(lens), 2, seed=5, lengths=lens, state=state, initial=True, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("varlen %s out" % state, o, ro)
+    check("varlen %s final" % state, f, rf)
+    # empty sequences pass the state through (bf16 -> fp32 -> bf16 is exact)
+    init = d["initial_state"]
+    init64 = ki.bf16_bits_to_f64(init) if state == "bf16" else init.astype(np.float64)
+    assert np.array_equal(f[1], init64[1]) and np.array_equal(f[6], init64[6])
+
+
+def test_no_state_and_final_only():
+    gu = _gpu()
+    d = ki.make_inputs(1, 300, 2, seed=6, state="fp32", initial=False)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("final-only out", o, ro)
+    check("final-only final", f, rf)
+    d2 = ki.make_inputs(1, 300, 2, seed=6)
+    o2, f2 = gu.run_gpu(d2)
+    assert f2 is None and np.array_equal(o2, o)
+
+
+@pytest.mark.parametrize("lb", [0.0, -1.0, -10.0])
+def test_lower_bound_range(lb):
+    gu = _gpu()
+    d = ki.make_inputs(1, 256, 2, seed=7, lower_bound=lb, state="fp32", initial=True, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("lb=%g out" % lb, o, ro)
+    check("lb=%g final" % lb, f, rf)
+
+
+def test_unnormalised_inputs():
+    """q and k that are not unit rows are normalised inside the kernel."""
+    gu = _gpu()
+    d = ki.make_inputs(1, 192, 2, seed=8, state="fp32", initial=True)
+    rng = np.random.default_rng(0)
+    for key in ("q", "k"):
+        x = ki.bf16_bits_to_f32(d[key]) * rng.uniform(0.1, 30.0, d[key].shape[:-1] + (1,)).astype(np.float32)
+        d[key] = ki.f32_to_bf16_bits(x)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("unnormalised out", o, ro)
+    check("unnormalised final", f, rf)
+
+
+# ---------------------------------------------------------------- exact invariants
+def test_varlen_equals_separate_bitwise():
+    gu = _gpu()
+    lens = [70, 1, 128, 129, 3]
+    d = ki.make_inputs(1, sum(lens), 2, seed=9, lengths=lens, state="fp32", initial=True)
+    o, f = gu.run_gpu(d)
+    cu = d["cu_seqlens"]
+    for n in range(len(lens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        e = dict(d)
+        for key in ("q", "k", "v", "g", "beta"):
+            e[key] = np.ascontiguousarray(d[key][:, a:b])
+        e.update(T=b - a, N=1, cu_seqlens=None, initial_state=np.ascontiguousarray(d["initial_state"][n:n + 1]))
+        on, fn = gu.run_gpu(e)
+        assert np.array_equal(on, o[:, a:b]) and np.array_equal(fn[0], f[n]), n
+
+
+def test_batch_equals_separate_bitwise():
+    gu = _gpu()
+    d = ki.make_inputs(3, 150, 2, seed=10, state="bf16", initial=True)
+    o, f = gu.run_gpu(d)
+    for b in range(3):
+        e = dict(d)
+        for key in ("q", "k", "v", "g", "beta"):
+            e[key] = np.ascontiguousarray(d[key][b:b + 1])
+        e.update(B=1, N=1, initial_state=np.ascontiguousarray(d["initial_state"][b:b + 1]))
+        ob, fb = gu.run_gpu(e)
+        assert np.array_equal(ob, o[b:b + 1]) and np.array_equal(fb, f[b:b + 1])
+
+
+@pytest.mark.parametrize("split", [128, 100])
+def test_state_chaining(split):
+    gu = _gpu()
+    d = ki.make_inputs(1, 320, 2, seed=11, state="fp32", initial=True)
+    o, f = gu.run_gpu(d)
+    first, second = dict(d), dict(d)
+    for key in ("q", "k", "v", "g", "beta"):
+        first[key] = np.ascontiguousarray(d[key][:, :split])
+        second[key] = np.ascontiguousarray(d[key][:, split:])
+    first["T"], second["T"] = split, 320 - split
+    o1, f1 = gu.run_gpu(first)
+    second["initial_state"] = f1.astype(np.float32)
+    o2, f2 = gu.run_gpu(second)
+    oc = np.concatenate([o1, o2], axis=1)
+    if split % 64 == 0:
+        assert np.array_equal(oc, o) and np.array_equal(f2, f)
+    else:
+        check("chain out", oc, o)
+        check("chain final", f2, f)
+
+
+def test_in_place_state():
+    gu = _gpu()
+    d = ki.make_inputs(2, 100, 2, seed=12, state="fp32", initial=True)
+    o, f = gu.run_gpu(d)
+    o2, f2 = gu.run_gpu(d, in_place=True)
+    assert np.array_equal(o, o2) and np.array_equal(f, f2)
+
+
+def test_deterministic_and_full_coverage():
+    gu = _gpu()
+    d = ki.make_inputs(1, 333, 3, seed=13, state="fp32", initial=True)
+    t = gu.dev_inputs(d)
+    out = torch.full((1, 333, 3, 128), float("nan"), dtype=torch.bfloat16, device=gu.DEV)
+    o1, f1 = gu.run_gpu(d, t=t, out=out)
+    assert np.all(np.isfinite(o1))
+    out2 = torch.full((1, 333, 3, 128), float("nan"), dtype=torch.bfloat16, device=gu.DEV)
+    o2, f2 = gu.run_gpu(d, t=t, out=out2)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+def test_guard_bands_untouched():
+    """Writes stay inside out and final_state (canaries around both)."""
+    gu = _gpu()
+    import kimi_delta_attention_fwd_amd as kda
+    d = ki.make_inputs(1, 130, 2, seed=14, state="fp32", initial=True)
+    t = gu.dev_inputs(d)
+    n_out = 130 * 2 * 128
+    big = torch.full((n_out + 2048,), 7.0, dtype=torch.bfloat16, device=gu.DEV)
+    out = big[1024:1024 + n_out].view(1, 130, 2, 128)
+    n_st = 2 * 128 * 128
+    bigs = torch.full((n_st + 2048,), 3.0, dtype=torch.float32, device=gu.DEV)
+    fin = bigs[1024:1024 + n_st].view(1, 2, 128, 128)
+    kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], out, t["A_log"], t["dt_bias"],
+            d["lower_bound"], initial_state=t["initial_state"], final_state=fin)
+    torch.cuda.synchronize()
+    assert torch.all(big[:1024] == 7.0) and torch.all(big[1024 + n_out:] == 7.0)
+    assert torch.all(bigs[:1024] == 3.0) and torch.all(bigs[1024 + n_st:] == 3.0)
+
+
+# ---------------------------------------------------------------- pins on the GPU
+def test_retrieval_on_gpu():
+    """A beta = 1 write of a unit key is read back: out_t = scale * v_t."""
+    gu = _gpu()
+    d = ki.make_inputs(1, 128, 2, seed=15, state="fp32", initial=True)
+    picks = [5, 63, 64, 100]
+    for t in picks:
+        d["beta"][0, t] = ki.f32_to_bf16_bits(np.ones(2, np.float32))
+        d["q"][0, t] = d["k"][0, t]
+    o, _ = gu.run_gpu(d)
+    v = ki.bf16_bits_to_f64(d["v"])
+    for t in picks:
+        want = d["scale"] * v[0, t]
+        err = np.abs(o[0, t] - want).max() / np.abs(want).max()
+        assert err < 2e-2, (t, err)
+
+
+def test_frozen_state_on_gpu():
+    """beta = 0 and alpha = 1 (lower_bound 0 and A_log -30): final == initial exactly."""
+    gu = _gpu()
+    d = ki.make_inputs(1, 200, 2, seed=16, state="fp32", initial=True, lower_bound=0.0)
+    d["beta"][:] = 0
+    o, f = gu.run_gpu(d)
+    assert np.array_equal(f, d["initial_state"].astype(np.float64))
+    ro, _ = oracle.fwd_inputs(d, want_final=False)
+    check("frozen out", o, ro)
+
+
+# ---------------------------------------------------------------- argument errors
+def test_errors_raise():
+    gu = _gpu()
+    import kimi_delta_attention_fwd_amd as kda
+    d = ki.make_inputs(1, 64, 1, seed=17)
+    t = gu.dev_inputs(d)
+    out = torch.empty((1, 64, 1, 128), dtype=torch.bfloat16, device=gu.DEV)
+    with pytest.raises(ValueError, match="KDA_ERR_ARG"):
+        kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], out, t["A_log"], t["dt_bias"], 0.5)
+    with pytest.raises(ValueError, match="KDA_ERR_ARG"):
+        kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], out, t["A_log"], t["dt_bias"], -11.0)
+    with pytest.raises(ValueError, match="KDA_ERR_ALIAS"):
+        kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], t["v"], t["A_log"], t["dt_bias"], -5.0)
+    s32 = torch.zeros((1, 1, 128, 128), dtype=torch.float32, device=gu.DEV)
+    s16 = torch.zeros((1, 1, 128, 128), dtype=torch.bfloat16, device=gu.DEV)
+    with pytest.raises(ValueError):
+        kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], out, t["A_log"], t["dt_bias"], -5.0,
+                initial_state=s32, final_state=s16)
+    cu = torch.tensor([0, 32, 64], dtype=torch.int32, device=gu.DEV)
+    q2 = torch.zeros((2, 32, 1, 128), dtype=torch.bfloat16, device=gu.DEV)
+    b2 = torch.zeros((2, 32, 1), dtype=torch.bfloat16, device=gu.DEV)
+    o2 = torch.empty_like(q2)
+    with pytest.raises(ValueError, match="KDA_ERR_SHAPE"):
+        kda.fwd(q2, q2, q2, q2, b2, d["scale"], o2, t["A_log"], t["dt_bias"], -5.0, cu_seqlens=cu)

@@ -1,0 +1,104 @@
+"""Per-chunk intermediates of the prep kernel against the fp64 chunk twin.
+
+After a kda_fwd call the workspace holds one record per (chunk, head): -W, Q',
+K~^T, P (lower triangle), U and e^{G_L}, stored in MFMA operand order (see
+kda_internal.h: lane l covers row l % 16 of a 16-row tile and its 8 values
+cover positions kperm(l // 16, i) of a 32-wide block). This test decodes them
+and compares with oracle.chunk_twin's matrices, so a failure names the
+quantity that is wrong rather than only the final output.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import kda_inputs as ki
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+REC = dict(W=0, Q=16384, KT=32768, P=49152, U=55296, GL=71680, BYTES=72192)
+
+
+def kperm(g, i):
+    return 4 * g + i if i < 4 else 16 + 4 * g + (i - 4)
+
+
+def decode_frags(raw, nrow_tiles, nk_blocks, index):
+    """raw: uint16 record bytes; returns matrix [16*nrow_tiles, 32*nk_blocks]."""
+    M = np.zeros((16 * nrow_tiles, 32 * nk_blocks))
+    for mt in range(nrow_tiles):
+        for kb in range(nk_blocks):
+            f = index(mt, kb)
+            if f is None:
+                continue
+            frag = ki.bf16_bits_to_f64(raw[f * 512:(f + 1) * 512]).reshape(64, 8)
+            for lane in range(64):
+                for i in range(8):
+                    M[16 * mt + lane % 16, 32 * kb + kperm(lane // 16, i)] = frag[lane, i]
+    return M
+
+
+def pidx(mt, jb):
+    if jb > mt // 2:
+        return None
+    return mt if mt < 2 else 2 + 2 * (mt - 2) + jb
+
+
+def decode_record(rec):
+    u16 = rec.view(np.uint16)
+    W = -decode_frags(u16[REC["W"] // 2:], 4, 4, lambda mt, kb: mt * 4 + kb)
+    Q = decode_frags(u16[REC["Q"] // 2:], 4, 4, lambda mt, kb: mt * 4 + kb)
+    KtT = decode_frags(u16[REC["KT"] // 2:], 8, 2, lambda ct, jb: ct * 2 + jb)
+    P = decode_frags(u16[REC["P"] // 2:], 4, 2, pidx)
+    Uraw = ki.bf16_bits_to_f64(u16[REC["U"] // 2:REC["U"] // 2 + 8 * 64 * 16]).reshape(8, 64, 4, 4)
+    U = np.zeros((64, 128))
+    for nt in range(8):
+        for lane in range(64):
+            for mt in range(4):
+                for e in range(4):
+                    U[16 * mt + 4 * (lane // 16) + e, 16 * nt + lane % 16] = Uraw[nt, lane, mt, e]
+    gL = rec[REC["GL"]:REC["GL"] + 512].view(np.float32).astype(np.float64)
+    return dict(W=W, Q=Q, Kt=KtT.T, P=P, U=U, gL=gL)
+
+
+def rel(a, b):
+    return oracle.rel_l2(a, b)
+
+
+@pytest.mark.parametrize("lb", [-5.0, -3.0])
+def test_records_match_chunk_twin(lb):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from tests import gpu_util as gu
+    import kimi_delta_attention_fwd_amd as kda
+    T, H = 200, 2
+    d = ki.make_inputs(1, T, H, seed=21, lower_bound=lb, state="fp32", initial=True, sigma=0.05,
+                       dt_sigma=0.1)
+    ws = torch.zeros(kda.workspace_size(1, T, H, 0), dtype=torch.uint8, device=gu.DEV)
+    gu.run_gpu(d, workspace=ws)
+    raw = ws.cpu().numpy()
+    _, _, parts = oracle.chunk_twin(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], d["A_log"],
+                                    d["dt_bias"], lb, initial_state=d["initial_state"], return_parts=True)
+    sc = d["scale"]
+    worst = {}
+    for p in parts:
+        slot = p["start"] // 64
+        L = p["W"].shape[0]
+        off = (slot * H + p["head"]) * REC["BYTES"]
+        r = decode_record(raw[off:off + REC["BYTES"]])
+        want = dict(W=p["W"], Q=sc * (p["Qt"] - p["P"] @ p["W"]), Kt=p["Kt"], P=sc * p["P"],
+                    U=p["U"], gL=p["gL"])
+        for key in ("W", "Q", "Kt", "U"):
+            got = r[key][:L]
+            e = rel(got, want[key])
+            worst[key] = max(worst.get(key, 0.0), e)
+            assert np.all(r[key][L:] == 0.0), (key, slot, "pad rows must be zero")
+        e = rel(r["P"][:L, :L], want["P"])
+        worst["P"] = max(worst.get("P", 0.0), e)
+        # e^{G_L} is often far below the fp32 range under strong decay (it then
+        # reads 0), so it is compared in absolute terms
+        worst["gL_abs"] = max(worst.get("gL_abs", 0.0), float(np.max(np.abs(r["gL"] - want["gL"]))))
+    print("record rel_l2 (worst over chunks):", {k: "%.2e" % v for k, v in worst.items()}, flush=True)
+    for key, e in worst.items():
+        assert e < (1e-6 if key == "gL_abs" else 2e-2), (key, e)
