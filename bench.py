@@ -1,0 +1,178 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked Kimi Delta Attention forward (libkda) on one MI355X.
+
+A step is one kda_fwd call (chunk map if varlen, prep kernel, scan kernel) over
+one batch of seeded synthetic inputs already resident in HBM. The default
+workload is the long prefill: B = 1, T = 65536, H = 32, K = V = 128, bf16
+activations, lower_bound = -3, fp32 final state, no initial state.
+
+Prints one JSON line with the throughput (token*heads/s), the roofline of the
+dominant kernel (its algorithmic HBM bytes per launch over its mean duration,
+timed live with hipEvents on the launch stream), the roofline of the whole step,
+and the fp64 oracle timed on this host's cores on a bounded prefix of the same
+workload; the oracle's output on that prefix is also compared with the GPU's.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0..4]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA fwd tokens*heads/s + % of binding MFMA/HBM roofline, T=64K H=32"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+# algorithmic HBM bytes per token-head: q, k, g, v reads (4 x 256), out write (256), beta (2)
+PREP_BYTES_PER_TH = 4 * 256 + 2
+SCAN_BYTES_PER_TH = 256
+# algorithmic MFMA flops per token-head with 16x16 blocks and 64-token chunks:
+# state-side 6*K*V + intra-chunk 2*C*(3K + 2V)
+FLOPS_PER_TH = 6 * 128 * 128 + 2 * 64 * (3 * 128 + 2 * 128)
+
+
+def state_bytes(d):
+    if d["state_dtype"] is None:
+        return 0
+    per = 128 * 128 * (4 if d["state_dtype"] == "fp32" else 2)
+    n = (1 if d["initial_state"] is not None else 0) + (1 if d["final"] else 0)
+    return n * d["N"] * d["H"] * per
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload 0..4 (default: 3, the long prefill)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32768,
+                    help="prefix length on which the oracle is timed (all heads)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kda_inputs as ki
+    import kimi_delta_attention_fwd_amd as kda
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    kda.load_library()
+    dev = "cuda:0"
+    t_gen = time.time()
+    d = ki.config_inputs(args.config)
+    print("[bench] inputs for workload %d (%s) drawn in %.1f s" % (args.config, d["name"], time.time() - t_gen),
+          file=sys.stderr, flush=True)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, g, beta = bf(d["q"]), bf(d["k"]), bf(d["v"]), bf(d["g"]), bf(d["beta"])
+    A_log = torch.from_numpy(d["A_log"]).to(dev)
+    dt_bias = torch.from_numpy(d["dt_bias"]).to(dev)
+    sdt = torch.float32 if d["state_dtype"] == "fp32" else torch.bfloat16
+    init = None
+    if d["initial_state"] is not None:
+        init = torch.from_numpy(d["initial_state"]).to(dev) if sdt == torch.float32 else bf(d["initial_state"])
+    fin = torch.empty((d["N"], d["H"], 128, 128), dtype=sdt, device=dev) if d["final"] else None
+    cu = None if d["cu_seqlens"] is None else torch.from_numpy(d["cu_seqlens"]).to(dev)
+    B, T, H = d["B"], d["T"], d["H"]
+    out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device=dev)
+    nseq = 0 if cu is None else d["N"]
+    ws = torch.empty(kda.workspace_size(B, T, H, nseq), dtype=torch.uint8, device=dev)
+
+    def step():
+        kda.fwd(q, k, v, g, beta, d["scale"], out, A_log, dt_bias, d["lower_bound"],
+                initial_state=init, final_state=fin, cu_seqlens=cu, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kda.profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kda.profile_enable(False)
+    prof = kda.profile_read()
+    wall = t1 - t0
+    ms_per_step = wall / args.steps * 1e3
+    th = ki.token_heads(d)
+    value = th * args.steps / wall
+
+    # per-kernel live timing (hipEvents on the launch stream)
+    kernels = {name: tot / cnt for name, (tot, cnt) in prof.items()}
+    alg_bytes = {"kda_prep": th * PREP_BYTES_PER_TH,
+                 "kda_scan": th * SCAN_BYTES_PER_TH + state_bytes(d),
+                 "kda_chunk_map": 0}
+    dom = max(kernels, key=kernels.get)
+    dom_ms = kernels[dom]
+    achieved = alg_bytes.get(dom, 0) / (dom_ms * 1e-3) / 1e9
+    path_bytes = th * (PREP_BYTES_PER_TH + SCAN_BYTES_PER_TH) + state_bytes(d)
+    path_gbs = path_bytes / (ms_per_step * 1e-3) / 1e9
+    path_tflops = th * FLOPS_PER_TH / (ms_per_step * 1e-3) / 1e12
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "token*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy draws, recipe in kda_inputs)",
+        "config": {"workload": "%s: B=%d T=%d H=%d K=V=128 chunk=64 lower_bound=%g state=%s%s" % (
+            d["name"], B, T, H, d["lower_bound"], d["state_dtype"],
+            " varlen N=%d" % d["N"] if cu is not None else ""),
+            "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom,
+                     "kernel_ms": dom_ms, "alg_bytes_per_launch": alg_bytes.get(dom, 0)},
+        "kernels_ms": kernels,
+        "path_roofline": {"bound": "hbm", "alg_bytes_per_step": path_bytes, "achieved_GBs": path_gbs,
+                          "frac_hbm": path_gbs / PEAK_HBM_GBS, "achieved_TFLOPs": path_tflops,
+                          "frac_mfma": path_tflops / PEAK_BF16_TFLOPS},
+        "event_ms_per_step": ev0.elapsed_time(ev1) / args.steps,
+    }
+
+    if not args.no_cpu:
+        import oracle
+        ts = min(args.cpu_sample_tokens, T) if cu is None else T
+        if cu is None:
+            sub = dict(d)
+            for key in ("q", "k", "v", "g", "beta"):
+                sub[key] = np.ascontiguousarray(d[key][:, :ts])
+            sub["T"] = ts
+        else:
+            sub = d
+        threads = oracle.max_threads()
+        tc0 = time.perf_counter()
+        ro, _ = oracle.fwd_inputs(sub, want_final=False)
+        tc = time.perf_counter() - tc0
+        sample_th = ki.token_heads(sub)
+        got = out[:, :sub["T"]].float().cpu().numpy()
+        res["cpu_baseline"] = {"value": sample_th / tc, "unit": "token*heads/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": "fp64 per-token recurrence on the first %d tokens x %d heads of the "
+                                         "same workload (%d token-heads, %.1f s)" % (sub["T"], H, sample_th, tc)}
+        res["parity_sample"] = {"rel_l2": oracle.rel_l2(got, ro), "max_abs": oracle.max_abs(got, ro),
+                                "tokens": sub["T"]}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

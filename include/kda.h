@@ -62,7 +62,8 @@ typedef enum {
     KDA_ERR_STATE_DTYPE = 4, /* state_dtype inconsistent with the state pointers   */
     KDA_ERR_ARG = 5,         /* scale or lower_bound non-finite, lower_bound > 0, or
                                 lower_bound < KDA_LOWER_BOUND_MIN                 */
-    KDA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than kda_fwd_workspace_size */
+    KDA_ERR_WORKSPACE = 6,   /* workspace NULL, not 256-byte aligned, or smaller
+                                than kda_fwd_workspace_size                        */
     KDA_ERR_ALIAS = 7,       /* out overlaps an input, or the states overlap only
                                 partially                                          */
     KDA_ERR_HIP = 8          /* a HIP launch/runtime error after validation         */
@@ -127,14 +128,16 @@ KDA_API const char *kda_status_string(int status);
 
 /*
  * Kernel-level timing for measurement tools (host only, not thread-safe).
- *  kda_profile_enable(1) makes later kda_fwd calls bracket each kernel they
- *  enqueue with hipEvents on the call's stream; kda_profile_enable(0) stops it.
- *  kda_profile_read synchronises on the recorded events of the most recent
- *  profiled call and writes up to `cap` kernel names and durations in ms;
- *  it returns the number of kernels (or -1 if nothing was recorded).
+ *  kda_profile_enable(1) clears the record and makes later kda_fwd calls
+ *  bracket each kernel they enqueue with hipEvents on the call's stream (up to
+ *  8192 launches); kda_profile_enable(0) stops recording. kda_profile_read
+ *  synchronises on the recorded events and aggregates them per kernel: it
+ *  writes up to `cap` distinct kernel names (static strings), their summed
+ *  durations in ms and launch counts, and returns the number of kernels, or -1
+ *  on a HIP error. Events are created on first use and kept for the process.
  */
 KDA_API int kda_profile_enable(int on);
-KDA_API int kda_profile_read(const char **names, float *ms, int cap);
+KDA_API int kda_profile_read(const char **names, float *total_ms, int *counts, int cap);
 
 #ifdef __cplusplus
 }

@@ -55,8 +55,12 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     Returns the bf16 bit patterns as uint16. Inputs are finite by construction.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = x.view(np.uint32)
+    # finite inputs only: u + 0x8000 cannot wrap below 0xFF800000 (the NaN range)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 

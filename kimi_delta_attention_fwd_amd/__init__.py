@@ -58,7 +58,7 @@ def load_library():
     lib.kda_profile_enable.argtypes = [ctypes.c_int]
     lib.kda_profile_read.restype = ctypes.c_int
     lib.kda_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float),
-                                     ctypes.c_int]
+                                     ctypes.POINTER(ctypes.c_int), ctypes.c_int]
     _lib = lib
     return lib
 
@@ -73,20 +73,22 @@ def workspace_size(B: int, T: int, H: int, num_seqs: int = 0) -> int:
 
 
 def profile_enable(on: bool = True) -> None:
+    """Start (clearing earlier records) or stop per-kernel event timing."""
     rc = load_library().kda_profile_enable(1 if on else 0)
     if rc != 0:
         raise KdaError(status_string(rc))
 
 
 def profile_read(cap: int = 8):
-    """[(kernel name, ms)] of the most recent profiled ``fwd`` call (synchronises)."""
+    """{kernel name: (total ms, launches)} over the profiled calls (synchronises)."""
     lib = load_library()
     names = (ctypes.c_char_p * cap)()
     ms = (ctypes.c_float * cap)()
-    n = lib.kda_profile_read(names, ms, cap)
+    counts = (ctypes.c_int * cap)()
+    n = lib.kda_profile_read(names, ms, counts, cap)
     if n < 0:
-        return []
-    return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]
+        raise KdaError("kda_profile_read failed")
+    return {names[i].decode(): (float(ms[i]), int(counts[i])) for i in range(n)}
 
 
 _ws_cache = {}

@@ -27,7 +27,7 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
                                       int64_t nseq, int64_t T, int64_t H, void *out,
                                       const void *init_state, void *final_state, int state_fp32,
-                                      hipStream_t st);
+                                      void *sink, hipStream_t st);
 
 namespace {
 
@@ -46,13 +46,13 @@ bool overlap(const Range &a, const Range &b)
     return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi;
 }
 
-/* ---- optional kernel timing ---- */
-constexpr int kMaxProf = 8;
+/* ---- optional kernel timing: events around each launch, aggregated per kernel ---- */
+constexpr int kMaxProf = 8192; /* launches recorded per enable() */
 bool g_prof_on = false;
-int g_prof_n = -1;
+int g_prof_n = 0;
 const char *g_prof_names[kMaxProf];
 hipEvent_t g_ev[kMaxProf][2];
-bool g_ev_made = false;
+int g_ev_made = 0;
 
 struct ProfScope {
     int idx;
@@ -60,6 +60,11 @@ struct ProfScope {
     ProfScope(const char *name, hipStream_t s) : idx(-1), st(s)
     {
         if (!g_prof_on || g_prof_n >= kMaxProf) return;
+        if (g_prof_n >= g_ev_made) {
+            if (hipEventCreate(&g_ev[g_ev_made][0]) != hipSuccess) return;
+            if (hipEventCreate(&g_ev[g_ev_made][1]) != hipSuccess) return;
+            g_ev_made++;
+        }
         idx = g_prof_n++;
         g_prof_names[idx] = name;
         hipEventRecord(g_ev[idx][0], st);
@@ -98,32 +103,36 @@ extern "C" size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_
     if (B <= 0 || T <= 0 || H <= 0 || num_seqs < 0) return 0;
     if (num_seqs > 0 && B != 1) return 0;
     const int64_t nslots = kda_max_chunks(B, T, num_seqs);
-    return kda_chunk_map_bytes(num_seqs) + (size_t)nslots * (size_t)H * KDA_REC_BYTES;
+    return KDA_SINK_BYTES + kda_chunk_map_bytes(num_seqs) + (size_t)nslots * (size_t)H * KDA_REC_BYTES;
 }
 
 extern "C" int kda_profile_enable(int on)
 {
-    if (on && !g_ev_made) {
-        for (int i = 0; i < kMaxProf; i++)
-            for (int j = 0; j < 2; j++)
-                if (hipEventCreate(&g_ev[i][j]) != hipSuccess) return KDA_ERR_HIP;
-        g_ev_made = true;
-    }
     g_prof_on = on != 0;
+    if (g_prof_on) g_prof_n = 0;
     return KDA_OK;
 }
 
-extern "C" int kda_profile_read(const char **names, float *ms, int cap)
+extern "C" int kda_profile_read(const char **names, float *total_ms, int *counts, int cap)
 {
-    if (g_prof_n < 0) return -1;
-    for (int i = 0; i < g_prof_n && i < cap; i++) {
+    int nk = 0;
+    for (int i = 0; i < g_prof_n; i++) {
         if (hipEventSynchronize(g_ev[i][1]) != hipSuccess) return -1;
         float t = 0.f;
         if (hipEventElapsedTime(&t, g_ev[i][0], g_ev[i][1]) != hipSuccess) return -1;
-        if (names) names[i] = g_prof_names[i];
-        if (ms) ms[i] = t;
+        int j = 0;
+        while (j < nk && strcmp(names[j], g_prof_names[i]) != 0) j++;
+        if (j == nk) {
+            if (nk >= cap) continue;
+            names[nk] = g_prof_names[i];
+            total_ms[nk] = 0.f;
+            counts[nk] = 0;
+            nk++;
+        }
+        total_ms[j] += t;
+        counts[j] += 1;
     }
-    return g_prof_n;
+    return nk;
 }
 
 extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
@@ -174,8 +183,9 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
 
     /* ---- launches ---- */
     hipStream_t st = (hipStream_t)stream;
-    if (g_prof_on) g_prof_n = 0;
     unsigned char *ws = (unsigned char *)workspace;
+    void *sink = ws;
+    ws += KDA_SINK_BYTES;
     int32_t *chunk_off = nullptr;
     if (cu_seqlens) {
         chunk_off = (int32_t *)ws;
@@ -194,7 +204,7 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
         ProfScope ps("kda_scan", st);
         if (kda_launch_scan(records, cu_seqlens, chunk_off, N, T, H, out,
                             state_dtype == KDA_STATE_NONE ? nullptr : initial_state, final_state,
-                            state_dtype == KDA_STATE_FP32 ? 1 : 0, st) != hipSuccess)
+                            state_dtype == KDA_STATE_FP32 ? 1 : 0, sink, st) != hipSuccess)
             return KDA_ERR_HIP;
     }
     return KDA_OK;

@@ -41,14 +41,17 @@
 #define KDA_REC_Q 16384      /* Q'   : 16 fragments, index mt*4 + kb                                  */
 #define KDA_REC_KT 32768     /* Kt^T : 16 fragments, index ct*2 + jb (ct: key tile, jb: token block) */
 #define KDA_REC_P 49152      /* P    : 6 fragments (lower triangle), index kda_pidx(mt, jb)           */
-#define KDA_REC_U 55296      /* U    : [8 value tiles][64 lanes][4 token tiles][4] bf16              */
-#define KDA_REC_GL 71680     /* e^{G_L}: 128 fp32, key-channel order                               */
+#define KDA_REC_GL 55296     /* e^{G_L}: 128 fp32, key-channel order                               */
+#define KDA_REC_U 55808      /* U    : [8 value tiles][64 lanes][4 token tiles][4] bf16              */
 #define KDA_REC_BYTES 72192
 
 /* fragment index of P(mt, jb); only jb <= mt / 2 exists */
 #define KDA_PIDX(mt, jb) ((mt) < 2 ? (mt) : 2 + 2 * ((mt) - 2) + (jb))
 
-/* workspace = [chunk_off int32[N + 1], padded to 256 B][records] */
+/* workspace = [sink 2 KiB][chunk_off int32[N + 1], padded to 256 B][records]
+ * The sink receives the scan's stores of rows past the end of a sequence, so
+ * that its inner loop needs no branch; its contents are never read. */
+#define KDA_SINK_BYTES 2048
 static inline size_t kda_chunk_map_bytes(int64_t num_seqs)
 {
     return num_seqs > 0 ? (size_t)(((num_seqs + 1) * 4 + 255) / 256 * 256) : 0;

@@ -512,26 +512,132 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 /* ------------------------------------------------------------------------- */
 /* scan: one wave per (sequence, head, 16-column value tile)                   */
 /* ------------------------------------------------------------------------- */
-template <int WAVES>
-__global__ void __launch_bounds__(64 * WAVES)
+/*
+ * Every operand fragment of a chunk record feeds exactly one MFMA of this
+ * wave, so the load of the next chunk's fragment is issued right after that
+ * MFMA into the registers it frees: each load gets a whole chunk step of lead
+ * time with a single record's worth of registers (a rolling prefetch).
+ * sched_barrier keeps the compiler from hoisting those loads. The loop body
+ * is branch-free (rows past the end of a sequence are written to a sink in the
+ * workspace), which keeps the compiler's wait counts tight across iterations.
+ */
+__device__ __forceinline__ bf16x8 ldfrag(const unsigned char *base, int frag, int l)
+{
+    return *(const bf16x8 *)(base + (size_t)frag * 1024 + l * 16);
+}
+
+struct ScanRegs {
+    bf16x8 W[16], Q[16], K[16], P[6], U[2];
+    float4 gl;
+};
+
+__device__ __forceinline__ void scan_load_all(ScanRegs &R, const unsigned char *rec, size_t uoff, int l)
+{
+#pragma unroll
+    for (int f = 0; f < 16; f++) R.W[f] = ldfrag(rec + KDA_REC_W, f, l);
+#pragma unroll
+    for (int f = 0; f < 16; f++) R.Q[f] = ldfrag(rec + KDA_REC_Q, f, l);
+#pragma unroll
+    for (int f = 0; f < 6; f++) R.P[f] = ldfrag(rec + KDA_REC_P, f, l);
+    R.U[0] = *(const bf16x8 *)(rec + uoff);
+    R.U[1] = *(const bf16x8 *)(rec + uoff + 16);
+    R.gl = *(const float4 *)(rec + KDA_REC_GL + (l & 31) * 16);
+#pragma unroll
+    for (int f = 0; f < 16; f++) R.K[f] = ldfrag(rec + KDA_REC_KT, f, l);
+}
+
+/* one chunk step: consumes R (chunk at `rec`), refills R from `nrec` */
+__device__ __forceinline__ void scan_chunk(ScanRegs &R, f32x4 (&S)[8], const unsigned char *nrec, size_t uoff,
+                                           uint16_t *out, int64_t t0, int L, int H, int h, int nt,
+                                           uint16_t *sink, int l, int g, int n16)
+{
+    /* D = U - W S   (C layout: lane = value column, regs = token) */
+    f32x4 D[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+        const int o = (mt & 1) * 4;
+        const bf16x8 &u = R.U[mt >> 1];
+        D[mt] = f32x4{(float)u[o], (float)u[o + 1], (float)u[o + 2], (float)u[o + 3]};
+    }
+    bf16x8 sb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) {
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) D[mt] = mfma(R.W[mt * 4 + kb], sb[kb], D[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) R.W[mt * 4 + kb] = ldfrag(nrec + KDA_REC_W, mt * 4 + kb, l);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    /* out^T = S^T Q'^T + U^T P^T   (lane = token, regs = 4 value columns) */
+    f32x4 O[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) O[mt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) {
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) O[mt] = mfma(sb[kb], R.Q[mt * 4 + kb], O[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) R.Q[mt * 4 + kb] = ldfrag(nrec + KDA_REC_Q, mt * 4 + kb, l);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(R.U[jb], R.P[KDA_PIDX(mt, jb)], O[mt]);
+#pragma unroll
+    for (int f = 0; f < 6; f++) R.P[f] = ldfrag(nrec + KDA_REC_P, f, l);
+    /* S <- diag(e^{G_L}) S + K~^T D */
+    bf16x8 db[2];
+    db[0] = pack8(D[0], D[1]);
+    db[1] = pack8(D[2], D[3]);
+    R.U[0] = *(const bf16x8 *)(nrec + uoff);
+    R.U[1] = *(const bf16x8 *)(nrec + uoff + 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < 8; mt++) {
+        const int src = 4 * mt + g; /* lane holding e^{G_L}[16 mt + 4 g .. + 3] */
+        S[mt][0] *= __shfl(R.gl.x, src);
+        S[mt][1] *= __shfl(R.gl.y, src);
+        S[mt][2] *= __shfl(R.gl.z, src);
+        S[mt][3] *= __shfl(R.gl.w, src);
+    }
+    R.gl = *(const float4 *)(nrec + KDA_REC_GL + (l & 31) * 16);
+#pragma unroll
+    for (int jb = 0; jb < 2; jb++) {
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++) S[mt] = mfma(R.K[mt * 2 + jb], db[jb], S[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++) R.K[mt * 2 + jb] = ldfrag(nrec + KDA_REC_KT, mt * 2 + jb, l);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    /* out rows 16 mt + n16 of this chunk, 4 contiguous bf16 per lane; rows past the
+       sequence end go to the sink so that the store needs no branch */
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+        const int rr = 16 * mt + n16;
+        uint2 u;
+        u.x = f2bf_bits(O[mt][0]) | ((uint32_t)f2bf_bits(O[mt][1]) << 16);
+        u.y = f2bf_bits(O[mt][2]) | ((uint32_t)f2bf_bits(O[mt][3]) << 16);
+        uint16_t *dst = (rr < L) ? out + ((size_t)(t0 + rr) * H + h) * KDA_DV + 16 * nt + 4 * g
+                                 : sink + (mt * 64 + l) * 4;
+        *(uint2 *)dst = u;
+    }
+}
+
+extern "C" __global__ void __launch_bounds__(64)
 kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
                 const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H,
                 uint16_t *__restrict__ out, const void *__restrict__ init_state,
-                void *__restrict__ final_state, int state_fp32)
+                void *__restrict__ final_state, int state_fp32, uint16_t *__restrict__ sink)
 {
     const int l = threadIdx.x & 63, g = l >> 4, n16 = l & 15;
-    int64_t chain;
-    int nt;
-    if (WAVES == 1) {
-        /* the 8 value tiles of a chain run on one XCD (blockIdx % 8) and share L2 */
-        const int64_t b = blockIdx.x;
-        const int64_t xcd = b & 7, qd = b >> 3;
-        nt = (int)(qd & 7);
-        chain = (qd >> 3) * 8 + xcd;
-    } else {
-        chain = blockIdx.x;
-        nt = threadIdx.x >> 6;
-    }
+    /* the 8 value tiles of a chain run on one XCD (blockIdx % 8) and share its L2 */
+    const int64_t b = blockIdx.x;
+    const int64_t xcd = b & 7, qd = b >> 3;
+    const int nt = (int)(qd & 7);
+    const int64_t chain = (qd >> 3) * 8 + xcd;
     const int64_t nchain = nseq * H;
     if (chain >= nchain) return;
     const int64_t seq = chain / H;
@@ -564,64 +670,20 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
     }
 
     const int64_t nchunk = (eos - bos + KDA_CHUNK - 1) / KDA_CHUNK;
-    for (int64_t c = 0; c < nchunk; c++) {
-        const int64_t t0 = bos + c * KDA_CHUNK;
-        const int L = (int)((eos - t0) < KDA_CHUNK ? (eos - t0) : KDA_CHUNK);
-        const unsigned char *rec = rec_base + ((size_t)(slot0 + c) * H + h) * KDA_REC_BYTES;
-        const bf16x8 *Wf = (const bf16x8 *)(rec + KDA_REC_W);
-        const bf16x8 *Qf = (const bf16x8 *)(rec + KDA_REC_Q);
-        const bf16x8 *Kf = (const bf16x8 *)(rec + KDA_REC_KT);
-        const bf16x8 *Pf = (const bf16x8 *)(rec + KDA_REC_P);
-        const bf16x8 *Uf = (const bf16x8 *)(rec + KDA_REC_U + (size_t)(nt * 64 + l) * 32);
-        const float4 *gLf = (const float4 *)(rec + KDA_REC_GL);
-
-        bf16x8 ub[2];
-        ub[0] = Uf[0];
-        ub[1] = Uf[1];
-        f32x4 D[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++) {
-            const bf16x8 &u = ub[mt >> 1];
-            const int o = (mt & 1) * 4;
-            D[mt] = f32x4{(float)u[o], (float)u[o + 1], (float)u[o + 2], (float)u[o + 3]};
+    if (nchunk > 0) {
+        const size_t rec_stride = (size_t)H * KDA_REC_BYTES;
+        const unsigned char *rec = rec_base + ((size_t)slot0 * H + h) * KDA_REC_BYTES;
+        const unsigned char *last = rec + (size_t)(nchunk - 1) * rec_stride;
+        const size_t uoff = KDA_REC_U + (size_t)(nt * 64 + l) * 32;
+        ScanRegs R;
+        scan_load_all(R, rec, uoff, l);
+        for (int64_t c = 0; c < nchunk; c++) {
+            const int64_t t0 = bos + c * KDA_CHUNK;
+            const int L = (int)((eos - t0) < KDA_CHUNK ? (eos - t0) : KDA_CHUNK);
+            const unsigned char *nrec = rec < last ? rec + rec_stride : rec;
+            scan_chunk(R, S, nrec, uoff, out, t0, L, H, h, nt, sink, l, g, n16);
+            rec = nrec;
         }
-        bf16x8 sb[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; kb++) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
-        /* D = U - W S */
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++) D[mt] = mfma(Wf[(mt * 4 + kb) * 64 + l], sb[kb], D[mt]);
-        /* out = Q' S + P U */
-        f32x4 O[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++) {
-            O[mt] = zero4();
-#pragma unroll
-            for (int kb = 0; kb < 4; kb++) O[mt] = mfma(Qf[(mt * 4 + kb) * 64 + l], sb[kb], O[mt]);
-#pragma unroll
-            for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(Pf[KDA_PIDX(mt, jb) * 64 + l], ub[jb], O[mt]);
-        }
-        /* S <- diag(e^{G_L}) S + K~^T D */
-        bf16x8 db[2];
-        db[0] = pack8(D[0], D[1]);
-        db[1] = pack8(D[2], D[3]);
-#pragma unroll
-        for (int mt = 0; mt < 8; mt++) {
-            const float4 gl = gLf[4 * mt + g];
-            S[mt][0] *= gl.x; S[mt][1] *= gl.y; S[mt][2] *= gl.z; S[mt][3] *= gl.w;
-#pragma unroll
-            for (int jb = 0; jb < 2; jb++) S[mt] = mfma(Kf[(mt * 2 + jb) * 64 + l], db[jb], S[mt]);
-        }
-        /* store out rows 16 mt + 4 g + e of this chunk */
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int rr = 16 * mt + 4 * g + e;
-                if (rr < L) out[((size_t)(t0 + rr) * H + h) * KDA_DV + vcol] = f2bf_bits(O[mt][e]);
-            }
     }
 
     if (final_state) {
@@ -662,18 +724,12 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
                                       int64_t nseq, int64_t T, int64_t H, void *out,
                                       const void *init_state, void *final_state, int state_fp32,
-                                      hipStream_t st)
+                                      void *sink, hipStream_t st)
 {
     const int64_t nchain = nseq * H;
-    if (nchain * 8 <= 4096) {
-        const int64_t blocks = (nchain + 7) / 8 * 64;
-        hipLaunchKernelGGL(kda_scan_kernel<1>, dim3((unsigned)blocks), dim3(64), 0, st,
-                           (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H,
-                           (uint16_t *)out, init_state, final_state, state_fp32);
-    } else {
-        hipLaunchKernelGGL(kda_scan_kernel<8>, dim3((unsigned)nchain), dim3(512), 0, st,
-                           (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H,
-                           (uint16_t *)out, init_state, final_state, state_fp32);
-    }
+    const int64_t blocks = (nchain + 7) / 8 * 64;
+    hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)blocks), dim3(64), 0, st,
+                       (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H,
+                       (uint16_t *)out, init_state, final_state, state_fp32, (uint16_t *)sink);
     return hipGetLastError();
 }

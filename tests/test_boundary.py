@@ -34,11 +34,11 @@ def test_status_strings():
 
 
 def test_workspace_size():
-    rec = 72192
-    assert kda.workspace_size(1, 65536, 32) == 1024 * 32 * rec
-    assert kda.workspace_size(4, 2048, 16) == 4 * 32 * 16 * rec
-    assert kda.workspace_size(1, 100, 2) == 2 * 2 * rec
-    assert kda.workspace_size(1, 66399, 32, 16) == 256 + (66399 // 64 + 16) * 32 * rec
+    rec, sink = 72192, 2048
+    assert kda.workspace_size(1, 65536, 32) == sink + 1024 * 32 * rec
+    assert kda.workspace_size(4, 2048, 16) == sink + 4 * 32 * 16 * rec
+    assert kda.workspace_size(1, 100, 2) == sink + 2 * 2 * rec
+    assert kda.workspace_size(1, 66399, 32, 16) == sink + 256 + (66399 // 64 + 16) * 32 * rec
     assert kda.workspace_size(2, 100, 2, 3) == 0      # cu_seqlens requires B = 1
     assert kda.workspace_size(0, 100, 2) == 0
 
