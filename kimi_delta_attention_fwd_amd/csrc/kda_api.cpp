@@ -25,7 +25,7 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
                                       const int32_t *chunk_off, int64_t nseq, int64_t T, int64_t H,
                                       int64_t nslots, void *records, hipStream_t st);
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
-                                      int64_t nseq, int64_t T, int64_t H, void *out,
+                                      int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
                                       const void *init_state, void *final_state, int state_fp32,
                                       void *sink, hipStream_t st);
 
@@ -202,7 +202,7 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
     }
     {
         ProfScope ps("kda_scan", st);
-        if (kda_launch_scan(records, cu_seqlens, chunk_off, N, T, H, out,
+        if (kda_launch_scan(records, cu_seqlens, chunk_off, N, T, H, nslots, out,
                             state_dtype == KDA_STATE_NONE ? nullptr : initial_state, final_state,
                             state_dtype == KDA_STATE_FP32 ? 1 : 0, sink, st) != hipSuccess)
             return KDA_ERR_HIP;

@@ -150,29 +150,66 @@ kda_chunk_map_kernel(const int32_t *__restrict__ cu, int64_t nseq, int32_t *__re
 /* ------------------------------------------------------------------------- */
 /* prep: one workgroup of 4 waves per (chunk slot, head)                       */
 /* ------------------------------------------------------------------------- */
+/*
+ * Wave w owns tokens 16 w .. 16 w + 15 of the chunk (sub-chunk w); lane l holds
+ * token 16 w + l % 16 and the 32 key channels 32 kb + kperm(l / 16, i).
+ *
+ * Decay factors (log2 units; c = in-sub-chunk inclusive cumsum, m_w = c at the
+ * sub-chunk's 8th token, B_w = G before sub-chunk w, Gm_w = B_w + m_w):
+ *   diagonal block w:   (k^ 2^{c - m_w}) . (k^ 2^{m_w - c})          |exp| <= 8 |lb|
+ *   block (i, b < i):   (k^ 2^{c - m_i} 2^{m_i}) . (k^ 2^{m_b - c} 2^{B_i - Gm_b})
+ *                       both sides <= 1 (anchored at the start of sub-chunk i), so a
+ *                       factor only underflows where the pairwise decay is negligible
+ *   Q~ = q^ 2^{G} = (q^ 2^{c - m_w}) 2^{Gm_w},   R = k^ 2^{G} likewise,
+ *   K~ = k^ 2^{G_L - G} = (k^ 2^{m_w - c}) 2^{G_L - Gm_w}.
+ * beta enters through A's rows and through T's columns (TB = T diag(beta)):
+ * W = TB (K^ o e^G), U = TB V.
+ */
 struct PrepShared {
-    float tot[4][KDA_DK];     /* in-sub-chunk inclusive cumsum at row 15 (log2 units) */
-    float mid[4][KDA_DK];     /* ... at row 7 (the anchor)                            */
-    float f_cm[4][KDA_DK];    /* 2^{mid}                                              */
-    float f_zt[4][KDA_DK];    /* 2^{tot - mid}                                        */
-    float f_b[4][KDA_DK];     /* 2^{B_w}, B_w = G before sub-chunk w                  */
-    float f_k[4][KDA_DK];     /* 2^{G_L - B_w - tot_w}                                */
-    float f_t[4][KDA_DK];     /* 2^{tot_w} (bridge factors)                           */
-    bf16x8 z[4][4][64];       /* key side of off-diagonal blocks, per sub-chunk       */
-    bf16x8 rt[8][2][64];      /* R = beta K^ e^G, transposed fragments (key tile, token block) */
-    bf16x8 vt[8][2][64];      /* beta V, transposed fragments (value tile, token block)        */
-    float a[KDA_CHUNK][KDA_CHUNK]; /* A (strictly lower)                              */
-    float t[KDA_CHUNK][KDA_CHUNK]; /* T = (I + A)^-1                                  */
-    float m[4][16][16];       /* per-wave 16x16 scratch                               */
+    float fq[4][KDA_DK];      /* 2^{Gm_w}                                              */
+    float fk[4][KDA_DK];      /* 2^{G_L - Gm_w}                                        */
+    float fm[4][KDA_DK];      /* 2^{m_w}                                               */
+    float fy[6][KDA_DK];      /* 2^{B_i - Gm_b}, pair (i, b) -> i (i - 1) / 2 + b        */
+    float beta[KDA_CHUNK];
+    union {
+        struct {
+            float tot[4][KDA_DK]; /* in-sub-chunk inclusive cumsum at token 15 (log2)  */
+            float mid[4][KDA_DK]; /* ... at token 7 (the anchor m_w)                    */
+            bf16x8 yd[4][4][64];  /* diagonal key side k^ 2^{m_w - c}, per sub-chunk   */
+        } p1;
+        struct {
+            float t[KDA_CHUNK][KDA_CHUNK]; /* T = (I + A)^-1, lower blocks only          */
+            float m[1024];                 /* block products of the recursive inverse   */
+        } p2;
+    } u;
+    bf16x8 rt[8][2][64];      /* R^T fragments (key tile, token block)                 */
+    bf16x8 vt[8][2][64];      /* V^T fragments (value tile, token block)               */
+    float a[KDA_CHUNK][KDA_CHUNK]; /* A (strictly lower; beta_r on row r)              */
 };
 
-extern "C" __global__ void __launch_bounds__(256)
+/* R-form fragment (lane = token, 8 values over a 32-wide block) -> C-form 16x16 tile
+   (lane = column of the block, 4 regs = tokens 4 g + e) with a 0/1 selector MFMA */
+__device__ __forceinline__ void store_transposed(const bf16x8 &fr, const bf16x8 (&sel)[2], uint16_t *dst0,
+                                                 uint16_t *dst1)
+{
+    const f32x4 d0 = mfma(fr, sel[0], zero4());
+    const f32x4 d1 = mfma(fr, sel[1], zero4());
+    uint2 u0, u1;
+    u0.x = f2bf_bits(d0[0]) | ((uint32_t)f2bf_bits(d0[1]) << 16);
+    u0.y = f2bf_bits(d0[2]) | ((uint32_t)f2bf_bits(d0[3]) << 16);
+    u1.x = f2bf_bits(d1[0]) | ((uint32_t)f2bf_bits(d1[1]) << 16);
+    u1.y = f2bf_bits(d1[2]) | ((uint32_t)f2bf_bits(d1[3]) << 16);
+    *(uint2 *)dst0 = u0;
+    *(uint2 *)dst1 = u1;
+}
+
+extern "C" __global__ void __launch_bounds__(256, 2)
 kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                 const uint16_t *__restrict__ v, const uint16_t *__restrict__ gt,
                 const uint16_t *__restrict__ beta, const float *__restrict__ A_log,
                 const float *__restrict__ dt_bias, float scale, float lower_bound,
                 const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
-                int64_t nseq, int64_t T, int H, unsigned char *__restrict__ rec_base)
+                int64_t nseq, int64_t T, int H, int64_t nslots, unsigned char *__restrict__ rec_base)
 {
     __shared__ PrepShared sh;
     const int64_t slot = blockIdx.x / H;
@@ -180,18 +217,16 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     int64_t t0, seq;
     int L;
     if (!locate_chunk(slot, cu, chunk_off, nseq, T, t0, L, seq)) return;
-    unsigned char *rec = rec_base + ((size_t)slot * H + h) * KDA_REC_BYTES;
+    unsigned char *rec = rec_base + ((size_t)h * nslots + slot) * KDA_REC_BYTES;
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, r16 = l & 15;
     const int r = 16 * w + r16;
     const bool valid = r < L;
     const size_t row = (size_t)(t0 + (valid ? r : 0)) * H + h;
 
-    /* zero T (upper blocks stay zero) */
-    for (int i = tid; i < KDA_CHUNK * KDA_CHUNK; i += 256) (&sh.t[0][0])[i] = 0.f;
-
-    /* ---- load this lane's token row: 32 key channels kb*32 + kperm(g, i) ---- */
-    float qf[32], kf[32], la[32], vf[32];
+    /* ---- phase A: load this lane's token row, norms, gate, cumsum ---- */
+    float qf[32], kf[32], la[32];
+    bf16x8 vfr[4];
     const float bt = valid ? bf2f(beta[row]) : 0.f;
     const float decay_rate = __expf(A_log[h]);
     const float lb2 = lower_bound * LOG2E_F;
@@ -209,14 +244,17 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                 uv = *(const uint2 *)(v + row * KDA_DV + ch0);
             }
             const float4 db = *(const float4 *)(dt_bias + (size_t)h * KDA_DK + ch0);
-            const uint32_t wq[2] = {uq.x, uq.y}, wk[2] = {uk.x, uk.y}, wg[2] = {ug.x, ug.y}, wv[2] = {uv.x, uv.y};
+            const uint32_t wq[2] = {uq.x, uq.y}, wk[2] = {uk.x, uk.y}, wg[2] = {ug.x, ug.y};
             const float dbs[4] = {db.x, db.y, db.z, db.w};
+            vfr[kb][half * 4 + 0] = __builtin_bit_cast(__bf16, (uint16_t)(uv.x & 0xffff));
+            vfr[kb][half * 4 + 1] = __builtin_bit_cast(__bf16, (uint16_t)(uv.x >> 16));
+            vfr[kb][half * 4 + 2] = __builtin_bit_cast(__bf16, (uint16_t)(uv.y & 0xffff));
+            vfr[kb][half * 4 + 3] = __builtin_bit_cast(__bf16, (uint16_t)(uv.y >> 16));
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int sh16 = (e & 1) * 16;
                 qf[j0 + e] = bf2f((uint16_t)(wq[e >> 1] >> sh16));
                 kf[j0 + e] = bf2f((uint16_t)(wk[e >> 1] >> sh16));
-                vf[j0 + e] = bf2f((uint16_t)(wv[e >> 1] >> sh16));
                 const float x = bf2f((uint16_t)(wg[e >> 1] >> sh16)) + dbs[e];
                 /* softplus(x) = max(x, 0) + ln(1 + e^{-|x|}) */
                 const float sp = fmaxf(x, 0.f) + log2_fast(1.f + exp2_fast(-fabsf(x) * LOG2E_F)) * LN2_F;
@@ -225,7 +263,6 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
             }
         }
     }
-    /* ---- L2 normalisation (scale folded into q) ---- */
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int j = 0; j < 32; j++) { sq += qf[j] * qf[j]; sk += kf[j] * kf[j]; }
@@ -233,65 +270,49 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
     const float iq = scale / sqrtf(sq + 1e-6f), ik = 1.f / sqrtf(sk + 1e-6f);
 #pragma unroll
-    for (int j = 0; j < 32; j++) { qf[j] *= iq; kf[j] *= ik; vf[j] *= bt; }
-
-    /* ---- in-sub-chunk inclusive cumsum of log2 a over the 16 tokens ---- */
-#pragma unroll
     for (int j = 0; j < 32; j++) la[j] = row_scan16(la[j]);
 #pragma unroll
     for (int j = 0; j < 32; j++) {
         const int ch = 32 * (j >> 3) + kperm(g, j & 7);
-        if (r16 == 15) sh.tot[w][ch] = la[j];
-        if (r16 == 7) sh.mid[w][ch] = la[j];
+        if (r16 == 15) sh.u.p1.tot[w][ch] = la[j];
+        if (r16 == 7) sh.u.p1.mid[w][ch] = la[j];
     }
+    if (g == 0) sh.beta[r] = bt;
     __syncthreads();
-    /* ---- per (sub-chunk, channel) factors ---- */
+
+    /* ---- phase B: per (sub-chunk, channel) factors ---- */
     for (int p = tid; p < 4 * KDA_DK; p += 256) {
         const int ww = p >> 7, ch = p & 127;
         float B = 0.f, GL = 0.f;
+#pragma unroll
         for (int m = 0; m < 4; m++) {
-            const float tm = sh.tot[m][ch];
+            const float tm = sh.u.p1.tot[m][ch];
             if (m < ww) B += tm;
             GL += tm;
         }
-        const float tot = sh.tot[ww][ch], mid = sh.mid[ww][ch];
-        sh.f_cm[ww][ch] = exp2_fast(mid);
-        sh.f_zt[ww][ch] = exp2_fast(tot - mid);
-        sh.f_b[ww][ch] = exp2_fast(B);
-        sh.f_k[ww][ch] = exp2_fast(GL - B - tot);
-        sh.f_t[ww][ch] = exp2_fast(tot);
+        const float gm = B + sh.u.p1.mid[ww][ch];
+        sh.fq[ww][ch] = exp2_fast(gm);
+        sh.fk[ww][ch] = exp2_fast(GL - gm);
+        sh.fm[ww][ch] = exp2_fast(sh.u.p1.mid[ww][ch]);
         if (ww == 0) ((float *)(rec + KDA_REC_GL))[ch] = exp2_fast(GL);
+    }
+    for (int p = tid; p < 6 * KDA_DK; p += 256) {
+        const int pp = p >> 7, ch = p & 127;
+        const int i = pp < 1 ? 1 : (pp < 3 ? 2 : 3);
+        const int b = pp - i * (i - 1) / 2;
+        float Bi = 0.f, Bb = 0.f;
+        for (int m = 0; m < i; m++) {
+            const float tm = sh.u.p1.tot[m][ch];
+            Bi += tm;
+            if (m < b) Bb += tm;
+        }
+        sh.fy[pp][ch] = exp2_fast(Bi - (Bb + sh.u.p1.mid[b][ch]));
     }
     __syncthreads();
 
-    /* ---- decay-scaled operands of this lane (R-form: lane = token) ---- */
-    bf16x8 xdk[4], xdq[4], yd[4], qt[4];
-    float xok[32], xoq[32];
+    /* ---- phase C: decay-scaled operands (R-form), transposes ---- */
+    bf16x8 xdk_f[4], xdq_f[4], yd_f[4], qt_f[4], xok_f[4], xoq_f[4];
     {
-        float tmp_z[32], tmp_r[32], tmp_kt[32];
-#pragma unroll
-        for (int j = 0; j < 32; j++) {
-            const int ch = 32 * (j >> 3) + kperm(g, j & 7);
-            const float mid = sh.mid[w][ch];
-            const float e1 = exp2_fast(la[j] - mid); /* e^{G_r - G_m} */
-            const float e2 = exp2_fast(mid - la[j]); /* e^{G_m - G_r} */
-            const float fcm = sh.f_cm[w][ch], fzt = sh.f_zt[w][ch], fb = sh.f_b[w][ch], fk = sh.f_k[w][ch];
-            const float dk = kf[j] * e1, dq = qf[j] * e1, ykv = kf[j] * e2;
-            xok[j] = dk * fcm;       /* k^ e^{c_r}: anchored at the sub-chunk start */
-            xoq[j] = dq * fcm;
-            tmp_z[j] = ykv * fzt;    /* k^ e^{tot - c_r}: anchored at the sub-chunk end */
-            tmp_r[j] = bt * xok[j] * fb;     /* beta k^ e^{G_r} */
-            tmp_kt[j] = tmp_z[j] * fk;       /* k^ e^{G_L - G_r} */
-            xdk[j >> 3][j & 7] = (__bf16)dk;
-            xdq[j >> 3][j & 7] = (__bf16)dq;
-            yd[j >> 3][j & 7] = (__bf16)ykv;
-            qt[j >> 3][j & 7] = (__bf16)(xoq[j] * fb); /* scale Q^ e^{G_r} */
-        }
-        /* key side of off-diagonal blocks, for later sub-chunks */
-#pragma unroll
-        for (int kb = 0; kb < 4; kb++) sh.z[w][kb][l] = pack8f(&tmp_z[kb * 8]);
-
-        /* transposes via MFMA with a 0/1 selector: R-form tile -> C-form tile */
         bf16x8 sel[2];
 #pragma unroll
         for (int hh = 0; hh < 2; hh++)
@@ -300,76 +321,78 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
         const int jb = w >> 1, jh = w & 1;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++) {
-            const bf16x8 fr = pack8f(&tmp_r[kb * 8]);
-            const bf16x8 fv = pack8f(&vf[kb * 8]);
-            const bf16x8 fk = pack8f(&tmp_kt[kb * 8]);
+            bf16x8 rf, kt;
 #pragma unroll
-            for (int hh = 0; hh < 2; hh++) {
-                const int ct = 2 * kb + hh;
-                const f32x4 dr = mfma(fr, sel[hh], zero4());
-                const f32x4 dv = mfma(fv, sel[hh], zero4());
-                const f32x4 dkt = mfma(fk, sel[hh], zero4());
-                uint16_t *pr = (uint16_t *)&sh.rt[ct][jb][l] + 4 * jh;
-                uint16_t *pv = (uint16_t *)&sh.vt[ct][jb][l] + 4 * jh;
-                uint2 ur, uv2, uk;
-                ur.x = f2bf_bits(dr[0]) | ((uint32_t)f2bf_bits(dr[1]) << 16);
-                ur.y = f2bf_bits(dr[2]) | ((uint32_t)f2bf_bits(dr[3]) << 16);
-                uv2.x = f2bf_bits(dv[0]) | ((uint32_t)f2bf_bits(dv[1]) << 16);
-                uv2.y = f2bf_bits(dv[2]) | ((uint32_t)f2bf_bits(dv[3]) << 16);
-                uk.x = f2bf_bits(dkt[0]) | ((uint32_t)f2bf_bits(dkt[1]) << 16);
-                uk.y = f2bf_bits(dkt[2]) | ((uint32_t)f2bf_bits(dkt[3]) << 16);
-                *(uint2 *)pr = ur;
-                *(uint2 *)pv = uv2;
-                *(uint2 *)(rec + KDA_REC_KT + ((size_t)(ct * 2 + jb) * 64 + l) * 16 + jh * 8) = uk;
+            for (int i = 0; i < 8; i++) {
+                const int j = kb * 8 + i;
+                const int ch = 32 * kb + kperm(g, i);
+                const float d = la[j] - sh.u.p1.mid[w][ch];
+                const float e1 = exp2_fast(d), e2 = exp2_fast(-d);
+                const float kh = kf[j] * ik;
+                const float xk = kh * e1, xq = qf[j] * iq * e1, ykv = kh * e2;
+                const float fq = sh.fq[w][ch], fm = sh.fm[w][ch];
+                xok_f[kb][i] = (__bf16)(xk * fm); /* k^ 2^{c}: anchored at the sub-chunk start */
+                xoq_f[kb][i] = (__bf16)(xq * fm);
+                xdk_f[kb][i] = (__bf16)xk;
+                xdq_f[kb][i] = (__bf16)xq;
+                yd_f[kb][i] = (__bf16)ykv;
+                qt_f[kb][i] = (__bf16)(xq * fq);
+                rf[i] = (__bf16)(xk * fq);
+                kt[i] = (__bf16)(ykv * sh.fk[w][ch]);
             }
+            sh.u.p1.yd[w][kb][l] = yd_f[kb];
+            /* key tiles 2 kb and 2 kb + 1 of R, V and K~ */
+            store_transposed(rf, sel, (uint16_t *)&sh.rt[2 * kb][jb][l] + 4 * jh,
+                             (uint16_t *)&sh.rt[2 * kb + 1][jb][l] + 4 * jh);
+            store_transposed(vfr[kb], sel, (uint16_t *)&sh.vt[2 * kb][jb][l] + 4 * jh,
+                             (uint16_t *)&sh.vt[2 * kb + 1][jb][l] + 4 * jh);
+            store_transposed(kt, sel,
+                             (uint16_t *)(rec + KDA_REC_KT + ((size_t)((2 * kb) * 2 + jb) * 64 + l) * 16 + jh * 8),
+                             (uint16_t *)(rec + KDA_REC_KT + ((size_t)((2 * kb + 1) * 2 + jb) * 64 + l) * 16 + jh * 8));
         }
     }
-    __syncthreads(); /* z, rt, vt visible */
+    __syncthreads(); /* yd, rt, vt visible */
 
-    /* ---- tril A and P for row block w (outputs lane = token r, regs = j) ---- */
+    /* ---- phase D: tril A and P for row block w (lane = token r, regs = j) ---- */
     f32x4 at[4], pt[4];
 #pragma unroll
     for (int b = 0; b < 4; b++) { at[b] = zero4(); pt[b] = zero4(); }
-    f32x4 ad = zero4(), pd = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
-        ad = mfma(yd[kb], xdk[kb], ad);
-        pd = mfma(yd[kb], xdq[kb], pd);
-    }
-    for (int b = w - 1; b >= 0; b--) {
-        if (b < w - 1) {
-            /* extend the bridge over sub-chunk b + 1 */
-#pragma unroll
-            for (int j = 0; j < 32; j++) {
-                const int ch = 32 * (j >> 3) + kperm(g, j & 7);
-                const float ft = sh.f_t[b + 1][ch];
-                xok[j] *= ft;
-                xoq[j] *= ft;
-            }
-        }
-        f32x4 ta = zero4(), tp = zero4();
+    {
+        f32x4 ad = zero4(), pd = zero4();
 #pragma unroll
         for (int kb = 0; kb < 4; kb++) {
-            const bf16x8 zb = sh.z[b][kb][l];
-            ta = mfma(zb, pack8f(&xok[kb * 8]), ta);
-            tp = mfma(zb, pack8f(&xoq[kb * 8]), tp);
+            ad = mfma(yd_f[kb], xdk_f[kb], ad);
+            pd = mfma(yd_f[kb], xdq_f[kb], pd);
         }
-        /* b < w is a compile-time unknown; write through a switch-free select */
+        for (int b = 0; b < w; b++) {
+            /* key side k^_j 2^{m_b - c_j} 2^{B_w - Gm_b} = k^_j 2^{B_w - G_j} <= 1 */
+            const float *fy = sh.fy[w * (w - 1) / 2 + b];
+            f32x4 ta = zero4(), tp = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++) {
+                const bf16x8 yb = sh.u.p1.yd[b][kb][l];
+                bf16x8 ys;
+#pragma unroll
+                for (int i = 0; i < 8; i++) ys[i] = (__bf16)((float)yb[i] * fy[32 * kb + kperm(g, i)]);
+                ta = mfma(ys, xok_f[kb], ta);
+                tp = mfma(ys, xoq_f[kb], tp);
+            }
+#pragma unroll
+            for (int bb = 0; bb < 4; bb++)
+                if (bb == b) { at[bb] = ta; pt[bb] = tp; }
+        }
+        /* masks (select, never multiply: masked entries may be inf/nan) */
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int jj = 4 * g + e;
+            const float av = ad[e] * bt;
+            ad[e] = (jj < r16) ? av : 0.f;
+            pd[e] = (jj <= r16) ? pd[e] : 0.f;
+        }
 #pragma unroll
         for (int bb = 0; bb < 4; bb++)
-            if (bb == b) { at[bb] = ta; pt[bb] = tp; }
+            if (bb == w) { at[bb] = ad; pt[bb] = pd; }
     }
-    /* masks (select, never multiply: the masked entries may be inf/nan) and beta */
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-        const int jj = 4 * g + e;
-        const float av = ad[e] * bt;
-        ad[e] = (jj < r16) ? av : 0.f;
-        pd[e] = (jj <= r16) ? pd[e] : 0.f;
-    }
-#pragma unroll
-    for (int bb = 0; bb < 4; bb++)
-        if (bb == w) { at[bb] = ad; pt[bb] = pd; }
 #pragma unroll
     for (int b = 0; b < 4; b++) {
         if (b < w) {
@@ -378,7 +401,6 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
         }
         *(float4 *)&sh.a[r][16 * b + 4 * g] = make_float4(at[b][0], at[b][1], at[b][2], at[b][3]);
     }
-    /* P operand fragments (lane = token r, 8 regs over a 32-token block) */
     bf16x8 pf[2];
     pf[0] = pack8(pt[0], pt[1]);
     pf[1] = pack8(pt[2], pt[3]);
@@ -391,10 +413,13 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
             pdst[(2 + 2 * (w - 2) + 1) * 64 + l] = pf[1];
         }
     }
-    __syncthreads(); /* A visible */
+    __syncthreads(); /* A visible; p1 (tot/mid/yd) dead from here on */
 
-    /* ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution ---- */
+    /* ---- phase E: T = (I + A)^-1 by 2-level block recursion in fp32 ---- */
+    float(*tt)[KDA_CHUNK] = sh.u.p2.t;
+    float *mm = sh.u.p2.m;
     {
+        /* level 0: 16x16 diagonal blocks by forward substitution (column c per lane) */
         const int c = r16;
         float x[16];
 #pragma unroll
@@ -406,50 +431,70 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
         }
         if (g == 0) {
 #pragma unroll
-            for (int rr = 0; rr < 16; rr++) sh.t[16 * w + rr][16 * w + c] = x[rr];
+            for (int rr = 0; rr < 16; rr++) tt[16 * w + rr][16 * w + c] = x[rr];
         }
     }
     __syncthreads();
-    /* off-diagonal blocks by block diagonals: T_wb = -T_ww sum_{m=b}^{w-1} A_wm T_mb */
+    /* level 1: T_10 = -T_11 (A_10 T_00), T_32 = -T_33 (A_32 T_22); waves 0,1 / 2,3 */
     {
-        const int rr = l >> 2, c4 = 4 * (l & 3);
-        for (int d = 1; d < 4; d++) {
-            const int b = w - d;
-            if (b >= 0) {
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
-                for (int m = b; m < w; m++) {
+        const int pr = w >> 1;                 /* block pair: rows 16 (2 pr + 1), cols 16 (2 pr) */
+        const int rr = 8 * (w & 1) + (l >> 3); /* row inside the 16x16 block */
+        const int cc = 2 * (l & 7);            /* two columns */
+        const int R0 = 16 * (2 * pr + 1), C0 = 16 * (2 * pr);
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-                    for (int kk = 0; kk < 16; kk++) {
-                        const float a = sh.a[16 * w + rr][16 * m + kk];
-                        const float4 tv = *(const float4 *)&sh.t[16 * m + kk][16 * b + c4];
-                        acc[0] += a * tv.x; acc[1] += a * tv.y; acc[2] += a * tv.z; acc[3] += a * tv.w;
-                    }
-                }
-                *(float4 *)&sh.m[w][rr][c4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-            }
-            __syncthreads();
-            if (b >= 0) {
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 16; kk++) {
-                    const float tw = sh.t[16 * w + rr][16 * w + kk];
-                    const float4 mv = *(const float4 *)&sh.m[w][kk][c4];
-                    acc[0] += tw * mv.x; acc[1] += tw * mv.y; acc[2] += tw * mv.z; acc[3] += tw * mv.w;
-                }
-                *(float4 *)&sh.t[16 * w + rr][16 * b + c4] = make_float4(-acc[0], -acc[1], -acc[2], -acc[3]);
-            }
-            __syncthreads();
+        for (int kk = 0; kk < 16; kk++) {
+            const float av = sh.a[R0 + rr][C0 + kk];
+            a0 += av * tt[C0 + kk][C0 + cc];
+            a1 += av * tt[C0 + kk][C0 + cc + 1];
         }
+        mm[pr * 256 + rr * 16 + cc] = a0;
+        mm[pr * 256 + rr * 16 + cc + 1] = a1;
+        __syncthreads();
+        float b0 = 0.f, b1 = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 16; kk++) {
+            const float tv = tt[R0 + rr][R0 + kk];
+            b0 += tv * mm[pr * 256 + kk * 16 + cc];
+            b1 += tv * mm[pr * 256 + kk * 16 + cc + 1];
+        }
+        tt[R0 + rr][C0 + cc] = -b0;
+        tt[R0 + rr][C0 + cc + 1] = -b1;
     }
+    __syncthreads();
+    /* level 2: T_BA = -T_B (A_BA T_A), 32x32 blocks (B = rows 32..63, A = cols 0..31) */
+    {
+        const int i = tid >> 3, j4 = 4 * (tid & 7);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        const int m0 = j4 < 16 ? 0 : 16; /* T_A is zero above its block diagonal */
+        for (int m = m0; m < 32; m++) {
+            const float av = sh.a[32 + i][m];
+            const float4 tv = *(const float4 *)&tt[m][j4];
+            acc[0] += av * tv.x; acc[1] += av * tv.y; acc[2] += av * tv.z; acc[3] += av * tv.w;
+        }
+        *(float4 *)&mm[i * 32 + j4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        __syncthreads();
+        float bcc[4] = {0.f, 0.f, 0.f, 0.f};
+        const int m1 = i < 16 ? 16 : 32; /* T_B row i is zero beyond its block */
+        for (int m = 0; m < m1; m++) {
+            const float tv = tt[32 + i][32 + m];
+            const float4 yv = *(const float4 *)&mm[m * 32 + j4];
+            bcc[0] += tv * yv.x; bcc[1] += tv * yv.y; bcc[2] += tv * yv.z; bcc[3] += tv * yv.w;
+        }
+        *(float4 *)&tt[32 + i][j4] = make_float4(-bcc[0], -bcc[1], -bcc[2], -bcc[3]);
+    }
+    __syncthreads();
 
-    /* ---- W, U, P T and Q' for row block w ---- */
+    /* ---- phase F: TB = T diag(beta); W, U, P TB and Q' for row block w ---- */
     const int nkb = (w >= 2) ? 2 : 1; /* token blocks holding j <= 16 w + 15 */
-    bf16x8 tf[2];
+    bf16x8 tbf[2];
 #pragma unroll
     for (int jb = 0; jb < 2; jb++)
 #pragma unroll
-        for (int i = 0; i < 8; i++) tf[jb][i] = (__bf16)sh.t[r][32 * jb + kperm(g, i)];
-
+        for (int i = 0; i < 8; i++) {
+            const int j = 32 * jb + kperm(g, i);
+            tbf[jb][i] = (__bf16)((j <= r) ? tt[r][j] * sh.beta[j] : 0.f);
+        }
     /* W (stored negated), lane = token, regs = key channel */
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
@@ -457,8 +502,8 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 #pragma unroll
         for (int jb = 0; jb < 2; jb++)
             if (jb < nkb) {
-                d0 = mfma(sh.rt[2 * kb][jb][l], tf[jb], d0);
-                d1 = mfma(sh.rt[2 * kb + 1][jb][l], tf[jb], d1);
+                d0 = mfma(sh.rt[2 * kb][jb][l], tbf[jb], d0);
+                d1 = mfma(sh.rt[2 * kb + 1][jb][l], tbf[jb], d1);
             }
         ((bf16x8 *)(rec + KDA_REC_W))[(w * 4 + kb) * 64 + l] = pack8(-d0, -d1);
     }
@@ -468,24 +513,29 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
         f32x4 d = zero4();
 #pragma unroll
         for (int jb = 0; jb < 2; jb++)
-            if (jb < nkb) d = mfma(tf[jb], sh.vt[nt][jb][l], d);
+            if (jb < nkb) d = mfma(tbf[jb], sh.vt[nt][jb][l], d);
         uint2 u;
         u.x = f2bf_bits(d[0]) | ((uint32_t)f2bf_bits(d[1]) << 16);
         u.y = f2bf_bits(d[2]) | ((uint32_t)f2bf_bits(d[3]) << 16);
         *(uint2 *)(rec + KDA_REC_U + ((size_t)(nt * 64 + l) * 16 + w * 4) * 2) = u;
     }
-    /* P T, lane = token r, regs = j' */
+    /* P TB, lane = token r, regs = j' */
     f32x4 ptt[4];
 #pragma unroll
     for (int jt = 0; jt < 4; jt++) {
         ptt[jt] = zero4();
         if (jt <= w) {
+            const int jp = 16 * jt + r16;
+            const float bj = sh.beta[jp];
 #pragma unroll
             for (int jb = 0; jb < 2; jb++) {
                 if (jb >= nkb) continue;
                 bf16x8 tc;
 #pragma unroll
-                for (int i = 0; i < 8; i++) tc[i] = (__bf16)sh.t[32 * jb + kperm(g, i)][16 * jt + r16];
+                for (int i = 0; i < 8; i++) {
+                    const int j = 32 * jb + kperm(g, i);
+                    tc[i] = (__bf16)((jp <= j) ? tt[j][jp] * bj : 0.f);
+                }
                 ptt[jt] = mfma(tc, pf[jb], ptt[jt]);
             }
         }
@@ -493,12 +543,12 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     bf16x8 ptf[2];
     ptf[0] = pack8(-ptt[0], -ptt[1]);
     ptf[1] = pack8(-ptt[2], -ptt[3]);
-    /* Q' = Q~ - (P T) R, lane = token, regs = key channel */
+    /* Q' = Q~ - (P TB) R, lane = token, regs = key channel */
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
         f32x4 d0, d1;
 #pragma unroll
-        for (int e = 0; e < 4; e++) { d0[e] = (float)qt[kb][e]; d1[e] = (float)qt[kb][4 + e]; }
+        for (int e = 0; e < 4; e++) { d0[e] = (float)qt_f[kb][e]; d1[e] = (float)qt_f[kb][4 + e]; }
 #pragma unroll
         for (int jb = 0; jb < 2; jb++)
             if (jb < nkb) {
@@ -551,6 +601,7 @@ __device__ __forceinline__ void scan_chunk(ScanRegs &R, f32x4 (&S)[8], const uns
                                            uint16_t *out, int64_t t0, int L, int H, int h, int nt,
                                            uint16_t *sink, int l, int g, int n16)
 {
+    __builtin_amdgcn_sched_barrier(0);
     /* D = U - W S   (C layout: lane = value column, regs = token) */
     f32x4 D[4];
 #pragma unroll
@@ -624,11 +675,12 @@ __device__ __forceinline__ void scan_chunk(ScanRegs &R, f32x4 (&S)[8], const uns
                                  : sink + (mt * 64 + l) * 4;
         *(uint2 *)dst = u;
     }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 extern "C" __global__ void __launch_bounds__(64)
 kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
-                const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H,
+                const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
                 uint16_t *__restrict__ out, const void *__restrict__ init_state,
                 void *__restrict__ final_state, int state_fp32, uint16_t *__restrict__ sink)
 {
@@ -671,8 +723,8 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
 
     const int64_t nchunk = (eos - bos + KDA_CHUNK - 1) / KDA_CHUNK;
     if (nchunk > 0) {
-        const size_t rec_stride = (size_t)H * KDA_REC_BYTES;
-        const unsigned char *rec = rec_base + ((size_t)slot0 * H + h) * KDA_REC_BYTES;
+        const size_t rec_stride = KDA_REC_BYTES;
+        const unsigned char *rec = rec_base + ((size_t)h * nslots + slot0) * KDA_REC_BYTES;
         const unsigned char *last = rec + (size_t)(nchunk - 1) * rec_stride;
         const size_t uoff = KDA_REC_U + (size_t)(nt * 64 + l) * 32;
         ScanRegs R;
@@ -717,19 +769,19 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
     hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
                        (const uint16_t *)g, (const uint16_t *)beta, A_log, dt_bias, scale,
-                       lower_bound, cu, chunk_off, nseq, T, (int)H, (unsigned char *)records);
+                       lower_bound, cu, chunk_off, nseq, T, (int)H, nslots, (unsigned char *)records);
     return hipGetLastError();
 }
 
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
-                                      int64_t nseq, int64_t T, int64_t H, void *out,
+                                      int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
                                       const void *init_state, void *final_state, int state_fp32,
                                       void *sink, hipStream_t st)
 {
     const int64_t nchain = nseq * H;
     const int64_t blocks = (nchain + 7) / 8 * 64;
     hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)blocks), dim3(64), 0, st,
-                       (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H,
+                       (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H, nslots,
                        (uint16_t *)out, init_state, final_state, state_fp32, (uint16_t *)sink);
     return hipGetLastError();
 }
