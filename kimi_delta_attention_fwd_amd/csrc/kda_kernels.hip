@@ -560,111 +560,130 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 }
 
 /* ------------------------------------------------------------------------- */
-/* scan: one wave per (sequence, head, 16-column value tile)                   */
+/* scan: one workgroup of 3 waves per (sequence, head, 16-column value tile)   */
 /* ------------------------------------------------------------------------- */
 /*
- * Every operand fragment of a chunk record feeds exactly one MFMA of this
- * wave, so the load of the next chunk's fragment is issued right after that
- * MFMA into the registers it frees: each load gets a whole chunk step of lead
- * time with a single record's worth of registers (a rolling prefetch).
- * sched_barrier keeps the compiler from hoisting those loads. The loop body
- * is branch-free (rows past the end of a sequence are written to a sink in the
- * workspace), which keeps the compiler's wait counts tight across iterations.
+ * wave 0 (state):  D = U - W S and S <- diag(e^{G_L}) S + K~^T D; the fp32 state
+ *                  slice (128 key rows x 16 value columns) lives in its MFMA
+ *                  accumulators.
+ * wave 1 (output): out = Q' S + P U from the bf16 copy of the chunk's entering
+ *                  state that wave 0 leaves in a two-slot LDS ring.
+ * wave 2 (L2 warm): touches its eighth of the record four chunks ahead with
+ *                  LDS-DMA loads into a scratch LDS buffer, so that the eight
+ *                  workgroups of a chain find their records in L2.
+ * The three waves meet at one barrier per chunk. Waves 0 and 1 double-buffer
+ * their record operands in registers: all loads for chunk c + 1 are issued at
+ * the start of chunk c (two register sets alternate over a two-chunk unroll).
+ * The warming loads are issued through inline assembly, so the compiler does
+ * not track them and no wave ever waits for them, except wave 2 once before it
+ * exits (its LDS must not be released with DMA writes in flight).
  */
+struct ScanSetS {
+    bf16x8 W[16], K[16], U[2];
+    float4 gl;
+};
+struct ScanSetO {
+    bf16x8 Q[16], P[6], U[2];
+};
+
 __device__ __forceinline__ bf16x8 ldfrag(const unsigned char *base, int frag, int l)
 {
     return *(const bf16x8 *)(base + (size_t)frag * 1024 + l * 16);
 }
 
-struct ScanRegs {
-    bf16x8 W[16], Q[16], K[16], P[6], U[2];
-    float4 gl;
-};
-
-__device__ __forceinline__ void scan_load_all(ScanRegs &R, const unsigned char *rec, size_t uoff, int l)
+__device__ __forceinline__ void load_set(ScanSetS &X, const unsigned char *rec, size_t uoff, int l)
 {
 #pragma unroll
-    for (int f = 0; f < 16; f++) R.W[f] = ldfrag(rec + KDA_REC_W, f, l);
+    for (int f = 0; f < 16; f++) X.W[f] = ldfrag(rec + KDA_REC_W, f, l);
+    X.U[0] = *(const bf16x8 *)(rec + uoff);
+    X.U[1] = *(const bf16x8 *)(rec + uoff + 16);
+    X.gl = *(const float4 *)(rec + KDA_REC_GL + (l & 31) * 16);
 #pragma unroll
-    for (int f = 0; f < 16; f++) R.Q[f] = ldfrag(rec + KDA_REC_Q, f, l);
-#pragma unroll
-    for (int f = 0; f < 6; f++) R.P[f] = ldfrag(rec + KDA_REC_P, f, l);
-    R.U[0] = *(const bf16x8 *)(rec + uoff);
-    R.U[1] = *(const bf16x8 *)(rec + uoff + 16);
-    R.gl = *(const float4 *)(rec + KDA_REC_GL + (l & 31) * 16);
-#pragma unroll
-    for (int f = 0; f < 16; f++) R.K[f] = ldfrag(rec + KDA_REC_KT, f, l);
+    for (int f = 0; f < 16; f++) X.K[f] = ldfrag(rec + KDA_REC_KT, f, l);
 }
 
-/* one chunk step: consumes R (chunk at `rec`), refills R from `nrec` */
-__device__ __forceinline__ void scan_chunk(ScanRegs &R, f32x4 (&S)[8], const unsigned char *nrec, size_t uoff,
-                                           uint16_t *out, int64_t t0, int L, int H, int h, int nt,
-                                           uint16_t *sink, int l, int g, int n16)
+__device__ __forceinline__ void load_set(ScanSetO &X, const unsigned char *rec, size_t uoff, int l)
 {
-    __builtin_amdgcn_sched_barrier(0);
-    /* D = U - W S   (C layout: lane = value column, regs = token) */
+#pragma unroll
+    for (int f = 0; f < 16; f++) X.Q[f] = ldfrag(rec + KDA_REC_Q, f, l);
+#pragma unroll
+    for (int f = 0; f < 6; f++) X.P[f] = ldfrag(rec + KDA_REC_P, f, l);
+    X.U[0] = *(const bf16x8 *)(rec + uoff);
+    X.U[1] = *(const bf16x8 *)(rec + uoff + 16);
+}
+
+__device__ __forceinline__ void chunk_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+/* state wave: X holds chunk c; loads chunk c + 1 (at nrec) into Y */
+__device__ __forceinline__ void state_step(ScanSetS &X, ScanSetS &Y, f32x4 (&S)[8], const unsigned char *nrec,
+                                           size_t uoff, bf16x8 *slot, int l, int g)
+{
+    load_set(Y, nrec, uoff, l);
     f32x4 D[4];
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
         const int o = (mt & 1) * 4;
-        const bf16x8 &u = R.U[mt >> 1];
+        const bf16x8 &u = X.U[mt >> 1];
         D[mt] = f32x4{(float)u[o], (float)u[o + 1], (float)u[o + 2], (float)u[o + 3]};
     }
     bf16x8 sb[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
-#pragma unroll
     for (int kb = 0; kb < 4; kb++) {
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++) D[mt] = mfma(R.W[mt * 4 + kb], sb[kb], D[mt]);
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++) R.W[mt * 4 + kb] = ldfrag(nrec + KDA_REC_W, mt * 4 + kb, l);
-        __builtin_amdgcn_sched_barrier(0);
+        sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+        slot[kb * 64 + l] = sb[kb];
     }
+    chunk_barrier();
+    /* D = U - W S */
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) D[mt] = mfma(X.W[mt * 4 + kb], sb[kb], D[mt]);
+    /* S <- diag(e^{G_L}) S + K~^T D */
+#pragma unroll
+    for (int mt = 0; mt < 8; mt++) {
+        const int src = 4 * mt + g; /* lane holding e^{G_L}[16 mt + 4 g .. + 3] */
+        S[mt][0] *= __shfl(X.gl.x, src);
+        S[mt][1] *= __shfl(X.gl.y, src);
+        S[mt][2] *= __shfl(X.gl.z, src);
+        S[mt][3] *= __shfl(X.gl.w, src);
+    }
+    bf16x8 db[2];
+    db[0] = pack8(D[0], D[1]);
+    db[1] = pack8(D[2], D[3]);
+#pragma unroll
+    for (int jb = 0; jb < 2; jb++)
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++) S[mt] = mfma(X.K[mt * 2 + jb], db[jb], S[mt]);
+}
+
+/* output wave: X holds chunk c (tokens t0 .. t0 + L - 1); loads chunk c + 1 into Y */
+__device__ __forceinline__ void output_step(ScanSetO &X, ScanSetO &Y, const unsigned char *nrec, size_t uoff,
+                                            const bf16x8 *slot, uint16_t *out, int64_t t0, int L, int H,
+                                            int h, int nt, uint16_t *sink, int l, int g, int n16)
+{
+    load_set(Y, nrec, uoff, l);
+    chunk_barrier();
+    bf16x8 sb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) sb[kb] = slot[kb * 64 + l];
     /* out^T = S^T Q'^T + U^T P^T   (lane = token, regs = 4 value columns) */
     f32x4 O[4];
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) O[mt] = zero4();
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
+    for (int kb = 0; kb < 4; kb++)
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++) O[mt] = mfma(sb[kb], R.Q[mt * 4 + kb], O[mt]);
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++) R.Q[mt * 4 + kb] = ldfrag(nrec + KDA_REC_Q, mt * 4 + kb, l);
-        __builtin_amdgcn_sched_barrier(0);
-    }
+        for (int mt = 0; mt < 4; mt++) O[mt] = mfma(sb[kb], X.Q[mt * 4 + kb], O[mt]);
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-        for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(R.U[jb], R.P[KDA_PIDX(mt, jb)], O[mt]);
-#pragma unroll
-    for (int f = 0; f < 6; f++) R.P[f] = ldfrag(nrec + KDA_REC_P, f, l);
-    /* S <- diag(e^{G_L}) S + K~^T D */
-    bf16x8 db[2];
-    db[0] = pack8(D[0], D[1]);
-    db[1] = pack8(D[2], D[3]);
-    R.U[0] = *(const bf16x8 *)(nrec + uoff);
-    R.U[1] = *(const bf16x8 *)(nrec + uoff + 16);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int mt = 0; mt < 8; mt++) {
-        const int src = 4 * mt + g; /* lane holding e^{G_L}[16 mt + 4 g .. + 3] */
-        S[mt][0] *= __shfl(R.gl.x, src);
-        S[mt][1] *= __shfl(R.gl.y, src);
-        S[mt][2] *= __shfl(R.gl.z, src);
-        S[mt][3] *= __shfl(R.gl.w, src);
-    }
-    R.gl = *(const float4 *)(nrec + KDA_REC_GL + (l & 31) * 16);
-#pragma unroll
-    for (int jb = 0; jb < 2; jb++) {
-#pragma unroll
-        for (int mt = 0; mt < 8; mt++) S[mt] = mfma(R.K[mt * 2 + jb], db[jb], S[mt]);
-#pragma unroll
-        for (int mt = 0; mt < 8; mt++) R.K[mt * 2 + jb] = ldfrag(nrec + KDA_REC_KT, mt * 2 + jb, l);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    /* out rows 16 mt + n16 of this chunk, 4 contiguous bf16 per lane; rows past the
-       sequence end go to the sink so that the store needs no branch */
+        for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(X.U[jb], X.P[KDA_PIDX(mt, jb)], O[mt]);
+    /* rows past the sequence end go to the sink so that the store needs no branch */
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
         const int rr = 16 * mt + n16;
@@ -675,15 +694,26 @@ __device__ __forceinline__ void scan_chunk(ScanRegs &R, f32x4 (&S)[8], const uns
                                  : sink + (mt * 64 + l) * 4;
         *(uint2 *)dst = u;
     }
-    __builtin_amdgcn_sched_barrier(0);
 }
 
-extern "C" __global__ void __launch_bounds__(64)
+/* one 1 KiB LDS-DMA load (64 lanes x 16 bytes) that nobody waits for; m0 is not
+   otherwise used in this kernel (LDS instructions on gfx9 do not read it) */
+__device__ __forceinline__ void warm_l2(const unsigned char *p, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(lds_addr) : "memory", "m0");
+}
+
+#define KDA_WARM_AHEAD 4
+
+extern "C" __global__ void __launch_bounds__(192)
 kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
                 const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
                 uint16_t *__restrict__ out, const void *__restrict__ init_state,
                 void *__restrict__ final_state, int state_fp32, uint16_t *__restrict__ sink)
 {
+    __shared__ bf16x8 ring[2][4 * 64];                          /* 8 KiB: S(c) in bf16 */
+    __shared__ __attribute__((aligned(16))) unsigned char warm_sink[1024];
+    const int wave = threadIdx.x >> 6;
     const int l = threadIdx.x & 63, g = l >> 4, n16 = l & 15;
     /* the 8 value tiles of a chain run on one XCD (blockIdx % 8) and share its L2 */
     const int64_t b = blockIdx.x;
@@ -706,47 +736,93 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
         eos = cu[seq + 1];
         slot0 = chunk_off[seq];
     }
-
-    /* state slice: rows c = 16 mt + 4 g + e, column vcol */
-    f32x4 S[8];
-    const size_t sbase = (size_t)chain * KDA_DK * KDA_DV;
-#pragma unroll
-    for (int mt = 0; mt < 8; mt++) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const size_t idx = sbase + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
-            float s = 0.f;
-            if (init_state) s = state_fp32 ? ((const float *)init_state)[idx] : bf2f(((const uint16_t *)init_state)[idx]);
-            S[mt][e] = s;
-        }
-    }
-
     const int64_t nchunk = (eos - bos + KDA_CHUNK - 1) / KDA_CHUNK;
-    if (nchunk > 0) {
-        const size_t rec_stride = KDA_REC_BYTES;
-        const unsigned char *rec = rec_base + ((size_t)h * nslots + slot0) * KDA_REC_BYTES;
-        const unsigned char *last = rec + (size_t)(nchunk - 1) * rec_stride;
-        const size_t uoff = KDA_REC_U + (size_t)(nt * 64 + l) * 32;
-        ScanRegs R;
-        scan_load_all(R, rec, uoff, l);
-        for (int64_t c = 0; c < nchunk; c++) {
-            const int64_t t0 = bos + c * KDA_CHUNK;
-            const int L = (int)((eos - t0) < KDA_CHUNK ? (eos - t0) : KDA_CHUNK);
-            const unsigned char *nrec = rec < last ? rec + rec_stride : rec;
-            scan_chunk(R, S, nrec, uoff, out, t0, L, H, h, nt, sink, l, g, n16);
-            rec = nrec;
-        }
-    }
+    const unsigned char *rec0 = rec_base + ((size_t)h * nslots + slot0) * KDA_REC_BYTES;
+    /* record of chunk c, clamped to the last one (its reload is harmless) */
+    auto rec_of = [&](int64_t c) { return rec0 + (size_t)(c < nchunk ? c : nchunk - 1) * KDA_REC_BYTES; };
+    const size_t uoff = KDA_REC_U + (size_t)(nt * 64 + l) * 32;
 
-    if (final_state) {
+    if (wave == 0) {
+        /* ---------------- state wave ---------------- */
+        f32x4 S[8];
+        const size_t sbase = (size_t)chain * KDA_DK * KDA_DV;
 #pragma unroll
-        for (int mt = 0; mt < 8; mt++)
+        for (int mt = 0; mt < 8; mt++) {
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const size_t idx = sbase + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
-                if (state_fp32) ((float *)final_state)[idx] = S[mt][e];
-                else ((uint16_t *)final_state)[idx] = f2bf_bits(S[mt][e]);
+                float sv = 0.f;
+                if (init_state)
+                    sv = state_fp32 ? ((const float *)init_state)[idx] : bf2f(((const uint16_t *)init_state)[idx]);
+                S[mt][e] = sv;
             }
+        }
+        if (nchunk > 0) {
+            ScanSetS X, Y;
+            int64_t c = 0;
+            if (nchunk & 1) {
+                load_set(X, rec_of(0), uoff, l);
+                state_step(X, Y, S, rec_of(1), uoff, ring[0], l, g);
+                c = 1;
+            } else {
+                load_set(Y, rec_of(0), uoff, l);
+            }
+            for (; c < nchunk; c += 2) {
+                state_step(Y, X, S, rec_of(c + 1), uoff, ring[c & 1], l, g);
+                state_step(X, Y, S, rec_of(c + 2), uoff, ring[(c + 1) & 1], l, g);
+            }
+        }
+        if (final_state) {
+            const size_t sbase2 = (size_t)chain * KDA_DK * KDA_DV;
+#pragma unroll
+            for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const size_t idx = sbase2 + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
+                    if (state_fp32) ((float *)final_state)[idx] = S[mt][e];
+                    else ((uint16_t *)final_state)[idx] = f2bf_bits(S[mt][e]);
+                }
+        }
+    } else if (wave == 1) {
+        /* ---------------- output wave ---------------- */
+        if (nchunk > 0) {
+            ScanSetO X, Y;
+            int64_t c = 0;
+            auto t0_of = [&](int64_t cc) { return bos + cc * KDA_CHUNK; };
+            auto len_of = [&](int64_t cc) {
+                const int64_t rem = eos - t0_of(cc);
+                return (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
+            };
+            if (nchunk & 1) {
+                load_set(X, rec_of(0), uoff, l);
+                output_step(X, Y, rec_of(1), uoff, ring[0], out, t0_of(0), len_of(0), H, h, nt, sink, l, g, n16);
+                c = 1;
+            } else {
+                load_set(Y, rec_of(0), uoff, l);
+            }
+            for (; c < nchunk; c += 2) {
+                output_step(Y, X, rec_of(c + 1), uoff, ring[c & 1], out, t0_of(c), len_of(c), H, h, nt, sink,
+                            l, g, n16);
+                output_step(X, Y, rec_of(c + 2), uoff, ring[(c + 1) & 1], out, t0_of(c + 1), len_of(c + 1), H,
+                            h, nt, sink, l, g, n16);
+            }
+        }
+    } else {
+        /* ---------------- L2-warming wave ---------------- */
+        const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)warm_sink;
+        for (int64_t c = 0; c < nchunk; c++) {
+            const int64_t cw = c + KDA_WARM_AHEAD;
+            if (cw < nchunk) {
+                const unsigned char *r = rec0 + (size_t)cw * KDA_REC_BYTES;
+                /* this tile's eighth of the shared operands, 1 KiB pieces */
+                for (int i = nt; i < KDA_REC_U / 1024 + 1; i += 8) warm_l2(r + i * 1024 + l * 16, lds);
+                /* and its own 2 KiB of U */
+                warm_l2(r + KDA_REC_U + nt * 2048 + l * 16, lds);
+                warm_l2(r + KDA_REC_U + nt * 2048 + 1024 + l * 16, lds);
+            }
+            chunk_barrier();
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 }
 
@@ -780,7 +856,7 @@ extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, co
 {
     const int64_t nchain = nseq * H;
     const int64_t blocks = (nchain + 7) / 8 * 64;
-    hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)blocks), dim3(64), 0, st,
+    hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)blocks), dim3(192), 0, st,
                        (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H, nslots,
                        (uint16_t *)out, init_state, final_state, state_fp32, (uint16_t *)sink);
     return hipGetLastError();
