@@ -15,6 +15,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 INCLUDES = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+# kernel translation units and their extra flags
+KERNEL_UNITS = [
+    ("kda_prep.hip", []),
+    ("kda_scan.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),  # accumulators in VGPRs: no AGPR copies in the chunk loop
+]
 
 
 def _run(cmd):
@@ -31,13 +36,16 @@ def build(verbose: bool = False) -> str:
     """Compile the kernels and the C ABI into kimi_delta_attention_fwd_amd/libkda.so."""
     bdir = os.path.join(ROOT, "_build")
     os.makedirs(bdir, exist_ok=True)
-    k_obj = os.path.join(bdir, "kda_kernels.o")
+    objs = []
+    for name, extra in KERNEL_UNITS:
+        obj = os.path.join(bdir, name.replace(".hip", ".o"))
+        _run([HIPCC, *DEVICE_FLAGS, *extra, *INCLUDES, "-c", os.path.join(CSRC, name), "-o", obj])
+        objs.append(obj)
     a_obj = os.path.join(bdir, "kda_api.o")
-    _run([HIPCC, *DEVICE_FLAGS, *INCLUDES, "-c", os.path.join(CSRC, "kda_kernels.hip"), "-o", k_obj])
-    _run([HIPCC, "-O2", "-fPIC", "-std=c++17", "-Wall", "-fvisibility=hidden", *INCLUDES, "-c",
+    _run([HIPCC, "--offload-arch=gfx950", "-O2", "-fPIC", "-std=c++17", "-Wall", "-fvisibility=hidden", *INCLUDES, "-c",
           os.path.join(CSRC, "kda_api.cpp"), "-o", a_obj])
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", k_obj, a_obj, "-o", tmp])
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, a_obj, "-o", tmp])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -27,7 +27,7 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
                                       int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
                                       const void *init_state, void *final_state, int state_fp32,
-                                      void *sink, hipStream_t st);
+                                      hipStream_t st);
 
 namespace {
 
@@ -67,11 +67,11 @@ struct ProfScope {
         }
         idx = g_prof_n++;
         g_prof_names[idx] = name;
-        hipEventRecord(g_ev[idx][0], st);
+        (void)hipEventRecord(g_ev[idx][0], st);
     }
     ~ProfScope()
     {
-        if (idx >= 0) hipEventRecord(g_ev[idx][1], st);
+        if (idx >= 0) (void)hipEventRecord(g_ev[idx][1], st);
     }
 };
 
@@ -103,7 +103,7 @@ extern "C" size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_
     if (B <= 0 || T <= 0 || H <= 0 || num_seqs < 0) return 0;
     if (num_seqs > 0 && B != 1) return 0;
     const int64_t nslots = kda_max_chunks(B, T, num_seqs);
-    return KDA_SINK_BYTES + kda_chunk_map_bytes(num_seqs) + (size_t)nslots * (size_t)H * KDA_REC_BYTES;
+    return kda_chunk_map_bytes(num_seqs) + (size_t)nslots * (size_t)H * KDA_REC_BYTES;
 }
 
 extern "C" int kda_profile_enable(int on)
@@ -184,8 +184,6 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
     /* ---- launches ---- */
     hipStream_t st = (hipStream_t)stream;
     unsigned char *ws = (unsigned char *)workspace;
-    void *sink = ws;
-    ws += KDA_SINK_BYTES;
     int32_t *chunk_off = nullptr;
     if (cu_seqlens) {
         chunk_off = (int32_t *)ws;
@@ -204,7 +202,7 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
         ProfScope ps("kda_scan", st);
         if (kda_launch_scan(records, cu_seqlens, chunk_off, N, T, H, nslots, out,
                             state_dtype == KDA_STATE_NONE ? nullptr : initial_state, final_state,
-                            state_dtype == KDA_STATE_FP32 ? 1 : 0, sink, st) != hipSuccess)
+                            state_dtype == KDA_STATE_FP32 ? 1 : 0, st) != hipSuccess)
             return KDA_ERR_HIP;
     }
     return KDA_OK;

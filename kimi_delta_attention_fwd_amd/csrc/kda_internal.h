@@ -48,13 +48,10 @@
 /* fragment index of P(mt, jb); only jb <= mt / 2 exists */
 #define KDA_PIDX(mt, jb) ((mt) < 2 ? (mt) : 2 + 2 * ((mt) - 2) + (jb))
 
-/* workspace = [sink 2 KiB][chunk_off int32[N + 1], padded to 256 B][records]
+/* workspace = [chunk_off int32[N + 1], padded to 256 B][records]
  * Records are head-major, record(slot, h) at (h * nslots + slot) * KDA_REC_BYTES
  * with nslots = kda_max_chunks(...), so the chunks of one (sequence, head) that
- * the scan walks in order are adjacent in memory.
- * The sink receives the scan's stores of rows past the end of a sequence, so
- * that its inner loop needs no branch; its contents are never read. */
-#define KDA_SINK_BYTES 2048
+ * the scan walks in order are adjacent in memory. */
 static inline size_t kda_chunk_map_bytes(int64_t num_seqs)
 {
     return num_seqs > 0 ? (size_t)(((num_seqs + 1) * 4 + 255) / 256 * 256) : 0;

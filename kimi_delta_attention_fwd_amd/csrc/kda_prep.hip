@@ -1,118 +1,17 @@
 /*
- * kda_kernels.hip -- gfx950 kernels of the chunked Kimi Delta Attention forward.
+ * kda_prep.hip -- gfx950 kernels of the chunked Kimi Delta Attention forward:
  *
  *   kda_chunk_map_kernel : varlen chunk table (prefix sum of ceil(len / 64)).
  *   kda_prep_kernel      : one workgroup per (chunk, head); gate, q/k L2 norm,
  *                          in-chunk cumsum, tril A and P, T = (I + A)^-1 by
  *                          forward substitution in LDS, W, U, Q', K~^T.
- *   kda_scan_kernel      : one wave per (sequence, head, 16 value columns);
- *                          the sequential chunk loop with the 128 x 16 slice of
- *                          the fp32 state held in MFMA accumulators.
  *
  * The operation is the gated delta rule of the FlashKDA pages (ccm-staging
  * page, "Core Kernel API / flash_kda.fwd"; trend.ondo.sh page, "Kernel API and
  * Constraints"); the chunk algebra and the record layout are described in
- * kda_internal.h.
- *
- * Decay factors never overflow: inside a 16-token sub-chunk both sides of the
- * pairwise factor e^{G_r - G_j} are anchored at the sub-chunk's 8th token
- * (|exponent| <= 8 |lower_bound|); across sub-chunks the query side is anchored
- * at the start of its sub-chunk, the key side at the end of its own, and a
- * per-channel bridge e^{B_i - B_{b+1}} <= 1 joins them, so every factor there
- * is <= 1. Exponentials are taken base 2 (v_exp_f32) on log2-scaled sums.
+ * kda_internal.h. Exponentials are taken base 2 (v_exp_f32) on log2-scaled sums.
  */
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
-#include "kda_internal.h"
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-#define LOG2E_F 1.4426950408889634f
-#define LN2_F 0.6931471805599453f
-
-namespace {
-
-__device__ __forceinline__ f32x4 mfma(const bf16x8 &a, const bf16x8 &b, const f32x4 &c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-/* position inside a 32-wide contraction block of operand slot i of lane group g */
-__device__ __forceinline__ int kperm(int g, int i) { return i < 4 ? 4 * g + i : 12 + 4 * g + i; }
-
-__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-__device__ __forceinline__ uint16_t f2bf_bits(float x)
-{
-    __bf16 b = (__bf16)x; /* round to nearest even */
-    return __builtin_bit_cast(uint16_t, b);
-}
-
-__device__ __forceinline__ bf16x8 pack8(const f32x4 &a, const f32x4 &b)
-{
-    bf16x8 r;
-    r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
-    r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
-    return r;
-}
-
-__device__ __forceinline__ bf16x8 pack8f(const float *x)
-{
-    bf16x8 r;
-#pragma unroll
-    for (int i = 0; i < 8; i++) r[i] = (__bf16)x[i];
-    return r;
-}
-
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-/* inclusive prefix sum over the 16 lanes of a DPP row */
-__device__ __forceinline__ float row_scan16(float x)
-{
-    int v = __float_as_int(x);
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true));
-    v = __float_as_int(x);
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true));
-    v = __float_as_int(x);
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true));
-    v = __float_as_int(x);
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true));
-    return x;
-}
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
-
-/* sequence / chunk of a chunk slot; returns false for slots past the end */
-__device__ __forceinline__ bool locate_chunk(int64_t slot, const int32_t *cu, const int32_t *chunk_off,
-                                             int64_t nseq, int64_t T, int64_t &t0, int &L, int64_t &seq)
-{
-    if (cu == nullptr) {
-        const int64_t cps = (T + KDA_CHUNK - 1) / KDA_CHUNK;
-        seq = slot / cps;
-        const int64_t c = slot - seq * cps;
-        t0 = seq * T + c * KDA_CHUNK;
-        const int64_t rem = T - c * KDA_CHUNK;
-        L = (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
-        return true;
-    }
-    if (slot >= chunk_off[nseq]) return false;
-    int64_t lo = 0, hi = nseq - 1; /* largest n with chunk_off[n] <= slot */
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) >> 1;
-        if (chunk_off[mid] <= slot) lo = mid; else hi = mid - 1;
-    }
-    seq = lo;
-    const int64_t c = slot - chunk_off[lo];
-    t0 = cu[lo] + c * KDA_CHUNK;
-    const int64_t rem = cu[lo + 1] - t0;
-    L = (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
-    return true;
-}
-
-} // namespace
+#include "kda_device.h"
 
 /* ------------------------------------------------------------------------- */
 /* varlen chunk table: chunk_off[n] = sum_{m < n} ceil(len_m / 64)            */
@@ -560,273 +459,6 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
 }
 
 /* ------------------------------------------------------------------------- */
-/* scan: one workgroup of 3 waves per (sequence, head, 16-column value tile)   */
-/* ------------------------------------------------------------------------- */
-/*
- * wave 0 (state):  D = U - W S and S <- diag(e^{G_L}) S + K~^T D; the fp32 state
- *                  slice (128 key rows x 16 value columns) lives in its MFMA
- *                  accumulators.
- * wave 1 (output): out = Q' S + P U from the bf16 copy of the chunk's entering
- *                  state that wave 0 leaves in a two-slot LDS ring.
- * wave 2 (L2 warm): touches its eighth of the record four chunks ahead with
- *                  LDS-DMA loads into a scratch LDS buffer, so that the eight
- *                  workgroups of a chain find their records in L2.
- * The three waves meet at one barrier per chunk. Waves 0 and 1 double-buffer
- * their record operands in registers: all loads for chunk c + 1 are issued at
- * the start of chunk c (two register sets alternate over a two-chunk unroll).
- * The warming loads are issued through inline assembly, so the compiler does
- * not track them and no wave ever waits for them, except wave 2 once before it
- * exits (its LDS must not be released with DMA writes in flight).
- */
-struct ScanSetS {
-    bf16x8 W[16], K[16], U[2];
-    float4 gl;
-};
-struct ScanSetO {
-    bf16x8 Q[16], P[6], U[2];
-};
-
-__device__ __forceinline__ bf16x8 ldfrag(const unsigned char *base, int frag, int l)
-{
-    return *(const bf16x8 *)(base + (size_t)frag * 1024 + l * 16);
-}
-
-__device__ __forceinline__ void load_set(ScanSetS &X, const unsigned char *rec, size_t uoff, int l)
-{
-#pragma unroll
-    for (int f = 0; f < 16; f++) X.W[f] = ldfrag(rec + KDA_REC_W, f, l);
-    X.U[0] = *(const bf16x8 *)(rec + uoff);
-    X.U[1] = *(const bf16x8 *)(rec + uoff + 16);
-    X.gl = *(const float4 *)(rec + KDA_REC_GL + (l & 31) * 16);
-#pragma unroll
-    for (int f = 0; f < 16; f++) X.K[f] = ldfrag(rec + KDA_REC_KT, f, l);
-}
-
-__device__ __forceinline__ void load_set(ScanSetO &X, const unsigned char *rec, size_t uoff, int l)
-{
-#pragma unroll
-    for (int f = 0; f < 16; f++) X.Q[f] = ldfrag(rec + KDA_REC_Q, f, l);
-#pragma unroll
-    for (int f = 0; f < 6; f++) X.P[f] = ldfrag(rec + KDA_REC_P, f, l);
-    X.U[0] = *(const bf16x8 *)(rec + uoff);
-    X.U[1] = *(const bf16x8 *)(rec + uoff + 16);
-}
-
-__device__ __forceinline__ void chunk_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
-/* state wave: X holds chunk c; loads chunk c + 1 (at nrec) into Y */
-__device__ __forceinline__ void state_step(ScanSetS &X, ScanSetS &Y, f32x4 (&S)[8], const unsigned char *nrec,
-                                           size_t uoff, bf16x8 *slot, int l, int g)
-{
-    load_set(Y, nrec, uoff, l);
-    f32x4 D[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; mt++) {
-        const int o = (mt & 1) * 4;
-        const bf16x8 &u = X.U[mt >> 1];
-        D[mt] = f32x4{(float)u[o], (float)u[o + 1], (float)u[o + 2], (float)u[o + 3]};
-    }
-    bf16x8 sb[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
-        sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
-        slot[kb * 64 + l] = sb[kb];
-    }
-    chunk_barrier();
-    /* D = U - W S */
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++) D[mt] = mfma(X.W[mt * 4 + kb], sb[kb], D[mt]);
-    /* S <- diag(e^{G_L}) S + K~^T D */
-#pragma unroll
-    for (int mt = 0; mt < 8; mt++) {
-        const int src = 4 * mt + g; /* lane holding e^{G_L}[16 mt + 4 g .. + 3] */
-        S[mt][0] *= __shfl(X.gl.x, src);
-        S[mt][1] *= __shfl(X.gl.y, src);
-        S[mt][2] *= __shfl(X.gl.z, src);
-        S[mt][3] *= __shfl(X.gl.w, src);
-    }
-    bf16x8 db[2];
-    db[0] = pack8(D[0], D[1]);
-    db[1] = pack8(D[2], D[3]);
-#pragma unroll
-    for (int jb = 0; jb < 2; jb++)
-#pragma unroll
-        for (int mt = 0; mt < 8; mt++) S[mt] = mfma(X.K[mt * 2 + jb], db[jb], S[mt]);
-}
-
-/* output wave: X holds chunk c (tokens t0 .. t0 + L - 1); loads chunk c + 1 into Y */
-__device__ __forceinline__ void output_step(ScanSetO &X, ScanSetO &Y, const unsigned char *nrec, size_t uoff,
-                                            const bf16x8 *slot, uint16_t *out, int64_t t0, int L, int H,
-                                            int h, int nt, uint16_t *sink, int l, int g, int n16)
-{
-    load_set(Y, nrec, uoff, l);
-    chunk_barrier();
-    bf16x8 sb[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++) sb[kb] = slot[kb * 64 + l];
-    /* out^T = S^T Q'^T + U^T P^T   (lane = token, regs = 4 value columns) */
-    f32x4 O[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; mt++) O[mt] = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++) O[mt] = mfma(sb[kb], X.Q[mt * 4 + kb], O[mt]);
-#pragma unroll
-    for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-        for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(X.U[jb], X.P[KDA_PIDX(mt, jb)], O[mt]);
-    /* rows past the sequence end go to the sink so that the store needs no branch */
-#pragma unroll
-    for (int mt = 0; mt < 4; mt++) {
-        const int rr = 16 * mt + n16;
-        uint2 u;
-        u.x = f2bf_bits(O[mt][0]) | ((uint32_t)f2bf_bits(O[mt][1]) << 16);
-        u.y = f2bf_bits(O[mt][2]) | ((uint32_t)f2bf_bits(O[mt][3]) << 16);
-        uint16_t *dst = (rr < L) ? out + ((size_t)(t0 + rr) * H + h) * KDA_DV + 16 * nt + 4 * g
-                                 : sink + (mt * 64 + l) * 4;
-        *(uint2 *)dst = u;
-    }
-}
-
-/* one 1 KiB LDS-DMA load (64 lanes x 16 bytes) that nobody waits for; m0 is not
-   otherwise used in this kernel (LDS instructions on gfx9 do not read it) */
-__device__ __forceinline__ void warm_l2(const unsigned char *p, uint32_t lds_addr)
-{
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(lds_addr) : "memory", "m0");
-}
-
-#define KDA_WARM_AHEAD 4
-
-extern "C" __global__ void __launch_bounds__(192)
-kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
-                const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
-                uint16_t *__restrict__ out, const void *__restrict__ init_state,
-                void *__restrict__ final_state, int state_fp32, uint16_t *__restrict__ sink)
-{
-    __shared__ bf16x8 ring[2][4 * 64];                          /* 8 KiB: S(c) in bf16 */
-    __shared__ __attribute__((aligned(16))) unsigned char warm_sink[1024];
-    const int wave = threadIdx.x >> 6;
-    const int l = threadIdx.x & 63, g = l >> 4, n16 = l & 15;
-    /* the 8 value tiles of a chain run on one XCD (blockIdx % 8) and share its L2 */
-    const int64_t b = blockIdx.x;
-    const int64_t xcd = b & 7, qd = b >> 3;
-    const int nt = (int)(qd & 7);
-    const int64_t chain = (qd >> 3) * 8 + xcd;
-    const int64_t nchain = nseq * H;
-    if (chain >= nchain) return;
-    const int64_t seq = chain / H;
-    const int h = (int)(chain - seq * H);
-    const int vcol = 16 * nt + n16;
-
-    int64_t bos, eos, slot0;
-    if (cu == nullptr) {
-        bos = seq * T;
-        eos = bos + T;
-        slot0 = seq * ((T + KDA_CHUNK - 1) / KDA_CHUNK);
-    } else {
-        bos = cu[seq];
-        eos = cu[seq + 1];
-        slot0 = chunk_off[seq];
-    }
-    const int64_t nchunk = (eos - bos + KDA_CHUNK - 1) / KDA_CHUNK;
-    const unsigned char *rec0 = rec_base + ((size_t)h * nslots + slot0) * KDA_REC_BYTES;
-    /* record of chunk c, clamped to the last one (its reload is harmless) */
-    auto rec_of = [&](int64_t c) { return rec0 + (size_t)(c < nchunk ? c : nchunk - 1) * KDA_REC_BYTES; };
-    const size_t uoff = KDA_REC_U + (size_t)(nt * 64 + l) * 32;
-
-    if (wave == 0) {
-        /* ---------------- state wave ---------------- */
-        f32x4 S[8];
-        const size_t sbase = (size_t)chain * KDA_DK * KDA_DV;
-#pragma unroll
-        for (int mt = 0; mt < 8; mt++) {
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const size_t idx = sbase + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
-                float sv = 0.f;
-                if (init_state)
-                    sv = state_fp32 ? ((const float *)init_state)[idx] : bf2f(((const uint16_t *)init_state)[idx]);
-                S[mt][e] = sv;
-            }
-        }
-        if (nchunk > 0) {
-            ScanSetS X, Y;
-            int64_t c = 0;
-            if (nchunk & 1) {
-                load_set(X, rec_of(0), uoff, l);
-                state_step(X, Y, S, rec_of(1), uoff, ring[0], l, g);
-                c = 1;
-            } else {
-                load_set(Y, rec_of(0), uoff, l);
-            }
-            for (; c < nchunk; c += 2) {
-                state_step(Y, X, S, rec_of(c + 1), uoff, ring[c & 1], l, g);
-                state_step(X, Y, S, rec_of(c + 2), uoff, ring[(c + 1) & 1], l, g);
-            }
-        }
-        if (final_state) {
-            const size_t sbase2 = (size_t)chain * KDA_DK * KDA_DV;
-#pragma unroll
-            for (int mt = 0; mt < 8; mt++)
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const size_t idx = sbase2 + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
-                    if (state_fp32) ((float *)final_state)[idx] = S[mt][e];
-                    else ((uint16_t *)final_state)[idx] = f2bf_bits(S[mt][e]);
-                }
-        }
-    } else if (wave == 1) {
-        /* ---------------- output wave ---------------- */
-        if (nchunk > 0) {
-            ScanSetO X, Y;
-            int64_t c = 0;
-            auto t0_of = [&](int64_t cc) { return bos + cc * KDA_CHUNK; };
-            auto len_of = [&](int64_t cc) {
-                const int64_t rem = eos - t0_of(cc);
-                return (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
-            };
-            if (nchunk & 1) {
-                load_set(X, rec_of(0), uoff, l);
-                output_step(X, Y, rec_of(1), uoff, ring[0], out, t0_of(0), len_of(0), H, h, nt, sink, l, g, n16);
-                c = 1;
-            } else {
-                load_set(Y, rec_of(0), uoff, l);
-            }
-            for (; c < nchunk; c += 2) {
-                output_step(Y, X, rec_of(c + 1), uoff, ring[c & 1], out, t0_of(c), len_of(c), H, h, nt, sink,
-                            l, g, n16);
-                output_step(X, Y, rec_of(c + 2), uoff, ring[(c + 1) & 1], out, t0_of(c + 1), len_of(c + 1), H,
-                            h, nt, sink, l, g, n16);
-            }
-        }
-    } else {
-        /* ---------------- L2-warming wave ---------------- */
-        const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)warm_sink;
-        for (int64_t c = 0; c < nchunk; c++) {
-            const int64_t cw = c + KDA_WARM_AHEAD;
-            if (cw < nchunk) {
-                const unsigned char *r = rec0 + (size_t)cw * KDA_REC_BYTES;
-                /* this tile's eighth of the shared operands, 1 KiB pieces */
-                for (int i = nt; i < KDA_REC_U / 1024 + 1; i += 8) warm_l2(r + i * 1024 + l * 16, lds);
-                /* and its own 2 KiB of U */
-                warm_l2(r + KDA_REC_U + nt * 2048 + l * 16, lds);
-                warm_l2(r + KDA_REC_U + nt * 2048 + 1024 + l * 16, lds);
-            }
-            chunk_barrier();
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-}
-
-/* ------------------------------------------------------------------------- */
 /* launchers (called by kda_api.cpp after validation)                          */
 /* ------------------------------------------------------------------------- */
 extern "C" hipError_t kda_launch_chunk_map(const int32_t *cu, int64_t nseq, int32_t *chunk_off, hipStream_t st)
@@ -849,15 +481,3 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
     return hipGetLastError();
 }
 
-extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
-                                      int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
-                                      const void *init_state, void *final_state, int state_fp32,
-                                      void *sink, hipStream_t st)
-{
-    const int64_t nchain = nseq * H;
-    const int64_t blocks = (nchain + 7) / 8 * 64;
-    hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)blocks), dim3(192), 0, st,
-                       (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H, nslots,
-                       (uint16_t *)out, init_state, final_state, state_fp32, (uint16_t *)sink);
-    return hipGetLastError();
-}

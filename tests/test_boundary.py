@@ -34,7 +34,7 @@ def test_status_strings():
 
 
 def test_workspace_size():
-    rec, sink = 72192, 2048
+    rec, sink = 72192, 0
     assert kda.workspace_size(1, 65536, 32) == sink + 1024 * 32 * rec
     assert kda.workspace_size(4, 2048, 16) == sink + 4 * 32 * 16 * rec
     assert kda.workspace_size(1, 100, 2) == sink + 2 * 2 * rec

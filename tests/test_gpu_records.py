@@ -18,7 +18,7 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 REC = dict(W=0, Q=16384, KT=32768, P=49152, GL=55296, U=55808, BYTES=72192)
-SINK = 2048   # the workspace starts with a 2 KiB sink, then (no cu_seqlens) the records
+SINK = 0      # without cu_seqlens the workspace starts with the records
 
 
 def kperm(g, i):
