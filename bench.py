@@ -15,6 +15,7 @@ workload; the oracle's output on that prefix is also compared with the GPU's.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0..4]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,13 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 # algorithmic HBM bytes per token-head: q, k, g, v reads (4 x 256), out write (256), beta (2)
 PREP_BYTES_PER_TH = 4 * 256 + 2
 SCAN_BYTES_PER_TH = 256
+# HBM bytes per launch read from rocprofv3 FETCH_SIZE / WRITE_SIZE counters,
+# scaled by the same counters' reading for a device copy of known size; valid
+# only while the kernel's sources hash to the recorded value
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+CSRC = os.path.join(ROOT, "kimi_delta_attention_fwd_amd", "csrc")
+KERNEL_SOURCES = {"kda_prep": ("kda_prep.hip", "kda_device.h", "kda_internal.h"),
+                  "kda_scan": ("kda_scan.hip", "kda_device.h", "kda_internal.h")}
 # algorithmic MFMA flops per token-head with 16x16 blocks and 64-token chunks:
 # state-side 6*K*V + intra-chunk 2*C*(3K + 2V)
 FLOPS_PER_TH = 6 * 128 * 128 + 2 * 64 * (3 * 128 + 2 * 128)
@@ -43,6 +51,28 @@ def state_bytes(d):
     return n * d["N"] * d["H"] * per
 
 
+def kernel_source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, ()):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of ``kernel`` on ``workload`` from the counter
+    summary, or None if there is none for the current sources."""
+    if kernel not in KERNEL_SOURCES or not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = kernel_source_hash(kernel)
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
+            if f.get("kernel") == kernel and f.get("workload") == workload and f.get("src") == want:
+                return float(f["hbm_bytes"])
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -52,6 +82,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768,
                     help="prefix length on which the oracle is timed (all heads)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, run 3 device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -110,6 +142,14 @@ def main():
     th = ki.token_heads(d)
     value = th * args.steps / wall
 
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # per-kernel live timing (hipEvents on the launch stream)
     kernels = {name: tot / cnt for name, (tot, cnt) in prof.items()}
     alg_bytes = {"kda_prep": th * PREP_BYTES_PER_TH,
@@ -140,7 +180,7 @@ def main():
             " varlen N=%d" % d["N"] if cu is not None else ""),
             "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom,
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(dom, d["name"]), "kernel": dom,
                      "kernel_ms": dom_ms, "alg_bytes_per_launch": alg_bytes.get(dom, 0)},
         "kernels_ms": kernels,
         "path_roofline": {"bound": "hbm", "alg_bytes_per_step": path_bytes, "achieved_GBs": path_gbs,
