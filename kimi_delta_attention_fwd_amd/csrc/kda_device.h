@@ -12,6 +12,7 @@
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define LOG2E_F 1.4426950408889634f
 #define LN2_F 0.6931471805599453f
@@ -48,6 +49,16 @@ __device__ __forceinline__ bf16x8 pack8f(const float *x)
 #pragma unroll
     for (int i = 0; i < 8; i++) r[i] = (__bf16)x[i];
     return r;
+}
+
+#define KDA_BUF_FLAGS 0x00020000 /* raw buffer, 32-bit data format (gfx9 family) */
+
+/* Buffer descriptor over [base, base + bytes): the base lives in SGPRs, lanes
+   pass 32-bit byte offsets, loads past the end return 0 and stores past the end
+   are dropped by the hardware range check. */
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)bytes, KDA_BUF_FLAGS);
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }

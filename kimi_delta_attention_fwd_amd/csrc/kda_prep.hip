@@ -103,9 +103,8 @@ __device__ __forceinline__ void store_transposed(const bf16x8 &fr, const bf16x8 
 }
 
 extern "C" __global__ void __launch_bounds__(256, 2)
-kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                const uint16_t *__restrict__ v, const uint16_t *__restrict__ gt,
-                const uint16_t *__restrict__ beta, const float *__restrict__ A_log,
+kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gt,
+                const uint16_t *beta, const float *__restrict__ A_log,
                 const float *__restrict__ dt_bias, float scale, float lower_bound,
                 const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
                 int64_t nseq, int64_t T, int H, int64_t nslots, unsigned char *__restrict__ rec_base)
@@ -121,34 +120,51 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, r16 = l & 15;
     const int r = 16 * w + r16;
     const bool valid = r < L;
-    const size_t row = (size_t)(t0 + (valid ? r : 0)) * H + h;
 
     /* ---- phase A: load this lane's token row, norms, gate, cumsum ---- */
+    /* Token rows past the chunk end fall outside the descriptors' ranges and load
+       as zeros, so every lane loads unconditionally (no branch, no early wait). */
+    const size_t act0 = ((size_t)t0 * H + h) * KDA_DK; /* element offset of (t0, h, 0) */
+    const uint32_t row_bytes = (uint32_t)H * KDA_DK * 2;
+    const uint32_t act_bytes = (uint32_t)(L - 1) * row_bytes + KDA_DK * 2;
+    const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + act0, act_bytes), rk = buf_rsrc(k + act0, act_bytes);
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gt + act0, act_bytes), rv = buf_rsrc(v + act0, act_bytes);
+    const __amdgpu_buffer_rsrc_t rb = buf_rsrc(beta + (size_t)t0 * H + h, (uint32_t)(L - 1) * H * 2 + 2);
+    const uint32_t voff = (uint32_t)r * row_bytes;
     float qf[32], kf[32], la[32];
     bf16x8 vfr[4];
-    const float bt = valid ? bf2f(beta[row]) : 0.f;
+    const float bt = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)r * H * 2, 0, 0));
     const float decay_rate = __expf(A_log[h]);
     const float lb2 = lower_bound * LOG2E_F;
+    u32x2 uqa[8], uka[8], uga[8], uva[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const uint32_t o = voff + (uint32_t)(32 * (i >> 1) + 16 * (i & 1) + 4 * g) * 2;
+        uqa[i] = __builtin_amdgcn_raw_buffer_load_b64(rq, o, 0, 0);
+        uka[i] = __builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, 0);
+        uga[i] = __builtin_amdgcn_raw_buffer_load_b64(rg, o, 0, 0);
+        uva[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, o, 0, 0);
+    }
+    /* All 33 loads are in flight before any of them is consumed. (The activation
+       pointers are deliberately not __restrict__: loads through restrict const
+       pointers count as invariant, and the compiler then re-issues some of them
+       next to their late first use, which costs a second memory round trip.) */
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
 #pragma unroll
         for (int half = 0; half < 2; half++) {
             const int ch0 = 32 * kb + 16 * half + 4 * g;
             const int j0 = kb * 8 + half * 4;
-            uint2 uq = make_uint2(0, 0), uk = uq, ug = uq, uv = uq;
-            if (valid) {
-                uq = *(const uint2 *)(q + row * KDA_DK + ch0);
-                uk = *(const uint2 *)(k + row * KDA_DK + ch0);
-                ug = *(const uint2 *)(gt + row * KDA_DK + ch0);
-                uv = *(const uint2 *)(v + row * KDA_DV + ch0);
-            }
+            const u32x2 uq = uqa[2 * kb + half], uk = uka[2 * kb + half], ug = uga[2 * kb + half];
+            const u32x2 uv = uva[2 * kb + half];
             const float4 db = *(const float4 *)(dt_bias + (size_t)h * KDA_DK + ch0);
-            const uint32_t wq[2] = {uq.x, uq.y}, wk[2] = {uk.x, uk.y}, wg[2] = {ug.x, ug.y};
+            const uint32_t wq[2] = {uq[0], uq[1]}, wk[2] = {uk[0], uk[1]}, wg[2] = {ug[0], ug[1]};
             const float dbs[4] = {db.x, db.y, db.z, db.w};
-            vfr[kb][half * 4 + 0] = __builtin_bit_cast(__bf16, (uint16_t)(uv.x & 0xffff));
-            vfr[kb][half * 4 + 1] = __builtin_bit_cast(__bf16, (uint16_t)(uv.x >> 16));
-            vfr[kb][half * 4 + 2] = __builtin_bit_cast(__bf16, (uint16_t)(uv.y & 0xffff));
-            vfr[kb][half * 4 + 3] = __builtin_bit_cast(__bf16, (uint16_t)(uv.y >> 16));
+            vfr[kb][half * 4 + 0] = __builtin_bit_cast(__bf16, (uint16_t)(uv[0] & 0xffff));
+            vfr[kb][half * 4 + 1] = __builtin_bit_cast(__bf16, (uint16_t)(uv[0] >> 16));
+            vfr[kb][half * 4 + 2] = __builtin_bit_cast(__bf16, (uint16_t)(uv[1] & 0xffff));
+            vfr[kb][half * 4 + 3] = __builtin_bit_cast(__bf16, (uint16_t)(uv[1] >> 16));
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int sh16 = (e & 1) * 16;
@@ -170,11 +186,14 @@ kda_prep_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const float iq = scale / sqrtf(sq + 1e-6f), ik = 1.f / sqrtf(sk + 1e-6f);
 #pragma unroll
     for (int j = 0; j < 32; j++) la[j] = row_scan16(la[j]);
+    if (r16 == 7 || r16 == 15) {
+        float *dst = (r16 == 15) ? sh.u.p1.tot[w] : sh.u.p1.mid[w];
 #pragma unroll
-    for (int j = 0; j < 32; j++) {
-        const int ch = 32 * (j >> 3) + kperm(g, j & 7);
-        if (r16 == 15) sh.u.p1.tot[w][ch] = la[j];
-        if (r16 == 7) sh.u.p1.mid[w][ch] = la[j];
+        for (int kb = 0; kb < 4; kb++) {
+            *(float4 *)&dst[32 * kb + 4 * g] = make_float4(la[8 * kb], la[8 * kb + 1], la[8 * kb + 2], la[8 * kb + 3]);
+            *(float4 *)&dst[32 * kb + 16 + 4 * g] =
+                make_float4(la[8 * kb + 4], la[8 * kb + 5], la[8 * kb + 6], la[8 * kb + 7]);
+        }
     }
     if (g == 0) sh.beta[r] = bt;
     __syncthreads();

@@ -35,14 +35,10 @@ struct ScanSetO {
     bf16x8 Q[16], P[6], U[2];
 };
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-#define KDA_BUF_FLAGS 0x00020000 /* raw buffer, 32-bit data format (gfx9 family) */
-
 /* buffer descriptor over one chunk record: SGPR base, lane offsets in VGPRs */
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const unsigned char *rec)
 {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)rec, 0, KDA_REC_BYTES, KDA_BUF_FLAGS);
+    return buf_rsrc(rec, KDA_REC_BYTES);
 }
 
 __device__ __forceinline__ bf16x8 bufld(__amdgpu_buffer_rsrc_t r, int voff, int soff)
@@ -143,13 +139,13 @@ __device__ __forceinline__ void output_step(ScanSetO &X, ScanSetO &Y, const unsi
 #pragma unroll
         for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(X.U[jb], X.P[KDA_PIDX(mt, jb)], O[mt]);
     const int row_bytes = H * KDA_DV * 2;
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(out + ((size_t)t0 * H + h) * KDA_DV), 0, (L - 1) * row_bytes + KDA_DV * 2, KDA_BUF_FLAGS);
+    const __amdgpu_buffer_rsrc_t ro =
+        buf_rsrc(out + ((size_t)t0 * H + h) * KDA_DV, (uint32_t)((L - 1) * row_bytes + KDA_DV * 2));
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
-        i32x2 u;
-        u[0] = (int)(f2bf_bits(O[mt][0]) | ((uint32_t)f2bf_bits(O[mt][1]) << 16));
-        u[1] = (int)(f2bf_bits(O[mt][2]) | ((uint32_t)f2bf_bits(O[mt][3]) << 16));
+        u32x2 u;
+        u[0] = f2bf_bits(O[mt][0]) | ((uint32_t)f2bf_bits(O[mt][1]) << 16);
+        u[1] = f2bf_bits(O[mt][2]) | ((uint32_t)f2bf_bits(O[mt][3]) << 16);
         __builtin_amdgcn_raw_buffer_store_b64(u, ro, (16 * mt + n16) * row_bytes + (16 * nt + 4 * g) * 2, 0, 0);
     }
 }
