@@ -64,27 +64,39 @@ kda_chunk_map_kernel(const int32_t *__restrict__ cu, int64_t nseq, int32_t *__re
  * beta enters through A's rows and through T's columns (TB = T diag(beta)):
  * W = TB (K^ o e^G), U = TB V.
  */
+#define KDA_TS 68 /* row stride (floats) of the fp32 64x64 tiles: 16-byte rows, rows spread over the banks */
+
 struct PrepShared {
-    float fq[4][KDA_DK];      /* 2^{Gm_w}                                              */
-    float fk[4][KDA_DK];      /* 2^{G_L - Gm_w}                                        */
-    float fm[4][KDA_DK];      /* 2^{m_w}                                               */
-    float fy[6][KDA_DK];      /* 2^{B_i - Gm_b}, pair (i, b) -> i (i - 1) / 2 + b        */
     float beta[KDA_CHUNK];
     union {
-        struct {
+        struct { /* phases A-D */
             float tot[4][KDA_DK]; /* in-sub-chunk inclusive cumsum at token 15 (log2)  */
             float mid[4][KDA_DK]; /* ... at token 7 (the anchor m_w)                    */
-            bf16x8 yd[4][4][64];  /* diagonal key side k^ 2^{m_w - c}, per sub-chunk   */
+            float fq[4][KDA_DK];  /* 2^{Gm_w}                                           */
+            float fk[4][KDA_DK];  /* 2^{G_L - Gm_w}                                     */
+            float fm[4][KDA_DK];  /* 2^{m_w}                                            */
+            float fy[6][KDA_DK];  /* 2^{B_i - Gm_b}, pair (i, b) -> i (i - 1) / 2 + b     */
+            bf16x8 yd[4][4][64];  /* diagonal key side k^ 2^{m_w - c}, per sub-chunk    */
         } p1;
-        struct {
-            float t[KDA_CHUNK][KDA_CHUNK]; /* T = (I + A)^-1, lower blocks only          */
-            float m[1024];                 /* block products of the recursive inverse   */
+        struct { /* phases E-F */
+            float t[KDA_CHUNK][KDA_TS]; /* T = (I + A)^-1, blocks on or below the diagonal */
+            bf16x8 tbt[6][64];          /* (T diag(beta))^T fragments, index kda_tbt_idx  */
         } p2;
     } u;
     bf16x8 rt[8][2][64];      /* R^T fragments (key tile, token block)                 */
     bf16x8 vt[8][2][64];      /* V^T fragments (value tile, token block)               */
-    float a[KDA_CHUNK][KDA_CHUNK]; /* A (strictly lower; beta_r on row r)              */
+    float a[KDA_CHUNK][KDA_TS]; /* A (strictly lower; beta_r on row r)                 */
 };
+
+/* (T diag(beta))^T fragment (column block jt, row block pair jb): lane = column
+   16 jt + l % 16, 8 values over rows 32 jb + kperm(l / 16, i); only jb >= jt / 2 is
+   nonzero */
+__device__ __forceinline__ int kda_tbt_idx(int jt, int jb) { return jt < 2 ? 2 * jt + jb : 2 + jt; }
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 /* R-form fragment (lane = token, 8 values over a 32-wide block) -> C-form 16x16 tile
    (lane = column of the block, 4 regs = tokens 4 g + e) with a 0/1 selector MFMA */
@@ -209,9 +221,9 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
             GL += tm;
         }
         const float gm = B + sh.u.p1.mid[ww][ch];
-        sh.fq[ww][ch] = exp2_fast(gm);
-        sh.fk[ww][ch] = exp2_fast(GL - gm);
-        sh.fm[ww][ch] = exp2_fast(sh.u.p1.mid[ww][ch]);
+        sh.u.p1.fq[ww][ch] = exp2_fast(gm);
+        sh.u.p1.fk[ww][ch] = exp2_fast(GL - gm);
+        sh.u.p1.fm[ww][ch] = exp2_fast(sh.u.p1.mid[ww][ch]);
         if (ww == 0) ((float *)(rec + KDA_REC_GL))[ch] = exp2_fast(GL);
     }
     for (int p = tid; p < 6 * KDA_DK; p += 256) {
@@ -224,7 +236,7 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
             Bi += tm;
             if (m < b) Bb += tm;
         }
-        sh.fy[pp][ch] = exp2_fast(Bi - (Bb + sh.u.p1.mid[b][ch]));
+        sh.u.p1.fy[pp][ch] = exp2_fast(Bi - (Bb + sh.u.p1.mid[b][ch]));
     }
     __syncthreads();
 
@@ -248,7 +260,7 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
                 const float e1 = exp2_fast(d), e2 = exp2_fast(-d);
                 const float kh = kf[j] * ik;
                 const float xk = kh * e1, xq = qf[j] * iq * e1, ykv = kh * e2;
-                const float fq = sh.fq[w][ch], fm = sh.fm[w][ch];
+                const float fq = sh.u.p1.fq[w][ch], fm = sh.u.p1.fm[w][ch];
                 xok_f[kb][i] = (__bf16)(xk * fm); /* k^ 2^{c}: anchored at the sub-chunk start */
                 xoq_f[kb][i] = (__bf16)(xq * fm);
                 xdk_f[kb][i] = (__bf16)xk;
@@ -256,7 +268,7 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
                 yd_f[kb][i] = (__bf16)ykv;
                 qt_f[kb][i] = (__bf16)(xq * fq);
                 rf[i] = (__bf16)(xk * fq);
-                kt[i] = (__bf16)(ykv * sh.fk[w][ch]);
+                kt[i] = (__bf16)(ykv * sh.u.p1.fk[w][ch]);
             }
             sh.u.p1.yd[w][kb][l] = yd_f[kb];
             /* key tiles 2 kb and 2 kb + 1 of R, V and K~ */
@@ -284,7 +296,7 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
         }
         for (int b = 0; b < w; b++) {
             /* key side k^_j 2^{m_b - c_j} 2^{B_w - Gm_b} = k^_j 2^{B_w - G_j} <= 1 */
-            const float *fy = sh.fy[w * (w - 1) / 2 + b];
+            const float *fy = sh.u.p1.fy[w * (w - 1) / 2 + b];
             f32x4 ta = zero4(), tp = zero4();
 #pragma unroll
             for (int kb = 0; kb < 4; kb++) {
@@ -333,11 +345,10 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
     }
     __syncthreads(); /* A visible; p1 (tot/mid/yd) dead from here on */
 
-    /* ---- phase E: T = (I + A)^-1 by 2-level block recursion in fp32 ---- */
-    float(*tt)[KDA_CHUNK] = sh.u.p2.t;
-    float *mm = sh.u.p2.m;
+    /* ---- phase E: T = (I + A)^-1 in fp32 ---- */
+    float(*tt)[KDA_TS] = sh.u.p2.t;
     {
-        /* level 0: 16x16 diagonal blocks by forward substitution (column c per lane) */
+        /* 16x16 diagonal blocks by forward substitution (column c per lane) */
         const int c = r16;
         float x[16];
 #pragma unroll
@@ -353,53 +364,53 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
         }
     }
     __syncthreads();
-    /* level 1: T_10 = -T_11 (A_10 T_00), T_32 = -T_33 (A_32 T_22); waves 0,1 / 2,3 */
+    /* Block column w below the diagonal, by block forward substitution with fp32
+       MFMAs: T_iw = -T_ii sum_{w <= k < i} A_ik T_kw. Blocks are held in the 16x16
+       accumulator layout (lane = column, 4 registers = rows 4 g + e), which is also
+       the B-operand layout when the contraction index is split as 4 g + s over the
+       4 steps s; A operands are rows of A and T_ii read 4 at a time from LDS. */
     {
-        const int pr = w >> 1;                 /* block pair: rows 16 (2 pr + 1), cols 16 (2 pr) */
-        const int rr = 8 * (w & 1) + (l >> 3); /* row inside the 16x16 block */
-        const int cc = 2 * (l & 7);            /* two columns */
-        const int R0 = 16 * (2 * pr + 1), C0 = 16 * (2 * pr);
-        float a0 = 0.f, a1 = 0.f;
+        f32x4 tb[4];
 #pragma unroll
-        for (int kk = 0; kk < 16; kk++) {
-            const float av = sh.a[R0 + rr][C0 + kk];
-            a0 += av * tt[C0 + kk][C0 + cc];
-            a1 += av * tt[C0 + kk][C0 + cc + 1];
-        }
-        mm[pr * 256 + rr * 16 + cc] = a0;
-        mm[pr * 256 + rr * 16 + cc + 1] = a1;
-        __syncthreads();
-        float b0 = 0.f, b1 = 0.f;
+        for (int e = 0; e < 4; e++) tb[w][e] = tt[16 * w + 4 * g + e][16 * w + r16];
 #pragma unroll
-        for (int kk = 0; kk < 16; kk++) {
-            const float tv = tt[R0 + rr][R0 + kk];
-            b0 += tv * mm[pr * 256 + kk * 16 + cc];
-            b1 += tv * mm[pr * 256 + kk * 16 + cc + 1];
+        for (int i = 1; i < 4; i++) {
+            if (i <= w) continue;
+            f32x4 xs = zero4();
+#pragma unroll
+            for (int kk = 0; kk < i; kk++) {
+                if (kk < w) continue;
+                const float4 av = *(const float4 *)&sh.a[16 * i + r16][16 * kk + 4 * g];
+                xs = mfma_f32(av.x, tb[kk][0], xs);
+                xs = mfma_f32(av.y, tb[kk][1], xs);
+                xs = mfma_f32(av.z, tb[kk][2], xs);
+                xs = mfma_f32(av.w, tb[kk][3], xs);
+            }
+            const float4 tv = *(const float4 *)&tt[16 * i + r16][16 * i + 4 * g];
+            f32x4 y = zero4();
+            y = mfma_f32(tv.x, xs[0], y);
+            y = mfma_f32(tv.y, xs[1], y);
+            y = mfma_f32(tv.z, xs[2], y);
+            y = mfma_f32(tv.w, xs[3], y);
+            tb[i] = -y;
         }
-        tt[R0 + rr][C0 + cc] = -b0;
-        tt[R0 + rr][C0 + cc + 1] = -b1;
-    }
-    __syncthreads();
-    /* level 2: T_BA = -T_B (A_BA T_A), 32x32 blocks (B = rows 32..63, A = cols 0..31) */
-    {
-        const int i = tid >> 3, j4 = 4 * (tid & 7);
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        const int m0 = j4 < 16 ? 0 : 16; /* T_A is zero above its block diagonal */
-        for (int m = m0; m < 32; m++) {
-            const float av = sh.a[32 + i][m];
-            const float4 tv = *(const float4 *)&tt[m][j4];
-            acc[0] += av * tv.x; acc[1] += av * tv.y; acc[2] += av * tv.z; acc[3] += av * tv.w;
+        /* off-diagonal blocks to LDS (rows of T for the W and U operands) */
+#pragma unroll
+        for (int i = 1; i < 4; i++) {
+            if (i <= w) continue;
+#pragma unroll
+            for (int e = 0; e < 4; e++) tt[16 * i + 4 * g + e][16 * w + r16] = tb[i][e];
         }
-        *(float4 *)&mm[i * 32 + j4] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        __syncthreads();
-        float bcc[4] = {0.f, 0.f, 0.f, 0.f};
-        const int m1 = i < 16 ? 16 : 32; /* T_B row i is zero beyond its block */
-        for (int m = 0; m < m1; m++) {
-            const float tv = tt[32 + i][32 + m];
-            const float4 yv = *(const float4 *)&mm[m * 32 + j4];
-            bcc[0] += tv * yv.x; bcc[1] += tv * yv.y; bcc[2] += tv * yv.z; bcc[3] += tv * yv.w;
+        /* (T diag(beta))^T fragments of column block w; blocks above the diagonal are 0 */
+        const float bj = sh.beta[16 * w + r16];
+#pragma unroll
+        for (int jb = 0; jb < 2; jb++) {
+            if (jb < (w >> 1)) continue;
+            f32x4 lo = zero4(), hi = zero4();
+            if (2 * jb >= w) lo = tb[2 * jb] * bj;
+            if (2 * jb + 1 >= w) hi = tb[2 * jb + 1] * bj;
+            sh.u.p2.tbt[kda_tbt_idx(w, jb)][l] = pack8(lo, hi);
         }
-        *(float4 *)&tt[32 + i][j4] = make_float4(-bcc[0], -bcc[1], -bcc[2], -bcc[3]);
     }
     __syncthreads();
 
@@ -407,12 +418,16 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
     const int nkb = (w >= 2) ? 2 : 1; /* token blocks holding j <= 16 w + 15 */
     bf16x8 tbf[2];
 #pragma unroll
-    for (int jb = 0; jb < 2; jb++)
+    for (int jb = 0; jb < 2; jb++) {
+        if (jb >= nkb) { tbf[jb] = pack8(zero4(), zero4()); continue; }
+        const int j0 = 32 * jb + 4 * g, j1 = j0 + 16;
+        const float4 t0v = *(const float4 *)&tt[r][j0], t1v = *(const float4 *)&tt[r][j1];
+        const float4 b0v = *(const float4 *)&sh.beta[j0], b1v = *(const float4 *)&sh.beta[j1];
+        const float tv[8] = {t0v.x * b0v.x, t0v.y * b0v.y, t0v.z * b0v.z, t0v.w * b0v.w,
+                             t1v.x * b1v.x, t1v.y * b1v.y, t1v.z * b1v.z, t1v.w * b1v.w};
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int j = 32 * jb + kperm(g, i);
-            tbf[jb][i] = (__bf16)((j <= r) ? tt[r][j] * sh.beta[j] : 0.f);
-        }
+        for (int i = 0; i < 8; i++) tbf[jb][i] = (__bf16)((32 * jb + kperm(g, i) <= r) ? tv[i] : 0.f);
+    }
     /* W (stored negated), lane = token, regs = key channel */
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
@@ -442,20 +457,11 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
 #pragma unroll
     for (int jt = 0; jt < 4; jt++) {
         ptt[jt] = zero4();
-        if (jt <= w) {
-            const int jp = 16 * jt + r16;
-            const float bj = sh.beta[jp];
+        if (jt > w) continue;
 #pragma unroll
-            for (int jb = 0; jb < 2; jb++) {
-                if (jb >= nkb) continue;
-                bf16x8 tc;
-#pragma unroll
-                for (int i = 0; i < 8; i++) {
-                    const int j = 32 * jb + kperm(g, i);
-                    tc[i] = (__bf16)((jp <= j) ? tt[j][jp] * bj : 0.f);
-                }
-                ptt[jt] = mfma(tc, pf[jb], ptt[jt]);
-            }
+        for (int jb = 0; jb < 2; jb++) {
+            if (jb >= nkb || jb < (jt >> 1)) continue;
+            ptt[jt] = mfma(sh.u.p2.tbt[kda_tbt_idx(jt, jb)][l], pf[jb], ptt[jt]);
         }
     }
     bf16x8 ptf[2];
