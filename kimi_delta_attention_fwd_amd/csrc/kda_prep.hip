@@ -169,26 +169,24 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
             const int ch0 = 32 * kb + 16 * half + 4 * g;
             const int j0 = kb * 8 + half * 4;
             const u32x2 uq = uqa[2 * kb + half], uk = uka[2 * kb + half], ug = uga[2 * kb + half];
-            const u32x2 uv = uva[2 * kb + half];
             const float4 db = *(const float4 *)(dt_bias + (size_t)h * KDA_DK + ch0);
             const uint32_t wq[2] = {uq[0], uq[1]}, wk[2] = {uk[0], uk[1]}, wg[2] = {ug[0], ug[1]};
             const float dbs[4] = {db.x, db.y, db.z, db.w};
-            vfr[kb][half * 4 + 0] = __builtin_bit_cast(__bf16, (uint16_t)(uv[0] & 0xffff));
-            vfr[kb][half * 4 + 1] = __builtin_bit_cast(__bf16, (uint16_t)(uv[0] >> 16));
-            vfr[kb][half * 4 + 2] = __builtin_bit_cast(__bf16, (uint16_t)(uv[1] & 0xffff));
-            vfr[kb][half * 4 + 3] = __builtin_bit_cast(__bf16, (uint16_t)(uv[1] >> 16));
 #pragma unroll
             for (int e = 0; e < 4; e++) {
                 const int sh16 = (e & 1) * 16;
                 qf[j0 + e] = bf2f((uint16_t)(wq[e >> 1] >> sh16));
                 kf[j0 + e] = bf2f((uint16_t)(wk[e >> 1] >> sh16));
-                const float x = bf2f((uint16_t)(wg[e >> 1] >> sh16)) + dbs[e];
-                /* softplus(x) = max(x, 0) + ln(1 + e^{-|x|}) */
-                const float sp = fmaxf(x, 0.f) + log2_fast(1.f + exp2_fast(-fabsf(x) * LOG2E_F)) * LN2_F;
-                const float l2 = fmaxf(-decay_rate * sp * LOG2E_F, lb2);
+                /* log2 a = max(-exp(A_log) softplus(x) log2(e), lower_bound log2(e)) with
+                   softplus(x) log2(e) = max(t, 0) + log2(1 + 2^{-|t|}),  t = x log2(e) */
+                const float t = (bf2f((uint16_t)(wg[e >> 1] >> sh16)) + dbs[e]) * LOG2E_F;
+                const float sp2 = fmaxf(t, 0.f) + log2_fast(1.f + exp2_fast(-fabsf(t)));
+                const float l2 = fmaxf(-decay_rate * sp2, lb2);
                 la[j0 + e] = valid ? l2 : 0.f; /* padded rows: no decay */
             }
         }
+        /* v stays in bf16: its two 4-channel pieces are operand slots 0..3 and 4..7 */
+        vfr[kb] = __builtin_bit_cast(bf16x8, u32x4{uva[2 * kb][0], uva[2 * kb][1], uva[2 * kb + 1][0], uva[2 * kb + 1][1]});
     }
     float sq = 0.f, sk = 0.f;
 #pragma unroll
