@@ -82,6 +82,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768,
                     help="prefix length on which the oracle is timed (all heads)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the single-token decode step instead (512 sequences x 64 heads, fp32 state)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run 3 device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -98,6 +100,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     kda.load_library()
+    if args.decode:
+        return run_decode(args)
     dev = "cuda:0"
     t_gen = time.time()
     d = ki.config_inputs(args.config)
@@ -211,6 +215,78 @@ def main():
                                          "same workload (%d token-heads, %.1f s)" % (sub["T"], H, sample_th, tc)}
         res["parity_sample"] = {"rel_l2": oracle.rel_l2(got, ro), "max_abs": oracle.max_abs(got, ro),
                                 "tokens": sub["T"]}
+    print(json.dumps(res), flush=True)
+
+
+DECODE_N, DECODE_H = 512, 64
+
+
+def run_decode(args):
+    """One kda_decode call per step on 512 sequences x 64 heads with an fp32
+    state updated in place (the decode neighbour of the continuation workload).
+    Algorithmic bytes per (sequence, head): the fp32 state read and written
+    (2 x 64 KiB), q, k, v, g read and out written (5 x 256 B), beta (2 B)."""
+    import numpy as np
+    import torch
+
+    import kda_inputs as ki
+    import kimi_delta_attention_fwd_amd as kda
+
+    dev = "cuda:0"
+    N, H = DECODE_N, DECODE_H
+    d = ki.make_inputs(1, N, H, seed=0, lengths=[1] * N, lower_bound=-5.0, state="fp32", initial=True,
+                       sigma=0.05)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, g, beta = (bf(d[x][0]) for x in ("q", "k", "v", "g", "beta"))
+    A_log = torch.from_numpy(d["A_log"]).to(dev)
+    dt_bias = torch.from_numpy(d["dt_bias"]).to(dev)
+    state = torch.from_numpy(d["initial_state"]).to(dev)
+    out = torch.empty_like(q)
+    state0 = state.clone()
+
+    def step():
+        kda.decode(q, k, v, g, beta, d["scale"], out, A_log, dt_bias, d["lower_bound"], state)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kda.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kda.profile_enable(False)
+    prof = kda.profile_read()
+    kern_ms = prof["kda_decode"][0] / prof["kda_decode"][1]
+    units = N * H
+    alg = units * (2 * 128 * 128 * 4 + 5 * 256 + 2) + H * 4 + H * 128 * 4
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": "KDA decode step tokens*heads/s (one token per sequence, state in place)",
+        "value": units * args.steps / wall, "unit": "token*heads/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded numpy draws)",
+        "config": {"workload": "decode: N=%d sequences x H=%d heads, one token each, fp32 state" % (N, H),
+                   "global_batch": N, "seq_len": 1, "heads": H, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "kda_decode",
+                     "kernel_ms": kern_ms, "alg_bytes_per_launch": alg},
+    }
+    if not args.no_cpu:
+        import oracle
+        tc0 = time.perf_counter()
+        ro, rf = oracle.fwd_inputs(d, want_final=True)
+        tc = time.perf_counter() - tc0
+        res["cpu_baseline"] = {"value": units / tc, "unit": "token*heads/s", "cores": oracle.max_threads(),
+                               "kind": "oracle", "sample": "fp64 recurrence on the whole workload (%d "
+                               "token-heads, %.2f s)" % (units, tc)}
+        # parity of one step from the initial state
+        state.copy_(state0)
+        step()
+        torch.cuda.synchronize()
+        res["parity_sample"] = {"rel_l2": oracle.rel_l2(out.float().cpu().numpy(), ro[0]),
+                                "state_rel_l2": oracle.rel_l2(state.cpu().numpy(), rf)}
     print(json.dumps(res), flush=True)
 
 

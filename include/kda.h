@@ -52,7 +52,7 @@ extern "C" {
 #define KDA_API __attribute__((visibility("default")))
 #endif
 
-/* Status codes returned by kda_fwd. */
+/* Status codes returned by kda_fwd and kda_decode. */
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL = 1,        /* a required pointer is NULL                         */
@@ -123,12 +123,38 @@ KDA_API int kda_fwd(const void *q, const void *k, const void *v, const void *g,
  */
 KDA_API size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t num_seqs);
 
+/*
+ * kda_decode -- one token per sequence: the single-token step of the same
+ * recurrence with the state updated in place (the decode use of flash_kda.fwd
+ * with T = 1 per sequence; the pages' argument list and state constraints as
+ * for kda_fwd). No chunking is involved, so any finite lower_bound <= 0 is
+ * accepted and no workspace is needed.
+ *
+ *  q, k, v, g : bf16 [N, H, 128] (token of sequence n);  beta : bf16 [N, H]
+ *  out        : bf16 [N, H, 128], written in full (round to nearest even);
+ *               must not overlap an input or the state.
+ *  scale, A_log, dt_bias : as for kda_fwd.
+ *  lower_bound: clamp of log a in natural-log units, finite and <= 0.
+ *  state      : [N, H, 128(K), 128(V)] of state_dtype (KDA_STATE_BF16 or
+ *               KDA_STATE_FP32), read and overwritten with the state after the
+ *               token (bf16 rounded to nearest even from fp32); must not
+ *               overlap an input.
+ *  N, H, K, V : sizes; K and V must be 128.
+ *  stream     : hipStream_t (as void*); NULL means the default stream.
+ * Errors as for kda_fwd (KDA_ERR_STATE_DTYPE if state_dtype is NONE or
+ * unknown, KDA_ERR_NULL if state is NULL); nothing is enqueued on error.
+ */
+KDA_API int kda_decode(const void *q, const void *k, const void *v, const void *g,
+               const void *beta, float scale, void *out, const float *A_log,
+               const float *dt_bias, float lower_bound, void *state, int state_dtype,
+               int64_t N, int64_t H, int64_t K, int64_t V, void *stream);
+
 /* Static, NUL-terminated description of a kda_status code (host only). */
 KDA_API const char *kda_status_string(int status);
 
 /*
  * Kernel-level timing for measurement tools (host only, not thread-safe).
- *  kda_profile_enable(1) clears the record and makes later kda_fwd calls
+ *  kda_profile_enable(1) clears the record and makes later kda_fwd / kda_decode calls
  *  bracket each kernel they enqueue with hipEvents on the call's stream (up to
  *  8192 launches); kda_profile_enable(0) stops recording. kda_profile_read
  *  synchronises on the recorded events and aggregates them per kernel: it

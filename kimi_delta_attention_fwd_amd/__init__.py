@@ -16,7 +16,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "workspace_size", "status_string", "library_path", "load_library",
+__all__ = ["fwd", "decode", "workspace_size", "status_string", "library_path", "load_library",
            "profile_enable", "profile_read", "KDA_LOWER_BOUND_MIN", "KdaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -25,7 +25,7 @@ _lib = None
 
 KDA_STATE_NONE, KDA_STATE_BF16, KDA_STATE_FP32 = 0, 1, 2
 KDA_LOWER_BOUND_MIN = -10.0
-EXPORTED = ("kda_fwd", "kda_fwd_workspace_size", "kda_status_string",
+EXPORTED = ("kda_fwd", "kda_decode", "kda_fwd_workspace_size", "kda_status_string",
             "kda_profile_enable", "kda_profile_read")
 
 
@@ -50,6 +50,9 @@ def load_library():
     lib.kda_fwd.restype = ctypes.c_int
     lib.kda_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_float, P, P,
                             ctypes.c_int, P, I64, I64, I64, I64, I64, I64, P, ctypes.c_size_t, P]
+    lib.kda_decode.restype = ctypes.c_int
+    lib.kda_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_float, P, ctypes.c_int,
+                               I64, I64, I64, I64, P]
     lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_fwd_workspace_size.argtypes = [I64, I64, I64, I64]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -185,6 +188,63 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
                      _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
                      _ptr(final_state), sd, _ptr(cu_seqlens), num_seqs, B, T, H, K, V,
                      _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
+    if rc == 0:
+        return out
+    msg = lib.kda_status_string(rc).decode()
+    if rc == 8:
+        raise KdaError(msg)
+    raise ValueError(msg)
+
+
+def decode(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, state):
+    """One token per sequence, state updated in place, on the current torch stream.
+
+    q, k, v, g, out: bf16 [N, H, 128]; beta: bf16 [N, H]; A_log: fp32 [H];
+    dt_bias: fp32 [H, 128]; lower_bound: finite, <= 0; state: [N, H, 128, 128]
+    bf16 or fp32 (read, then overwritten with the state after the token).
+    The same step as ``fwd`` with one token per sequence and
+    initial_state = final_state = state. Raises ValueError for invalid
+    arguments and KdaError for HIP failures.
+    """
+    import torch
+    lib = load_library()
+    bf16 = torch.bfloat16
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("out", out)):
+        if t.dtype != bf16:
+            raise ValueError("%s must be bfloat16 (got %s)" % (name, t.dtype))
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        if t.dtype != torch.float32:
+            raise ValueError("%s must be float32 (got %s)" % (name, t.dtype))
+    for t in (q, k, v, g, beta, out, A_log, dt_bias, state):
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, K]")
+    N, H, K = q.shape
+    V = v.shape[-1]
+    for name, t in (("k", k), ("g", g)):
+        if tuple(t.shape) != (N, H, K):
+            raise ValueError("%s must have the shape of q" % name)
+    if tuple(v.shape) != (N, H, V) or tuple(out.shape) != (N, H, V):
+        raise ValueError("v and out must be [N, H, V]")
+    if tuple(beta.shape) != (N, H):
+        raise ValueError("beta must be [N, H]")
+    if A_log.numel() != H or dt_bias.numel() != H * K:
+        raise ValueError("A_log must have H elements and dt_bias H*K")
+    if tuple(state.shape) != (N, H, K, V):
+        raise ValueError("state must be [N, H, K, V] = %s" % ((N, H, K, V),))
+    if state.dtype == torch.float32:
+        sd = KDA_STATE_FP32
+    elif state.dtype == bf16:
+        sd = KDA_STATE_BF16
+    else:
+        raise ValueError("state must be bfloat16 or float32")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+                        _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(state), sd, N, H, K, V,
+                        ctypes.c_void_p(stream))
     if rc == 0:
         return out
     msg = lib.kda_status_string(rc).decode()

@@ -28,6 +28,10 @@ extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, co
                                       int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
                                       const void *init_state, void *final_state, int state_fp32,
                                       hipStream_t st);
+extern "C" hipError_t kda_launch_decode(const void *q, const void *k, const void *v, const void *g,
+                                        const void *beta, const float *A_log, const float *dt_bias, float scale,
+                                        float lower_bound, void *state, int state_fp32, void *out, int64_t N,
+                                        int64_t H, hipStream_t st);
 
 namespace {
 
@@ -88,11 +92,11 @@ extern "C" const char *kda_status_string(int status)
     case KDA_ERR_STATE_DTYPE:
         return "KDA_ERR_STATE_DTYPE: state_dtype must be NONE exactly when no state is given, else BF16 or FP32";
     case KDA_ERR_ARG:
-        return "KDA_ERR_ARG: scale and lower_bound must be finite with -10 <= lower_bound <= 0";
+        return "KDA_ERR_ARG: scale and lower_bound must be finite with lower_bound <= 0 (and >= -10 for kda_fwd)";
     case KDA_ERR_WORKSPACE:
         return "KDA_ERR_WORKSPACE: workspace is NULL, not 256-byte aligned, or smaller than kda_fwd_workspace_size";
     case KDA_ERR_ALIAS:
-        return "KDA_ERR_ALIAS: out/final_state/workspace overlap an input, or the states overlap partially";
+        return "KDA_ERR_ALIAS: out/final_state/state/workspace overlap an input or each other, or the states overlap partially";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch or runtime error occurred";
     default: return "unknown kda status";
     }
@@ -205,5 +209,32 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
                             state_dtype == KDA_STATE_FP32 ? 1 : 0, st) != hipSuccess)
             return KDA_ERR_HIP;
     }
+    return KDA_OK;
+}
+
+extern "C" int kda_decode(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                          float scale, void *out, const float *A_log, const float *dt_bias, float lower_bound,
+                          void *state, int state_dtype, int64_t N, int64_t H, int64_t K, int64_t V, void *stream)
+{
+    /* ---- validation (host only, nothing enqueued yet) ---- */
+    if (K != KDA_DK || V != KDA_DV) return KDA_ERR_HEAD_DIM;
+    if (N <= 0 || H <= 0) return KDA_ERR_SHAPE;
+    if (!q || !k || !v || !g || !beta || !out || !A_log || !dt_bias || !state) return KDA_ERR_NULL;
+    if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP32) return KDA_ERR_STATE_DTYPE;
+    if (!std::isfinite(scale) || !std::isfinite(lower_bound) || lower_bound > 0.f) return KDA_ERR_ARG;
+    const size_t vec = (size_t)N * H * KDA_DK * 2;
+    const size_t sbytes = (size_t)N * H * KDA_DK * KDA_DV * (state_dtype == KDA_STATE_FP32 ? 4 : 2);
+    const Range r_out = rng(out, vec), r_state = rng(state, sbytes);
+    const Range inputs[] = {rng(q, vec), rng(k, vec), rng(v, vec), rng(g, vec), rng(beta, (size_t)N * H * 2),
+                            rng(A_log, (size_t)H * 4), rng(dt_bias, (size_t)H * KDA_DK * 4)};
+    for (const Range &in : inputs)
+        if (overlap(r_out, in) || overlap(r_state, in)) return KDA_ERR_ALIAS;
+    if (overlap(r_out, r_state)) return KDA_ERR_ALIAS;
+
+    hipStream_t st = (hipStream_t)stream;
+    ProfScope ps("kda_decode", st);
+    if (kda_launch_decode(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound, state,
+                          state_dtype == KDA_STATE_FP32 ? 1 : 0, out, N, H, st) != hipSuccess)
+        return KDA_ERR_HIP;
     return KDA_OK;
 }

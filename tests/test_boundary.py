@@ -129,3 +129,38 @@ def test_rejects_aliasing(fb):
     st = fb.addr["init"]
     assert fb.call(lib, sd=2, init=st, fin=st + 1024) == 7  # partial state overlap
     assert fb.call(lib, sd=2, init=st, fin=fb.addr["k"]) == 7
+
+
+def _decode_call(lib, over=None):
+    """kda_decode on fake, non-overlapping addresses (never dereferenced)."""
+    base, step = 1 << 40, 1 << 32
+    names = ["q", "k", "v", "g", "beta", "out", "A_log", "dt_bias", "state"]
+    a = {n: base + i * step for i, n in enumerate(names)}
+    kw = dict(scale=0.088, lb=-5.0, sd=2, N=4, H=2, K=128, V=128)
+    over = dict(over or {})
+    for n in names:
+        if "p_" + n in over:
+            a[n] = over.pop("p_" + n)
+    kw.update(over)
+    p = lambda n: None if a[n] is None else ctypes.c_void_p(a[n])
+    return lib.kda_decode(p("q"), p("k"), p("v"), p("g"), p("beta"), kw["scale"], p("out"), p("A_log"),
+                          p("dt_bias"), kw["lb"], p("state"), kw["sd"], kw["N"], kw["H"], kw["K"], kw["V"], None)
+
+
+def test_decode_rejects_bad_arguments():
+    """kda_decode validates on the host and enqueues nothing on error."""
+    lib = kda.load_library()
+    assert _decode_call(lib, {"K": 64}) == 2
+    assert _decode_call(lib, {"N": 0}) == 3
+    assert _decode_call(lib, {"H": -2}) == 3
+    for n in ["q", "k", "v", "g", "beta", "out", "A_log", "dt_bias", "state"]:
+        assert _decode_call(lib, {"p_" + n: None}) == 1, n
+    assert _decode_call(lib, {"sd": 0}) == 4                 # a state is required
+    assert _decode_call(lib, {"sd": 9}) == 4
+    assert _decode_call(lib, {"lb": 0.25}) == 5
+    assert _decode_call(lib, {"lb": float("-inf")}) == 5
+    assert _decode_call(lib, {"scale": float("nan")}) == 5
+    base, step = 1 << 40, 1 << 32
+    assert _decode_call(lib, {"p_out": base + 2 * step + 16}) == 7         # out overlaps v
+    assert _decode_call(lib, {"p_state": base + 0 * step + 256}) == 7      # state overlaps q
+    assert _decode_call(lib, {"p_out": base + 8 * step + 512}) == 7        # out inside the state
