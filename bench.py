@@ -37,7 +37,8 @@ SCAN_BYTES_PER_TH = 256
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "kimi_delta_attention_fwd_amd", "csrc")
 KERNEL_SOURCES = {"kda_prep": ("kda_prep.hip", "kda_device.h", "kda_internal.h"),
-                  "kda_scan": ("kda_scan.hip", "kda_device.h", "kda_internal.h")}
+                  "kda_scan": ("kda_scan.hip", "kda_device.h", "kda_internal.h"),
+                  "kda_decode": ("kda_decode.hip", "kda_device.h", "kda_internal.h")}
 # algorithmic MFMA flops per token-head with 16x16 blocks and 64-token chunks:
 # state-side 6*K*V + intra-chunk 2*C*(3K + 2V)
 FLOPS_PER_TH = 6 * 128 * 128 + 2 * 64 * (3 * 128 + 2 * 128)
@@ -259,6 +260,13 @@ def run_decode(args):
     kda.profile_enable(False)
     prof = kda.profile_read()
     kern_ms = prof["kda_decode"][0] / prof["kda_decode"][1]
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     units = N * H
     alg = units * (2 * 128 * 128 * 4 + 5 * 256 + 2) + H * 4 + H * 128 * 4
     achieved = alg / (kern_ms * 1e-3) / 1e9
@@ -270,7 +278,8 @@ def run_decode(args):
         "config": {"workload": "decode: N=%d sequences x H=%d heads, one token each, fp32 state" % (N, H),
                    "global_batch": N, "seq_len": 1, "heads": H, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "kda_decode",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic("kda_decode", "decode"),
+                     "kernel": "kda_decode",
                      "kernel_ms": kern_ms, "alg_bytes_per_launch": alg},
     }
     if not args.no_cpu:
