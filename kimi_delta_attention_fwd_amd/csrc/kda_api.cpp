@@ -18,7 +18,8 @@
 #include "kda.h"
 #include "kda_internal.h"
 
-extern "C" hipError_t kda_launch_chunk_map(const int32_t *cu, int64_t nseq, int32_t *chunk_off, hipStream_t st);
+extern "C" hipError_t kda_launch_chunk_map(const int32_t *cu, int64_t nseq, int64_t T, int32_t *chunk_off,
+                                           hipStream_t st);
 extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *v, const void *g,
                                       const void *beta, const float *A_log, const float *dt_bias,
                                       float scale, float lower_bound, const int32_t *cu,
@@ -107,7 +108,7 @@ extern "C" size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_
     if (B <= 0 || T <= 0 || H <= 0 || num_seqs < 0) return 0;
     if (num_seqs > 0 && B != 1) return 0;
     const int64_t nslots = kda_max_chunks(B, T, num_seqs);
-    return kda_chunk_map_bytes(num_seqs) + (size_t)nslots * (size_t)H * KDA_REC_BYTES;
+    return kda_chunk_map_bytes(num_seqs, T) + (size_t)nslots * (size_t)H * KDA_REC_BYTES;
 }
 
 extern "C" int kda_profile_enable(int on)
@@ -192,9 +193,9 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
     if (cu_seqlens) {
         chunk_off = (int32_t *)ws;
         ProfScope ps("kda_chunk_map", st);
-        if (kda_launch_chunk_map(cu_seqlens, num_seqs, chunk_off, st) != hipSuccess) return KDA_ERR_HIP;
+        if (kda_launch_chunk_map(cu_seqlens, num_seqs, T, chunk_off, st) != hipSuccess) return KDA_ERR_HIP;
     }
-    void *records = ws + kda_chunk_map_bytes(nseq_arg);
+    void *records = ws + kda_chunk_map_bytes(nseq_arg, T);
     const int64_t nslots = kda_max_chunks(B, T, nseq_arg);
     {
         ProfScope ps("kda_prep", st);

@@ -48,13 +48,21 @@
 /* fragment index of P(mt, jb); only jb <= mt / 2 exists */
 #define KDA_PIDX(mt, jb) ((mt) < 2 ? (mt) : 2 + 2 * ((mt) - 2) + (jb))
 
-/* workspace = [chunk_off int32[N + 1], padded to 256 B][records]
+/* In a packed (varlen) batch with many chains, sequences of more than
+ * KDA_MANY_MAX_CHUNKS chunks are scanned by the three-wave kernel and the rest
+ * by the eight-wave kernel. At most kda_max_long_seqs(T) of T packed tokens. */
+#define KDA_MANY_MAX_CHUNKS 128
+static inline int64_t kda_max_long_seqs(int64_t T) { return T / (KDA_MANY_MAX_CHUNKS * KDA_CHUNK + 1); }
+
+/* workspace = [chunk table, padded to 256 B][records]
+ * The chunk table (varlen only) is int32: chunk_off[N + 1], then the number of
+ * long sequences and their indices in ascending order (kda_max_long_seqs slots).
  * Records are head-major, record(slot, h) at (h * nslots + slot) * KDA_REC_BYTES
  * with nslots = kda_max_chunks(...), so the chunks of one (sequence, head) that
  * the scan walks in order are adjacent in memory. */
-static inline size_t kda_chunk_map_bytes(int64_t num_seqs)
+static inline size_t kda_chunk_map_bytes(int64_t num_seqs, int64_t T)
 {
-    return num_seqs > 0 ? (size_t)(((num_seqs + 1) * 4 + 255) / 256 * 256) : 0;
+    return num_seqs > 0 ? (size_t)(((num_seqs + 2 + kda_max_long_seqs(T)) * 4 + 255) / 256 * 256) : 0;
 }
 
 /* upper bound on the number of chunks: exact without cu_seqlens */

@@ -14,36 +14,45 @@
 #include "kda_device.h"
 
 /* ------------------------------------------------------------------------- */
-/* varlen chunk table: chunk_off[n] = sum_{m < n} ceil(len_m / 64)            */
+/* varlen chunk table: chunk_off[n] = sum_{m < n} ceil(len_m / 64), then the  */
+/* count and the ascending indices of sequences of more than                  */
+/* KDA_MANY_MAX_CHUNKS chunks (long_list[0] = count, long_list[1 + i]); the   */
+/* list holds max_long entries, which valid cu_seqlens never exceed            */
 /* ------------------------------------------------------------------------- */
 extern "C" __global__ void __launch_bounds__(1024)
-kda_chunk_map_kernel(const int32_t *__restrict__ cu, int64_t nseq, int32_t *__restrict__ chunk_off)
+kda_chunk_map_kernel(const int32_t *__restrict__ cu, int64_t nseq, int32_t *__restrict__ chunk_off,
+                     int64_t max_long)
 {
-    __shared__ int32_t s_wave[16];
-    __shared__ int32_t s_carry;
+    __shared__ int32_t s_wave[16], s_wave_l[16];
+    __shared__ int32_t s_carry, s_carry_l;
+    int32_t *long_list = chunk_off + nseq + 1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (tid == 0) { s_carry = 0; chunk_off[0] = 0; }
+    if (tid == 0) { s_carry = 0; s_carry_l = 0; chunk_off[0] = 0; }
     __syncthreads();
     for (int64_t base = 0; base < nseq; base += 1024) {
         const int64_t n = base + tid;
-        int32_t x = 0;
+        int32_t x = 0, f = 0;
         if (n < nseq) {
             const int32_t len = cu[n + 1] - cu[n];
             x = (len + KDA_CHUNK - 1) / KDA_CHUNK;
+            f = x > KDA_MANY_MAX_CHUNKS;
         }
+        const int32_t f0 = f;
         for (int d = 1; d < 64; d <<= 1) {
-            const int32_t y = __shfl_up(x, d);
-            if (lane >= d) x += y;
+            const int32_t y = __shfl_up(x, d), yf = __shfl_up(f, d);
+            if (lane >= d) { x += y; f += yf; }
         }
-        if (lane == 63) s_wave[wave] = x;
+        if (lane == 63) { s_wave[wave] = x; s_wave_l[wave] = f; }
         __syncthreads();
-        int32_t add = s_carry;
-        for (int w = 0; w < wave; w++) add += s_wave[w];
+        int32_t add = s_carry, add_l = s_carry_l;
+        for (int w = 0; w < wave; w++) { add += s_wave[w]; add_l += s_wave_l[w]; }
         if (n < nseq) chunk_off[n + 1] = add + x;
+        if (f0 && add_l + f - 1 < max_long) long_list[1 + add_l + f - 1] = (int32_t)n;
         __syncthreads();
-        if (tid == 1023) s_carry = add + x;
+        if (tid == 1023) { s_carry = add + x; s_carry_l = add_l + f; }
         __syncthreads();
     }
+    if (tid == 0) long_list[0] = (int32_t)(s_carry_l < max_long ? s_carry_l : max_long);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -484,9 +493,10 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
 /* ------------------------------------------------------------------------- */
 /* launchers (called by kda_api.cpp after validation)                          */
 /* ------------------------------------------------------------------------- */
-extern "C" hipError_t kda_launch_chunk_map(const int32_t *cu, int64_t nseq, int32_t *chunk_off, hipStream_t st)
+extern "C" hipError_t kda_launch_chunk_map(const int32_t *cu, int64_t nseq, int64_t T, int32_t *chunk_off,
+                                           hipStream_t st)
 {
-    hipLaunchKernelGGL(kda_chunk_map_kernel, dim3(1), dim3(1024), 0, st, cu, nseq, chunk_off);
+    hipLaunchKernelGGL(kda_chunk_map_kernel, dim3(1), dim3(1024), 0, st, cu, nseq, chunk_off, kda_max_long_seqs(T));
     return hipGetLastError();
 }
 

@@ -163,7 +163,7 @@ extern "C" __global__ void __launch_bounds__(192)
 kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
                 const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
                 uint16_t *__restrict__ out, const void *__restrict__ init_state,
-                void *__restrict__ final_state, int state_fp32)
+                void *__restrict__ final_state, int state_fp32, const int32_t *__restrict__ long_list)
 {
     __shared__ bf16x8 ring[2][4 * 64];                          /* 8 KiB: S(c) in bf16 */
     __shared__ __attribute__((aligned(16))) unsigned char warm_sink[1024];
@@ -173,11 +173,22 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
     const int64_t b = blockIdx.x;
     const int64_t xcd = b & 7, qd = b >> 3;
     const int nt = (int)(qd & 7);
-    const int64_t chain = (qd >> 3) * 8 + xcd;
-    const int64_t nchain = nseq * H;
-    if (chain >= nchain) return;
-    const int64_t seq = chain / H;
-    const int h = (int)(chain - seq * H);
+    const int64_t ci = (qd >> 3) * 8 + xcd;
+    /* ci is the chain (sequence * H + head), or with a long-sequence list
+       (long_list[0] entries, then sequence indices) the list slot * H + head */
+    int64_t seq;
+    int h;
+    if (long_list == nullptr) {
+        if (ci >= nseq * H) return;
+        seq = ci / H;
+        h = (int)(ci - seq * H);
+    } else {
+        const int64_t slot = ci / H;
+        if (slot >= long_list[0]) return;
+        seq = long_list[1 + slot];
+        h = (int)(ci - slot * H);
+    }
+    const int64_t chain = seq * H + h;
     const int vcol = 16 * nt + n16;
 
     int64_t bos, eos, slot0;
@@ -265,6 +276,13 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
         /* ---------------- L2-warming wave ---------------- */
         const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)warm_sink;
         for (int64_t c = 0; c < nchunk; c++) {
+            /* Code placement: the chunk time of the whole workgroup was measured
+               to depend on where this loop sits relative to 32-byte instruction
+               fetch blocks (1.035 to 1.112 ms per long-prefill launch over the
+               eight offsets; the other two loops showed no such effect). The
+               loop is pinned to a 32-byte boundary plus two s_nop, the fastest
+               offset; an edit of this loop needs the offset measured again. */
+            asm volatile(".p2align 5\n\ts_nop 0\n\ts_nop 0");
             const int64_t cw = c + KDA_WARM_AHEAD;
             if (cw < nchunk) {
                 const unsigned char *r = rec0 + (size_t)cw * KDA_REC_BYTES;
@@ -281,17 +299,246 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
 }
 
 /* ------------------------------------------------------------------------- */
+/* many-chain scan: one workgroup of 8 waves per (sequence, head)              */
+/* ------------------------------------------------------------------------- */
+/*
+ * The three-wave kernel above holds a whole CU (its waves need ~450 registers
+ * each) to hide the latency of one long chain, and its eight value tiles each
+ * read the whole record. When there are many chains (packed batches of short
+ * sequences, per-sequence states in and out) the latency is hidden by running
+ * many chains side by side instead, and the record is read once per chain:
+ * the workgroup copies the shared part of each chunk's record (W, Q', K~, P,
+ * e^{G_L}: the first KDA_REC_U bytes, in record layout) into LDS, and wave w
+ * runs value tile w (state update and output) from there, with its own slice
+ * of U read from memory. Waves are limited to 128 registers and the workgroup
+ * to 55.8 KB of LDS, so two workgroups share a CU. The arithmetic, its order
+ * and the operand layouts are those of the three-wave kernel, so both produce
+ * the same bits.
+ * The state slice is read and written through buffer descriptors whose range is
+ * empty when the state pointer is null (loads return 0, stores are dropped).
+ */
+__device__ __forceinline__ void state_io_rsrc(const void *state, int state_fp32, int64_t chain, const void *dummy,
+                                              __amdgpu_buffer_rsrc_t &r)
+{
+    const uint32_t bytes = (uint32_t)(KDA_DK * KDA_DV * (state_fp32 ? 4 : 2));
+    r = state ? buf_rsrc((const unsigned char *)state + (size_t)chain * bytes, bytes) : buf_rsrc(dummy, 0);
+}
+
+#define KDA_SHARED_PIECES (KDA_REC_U / 16) /* 16-byte pieces of the shared operands */
+#define KDA_FILL_ITERS ((KDA_SHARED_PIECES + 511) / 512)
+
+__device__ __forceinline__ bf16x8 ldsld(const unsigned char *base, int off)
+{
+    return *(const bf16x8 *)(base + off);
+}
+
+extern "C" __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ cu,
+                     const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
+                     uint16_t *out, const void *init_state, void *final_state, int state_fp32, int64_t max_chunks)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char opnd[KDA_REC_U];
+    const int tid = threadIdx.x;
+    const int l = tid & 63, g = l >> 4, n16 = l & 15;
+    const int nt = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t chain = blockIdx.x;
+    const int64_t seq = chain / H;
+    const int h = (int)(chain - seq * H);
+
+    int64_t bos, eos, slot0;
+    if (cu == nullptr) {
+        bos = seq * T;
+        eos = bos + T;
+        slot0 = seq * ((T + KDA_CHUNK - 1) / KDA_CHUNK);
+    } else {
+        bos = cu[seq];
+        eos = cu[seq + 1];
+        slot0 = chunk_off[seq];
+    }
+    const int64_t nchunk = (eos - bos + KDA_CHUNK - 1) / KDA_CHUNK;
+    if (nchunk > max_chunks) return; /* left to the three-wave kernel (uniform over the workgroup) */
+    const unsigned char *rec0 = rec_base + ((size_t)h * nslots + slot0) * KDA_REC_BYTES;
+    const int ubase = KDA_REC_U + nt * 2048;
+    const int row_bytes = H * KDA_DV * 2;
+
+    /* element (16 mt + 4 g + e, 16 nt + n16) of the state */
+    const int esz = state_fp32 ? 4 : 2;
+    const int soff = ((4 * g) * KDA_DV + 16 * nt + n16) * esz;
+    __amdgpu_buffer_rsrc_t ri, rf;
+    state_io_rsrc(init_state, state_fp32, chain, rec_base, ri);
+    state_io_rsrc(final_state, state_fp32, chain, rec_base, rf);
+    f32x4 S[8];
+    if (state_fp32) {
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                S[mt][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ri, soff, (16 * mt + e) * KDA_DV * 4, 0));
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                S[mt][e] = bf2f(__builtin_amdgcn_raw_buffer_load_b16(ri, soff, (16 * mt + e) * KDA_DV * 2, 0));
+    }
+
+    for (int64_t c = 0; c < nchunk; c++) {
+        const __amdgpu_buffer_rsrc_t r = rec_rsrc(rec0 + (size_t)c * KDA_REC_BYTES);
+        const int64_t t0 = bos + c * KDA_CHUNK;
+        const int64_t rem = eos - t0;
+        const int L = (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
+        /* this chunk's shared operands: loads issued before the barrier that
+           frees the LDS copy of the previous chunk, stores after it */
+        u32x4 stage[KDA_FILL_ITERS];
+#pragma unroll
+        for (int i = 0; i < KDA_FILL_ITERS; i++) {
+            const int p = i * 512 + tid;
+            stage[i] = p < KDA_SHARED_PIECES ? __builtin_amdgcn_raw_buffer_load_b128(r, p * 16, 0, 0) : u32x4{0, 0, 0, 0};
+        }
+        bf16x8 U[2];
+        U[0] = bufld(r, l * 32, ubase);
+        U[1] = bufld(r, l * 32, ubase + 16);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KDA_FILL_ITERS; i++) {
+            const int p = i * 512 + tid;
+            if (p < KDA_SHARED_PIECES) *(u32x4 *)(opnd + p * 16) = stage[i];
+        }
+        __syncthreads();
+
+        bf16x8 sb[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+        /* D = U - W S; LDS operands are read in groups of eight fragments */
+        f32x4 D[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+            const int o = (mt & 1) * 4;
+            const bf16x8 &u = U[mt >> 1];
+            D[mt] = f32x4{(float)u[o], (float)u[o + 1], (float)u[o + 2], (float)u[o + 3]};
+        }
+        bf16x8 fr[8];
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int kb = 2 * half + (i >> 2), mt = i & 3;
+                fr[i] = ldsld(opnd, KDA_REC_W + (mt * 4 + kb) * 1024 + l * 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int kb = 2 * half + (i >> 2), mt = i & 3;
+                D[mt] = mfma(fr[i], sb[kb], D[mt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        /* out^T = S^T Q'^T + U^T P^T */
+        f32x4 O[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) O[mt] = zero4();
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int kb = 2 * half + (i >> 2), mt = i & 3;
+                fr[i] = ldsld(opnd, KDA_REC_Q + (mt * 4 + kb) * 1024 + l * 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int kb = 2 * half + (i >> 2), mt = i & 3;
+                O[mt] = mfma(sb[kb], fr[i], O[mt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int f = 0; f < 6; f++) fr[f] = ldsld(opnd, KDA_REC_P + f * 1024 + l * 16);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+            for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(U[jb], fr[KDA_PIDX(mt, jb)], O[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+        const __amdgpu_buffer_rsrc_t ro =
+            buf_rsrc(out + ((size_t)t0 * H + h) * KDA_DV, (uint32_t)((L - 1) * row_bytes + KDA_DV * 2));
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) {
+            u32x2 u;
+            u[0] = f2bf_bits(O[mt][0]) | ((uint32_t)f2bf_bits(O[mt][1]) << 16);
+            u[1] = f2bf_bits(O[mt][2]) | ((uint32_t)f2bf_bits(O[mt][3]) << 16);
+            __builtin_amdgcn_raw_buffer_store_b64(u, ro, (16 * mt + n16) * row_bytes + (16 * nt + 4 * g) * 2, 0, 0);
+        }
+
+        /* S <- diag(e^{G_L}) S + K~^T D */
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++) S[mt] *= *(const f32x4 *)(opnd + KDA_REC_GL + mt * 64 + g * 16);
+        bf16x8 db[2];
+        db[0] = pack8(D[0], D[1]);
+        db[1] = pack8(D[2], D[3]);
+#pragma unroll
+        for (int jb = 0; jb < 2; jb++) {
+#pragma unroll
+            for (int mt = 0; mt < 8; mt++) fr[mt] = ldsld(opnd, KDA_REC_KT + (mt * 2 + jb) * 1024 + l * 16);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int mt = 0; mt < 8; mt++) S[mt] = mfma(fr[mt], db[jb], S[mt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    if (state_fp32) {
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[mt][e]), rf, soff, (16 * mt + e) * KDA_DV * 4, 0);
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                __builtin_amdgcn_raw_buffer_store_b16(f2bf_bits(S[mt][e]), rf, soff, (16 * mt + e) * KDA_DV * 2, 0);
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* launcher (called by kda_api.cpp after validation)                           */
 /* ------------------------------------------------------------------------- */
+/*
+ * With fewer than KDA_MANY_CHAINS (sequence, head) chains the three-wave kernel
+ * runs them all (a CU per value tile hides the latency of a long chain, about
+ * 1 us per chunk, for 32 chains at a time). With more, the eight-wave kernel
+ * runs up to 512 chains at once (about 3-6 us per chunk, bound by memory
+ * traffic): in a fixed-length batch all of them; in a packed batch every chain
+ * of at most KDA_MANY_MAX_CHUNKS chunks, and the three-wave kernel then runs the
+ * longer ones (a few long prompts among many short ones) from the list of long
+ * sequences the chunk-table kernel leaves after chunk_off.
+ */
+#define KDA_MANY_CHAINS 128
+
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
                                       int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
                                       const void *init_state, void *final_state, int state_fp32,
                                       hipStream_t st)
 {
     const int64_t nchain = nseq * H;
-    const int64_t blocks = (nchain + 7) / 8 * 64;
-    hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)blocks), dim3(192), 0, st,
+    if (nchain < KDA_MANY_CHAINS) {
+        hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)((nchain + 7) / 8 * 64)), dim3(192), 0, st,
+                           (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H, nslots,
+                           (uint16_t *)out, init_state, final_state, state_fp32, (const int32_t *)nullptr);
+        return hipGetLastError();
+    }
+    const int64_t max_chunks = cu == nullptr ? INT64_MAX : (int64_t)KDA_MANY_MAX_CHUNKS;
+    hipLaunchKernelGGL(kda_scan_many_kernel, dim3((unsigned)nchain), dim3(512), 0, st,
+                       (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H, nslots, (uint16_t *)out,
+                       init_state, final_state, state_fp32, max_chunks);
+    const hipError_t e = hipGetLastError();
+    const int64_t max_long = kda_max_long_seqs(T);
+    if (e != hipSuccess || cu == nullptr || max_long == 0) return e;
+    hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)((max_long * H + 7) / 8 * 64)), dim3(192), 0, st,
                        (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H, nslots,
-                       (uint16_t *)out, init_state, final_state, state_fp32);
+                       (uint16_t *)out, init_state, final_state, state_fp32, chunk_off + nseq + 1);
     return hipGetLastError();
 }

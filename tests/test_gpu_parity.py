@@ -138,6 +138,53 @@ def test_varlen_equals_separate_bitwise():
         assert np.array_equal(on, o[:, a:b]) and np.array_equal(fn[0], f[n]), n
 
 
+# With 128 or more (sequence, head) chains the scan runs on its eight-wave
+# kernel; in a packed batch, sequences of more than 128 chunks go to its
+# three-wave kernel instead (listed by the chunk-table kernel). With fewer chains
+# the three-wave kernel runs them all. The two use the same arithmetic in the
+# same order, so a sequence gives the same bits either way.
+@pytest.mark.parametrize("state", ["fp32", "bf16"])
+def test_many_chain_scan(state):
+    gu = _gpu()
+    rng = np.random.default_rng(21)
+    lens = [8300, 0, 1, 64, 65, 129, 8200] + [int(x) for x in rng.integers(1, 300, 57)]
+    d = ki.make_inputs(1, sum(lens), 2, seed=21, lengths=lens, state=state, initial=True, sigma=0.05)
+    assert len(lens) * 2 >= 128 and lens[0] > 128 * 64 and lens[6] > 128 * 64
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("many-chain %s out" % state, o, ro)
+    check("many-chain %s final" % state, f, rf)
+    cu = d["cu_seqlens"]
+    for n in range(len(lens)):
+        a, b = int(cu[n]), int(cu[n + 1])
+        e = dict(d)
+        for key in ("q", "k", "v", "g", "beta"):
+            e[key] = np.ascontiguousarray(d[key][:, a:b])
+        e.update(T=b - a, N=1, cu_seqlens=None, initial_state=np.ascontiguousarray(d["initial_state"][n:n + 1]))
+        if b == a:
+            continue
+        on, fn = gu.run_gpu(e)
+        assert np.array_equal(on, o[:, a:b]) and np.array_equal(fn[0], f[n]), n
+
+
+def test_many_chain_fixed_batch():
+    """A fixed-length batch of 128 chains (eight-wave kernel) against the oracle
+    and, bit for bit, against single-sequence calls (three-wave kernel)."""
+    gu = _gpu()
+    d = ki.make_inputs(64, 200, 2, seed=22, state="fp32", initial=True, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("fixed-batch out", o, ro)
+    check("fixed-batch final", f, rf)
+    for b in (0, 17, 63):
+        e = dict(d)
+        for key in ("q", "k", "v", "g", "beta"):
+            e[key] = np.ascontiguousarray(d[key][b:b + 1])
+        e.update(B=1, N=1, initial_state=np.ascontiguousarray(d["initial_state"][b:b + 1]))
+        ob, fb = gu.run_gpu(e)
+        assert np.array_equal(ob, o[b:b + 1]) and np.array_equal(fb, f[b:b + 1]), b
+
+
 def test_batch_equals_separate_bitwise():
     gu = _gpu()
     d = ki.make_inputs(3, 150, 2, seed=10, state="bf16", initial=True)
