@@ -85,6 +85,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
     ap.add_argument("--decode", action="store_true",
                     help="time the single-token decode step instead (512 sequences x 64 heads, fp32 state)")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="keep only the first N heads of the workload (one GPU's share when heads are sharded)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run 3 device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -106,6 +108,16 @@ def main():
     dev = "cuda:0"
     t_gen = time.time()
     d = ki.config_inputs(args.config)
+    if 0 < args.heads < d["H"]:
+        nh = args.heads
+        for key in ("q", "k", "v", "g", "beta"):
+            d[key] = np.ascontiguousarray(d[key][:, :, :nh])
+        for key in ("A_log", "dt_bias"):
+            d[key] = np.ascontiguousarray(d[key][:nh])
+        if d["initial_state"] is not None:
+            d["initial_state"] = np.ascontiguousarray(d["initial_state"][:, :nh])
+        d["H"] = nh
+        d["name"] = "%s_h%d" % (d["name"], nh)
     print("[bench] inputs for workload %d (%s) drawn in %.1f s" % (args.config, d["name"], time.time() - t_gen),
           file=sys.stderr, flush=True)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)

@@ -27,8 +27,8 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
                                       int64_t nslots, void *records, hipStream_t st);
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
                                       int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
-                                      const void *init_state, void *final_state, int state_fp32,
-                                      hipStream_t st);
+                                      const void *init_state, void *final_state, int state_fp32, int64_t nseg,
+                                      void *seg_area, hipStream_t st);
 extern "C" hipError_t kda_launch_decode(const void *q, const void *k, const void *v, const void *g,
                                         const void *beta, const float *A_log, const float *dt_bias, float scale,
                                         float lower_bound, void *state, int state_fp32, void *out, int64_t N,
@@ -108,7 +108,8 @@ extern "C" size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_
     if (B <= 0 || T <= 0 || H <= 0 || num_seqs < 0) return 0;
     if (num_seqs > 0 && B != 1) return 0;
     const int64_t nslots = kda_max_chunks(B, T, num_seqs);
-    return kda_chunk_map_bytes(num_seqs, T) + (size_t)nslots * (size_t)H * KDA_REC_BYTES;
+    return kda_chunk_map_bytes(num_seqs, T) + (size_t)nslots * (size_t)H * KDA_REC_BYTES +
+           kda_seg_bytes(B, T, H, num_seqs);
 }
 
 extern "C" int kda_profile_enable(int on)
@@ -207,7 +208,8 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
         ProfScope ps("kda_scan", st);
         if (kda_launch_scan(records, cu_seqlens, chunk_off, N, T, H, nslots, out,
                             state_dtype == KDA_STATE_NONE ? nullptr : initial_state, final_state,
-                            state_dtype == KDA_STATE_FP32 ? 1 : 0, st) != hipSuccess)
+                            state_dtype == KDA_STATE_FP32 ? 1 : 0, kda_scan_segments(B, T, H, nseq_arg),
+                            (unsigned char *)records + (size_t)nslots * (size_t)H * KDA_REC_BYTES, st) != hipSuccess)
             return KDA_ERR_HIP;
     }
     return KDA_OK;

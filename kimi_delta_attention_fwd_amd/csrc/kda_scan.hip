@@ -159,11 +159,15 @@ __device__ __forceinline__ void warm_l2(const unsigned char *p, uint32_t lds_add
 
 #define KDA_WARM_AHEAD 4
 
-extern "C" __global__ void __launch_bounds__(192)
-kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
-                const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
-                uint16_t *__restrict__ out, const void *__restrict__ init_state,
-                void *__restrict__ final_state, int state_fp32, const int32_t *__restrict__ long_list)
+/* the scan body; SEG instantiates the segment-parallel rescan (one workgroup per
+   (chain, segment, tile)), which the plain kernel compiles without */
+template <bool SEG>
+__device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
+                                          const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H,
+                                          int64_t nslots, uint16_t *__restrict__ out,
+                                          const void *__restrict__ init_state, void *__restrict__ final_state,
+                                          int state_fp32, const int32_t *__restrict__ long_list, int64_t nseg,
+                                          int64_t segc, const float *__restrict__ seg_init)
 {
     __shared__ bf16x8 ring[2][4 * 64];                          /* 8 KiB: S(c) in bf16 */
     __shared__ __attribute__((aligned(16))) unsigned char warm_sink[1024];
@@ -173,9 +177,12 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
     const int64_t b = blockIdx.x;
     const int64_t xcd = b & 7, qd = b >> 3;
     const int nt = (int)(qd & 7);
-    const int64_t ci = (qd >> 3) * 8 + xcd;
-    /* ci is the chain (sequence * H + head), or with a long-sequence list
-       (long_list[0] entries, then sequence indices) the list slot * H + head */
+    const int64_t cs = (qd >> 3) * 8 + xcd;
+    /* cs = ci * nseg + segment; ci is the chain (sequence * H + head), or with a
+       long-sequence list (long_list[0] entries, then sequence indices) the list
+       slot * H + head */
+    const int64_t seg = SEG ? cs % nseg : 0;
+    const int64_t ci = SEG ? cs / nseg : cs;
     int64_t seq;
     int h;
     if (long_list == nullptr) {
@@ -201,7 +208,25 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
         eos = cu[seq + 1];
         slot0 = chunk_off[seq];
     }
-    const int64_t nchunk = (eos - bos + KDA_CHUNK - 1) / KDA_CHUNK;
+    int64_t nchunk = (eos - bos + KDA_CHUNK - 1) / KDA_CHUNK;
+    /* a segment of the segment-parallel scan: chunks seg * segc .. from the
+       entering state the combine pass left in seg_init (fp32; segment 0's is a
+       copy of the initial state, so an in-place final state cannot race with
+       it); only the last segment writes the final state */
+    const void *ist = init_state;
+    int ist_fp32 = state_fp32;
+    size_t ibase = (size_t)chain * KDA_DK * KDA_DV;
+    void *fst = final_state;
+    if (SEG) {
+        const int64_t c_first = seg * segc;
+        nchunk = nchunk - c_first < segc ? nchunk - c_first : segc;
+        bos += c_first * KDA_CHUNK;
+        slot0 += c_first;
+        ist = seg_init;
+        ist_fp32 = 1;
+        ibase = ((size_t)chain * nseg + seg) * KDA_DK * KDA_DV;
+        if (seg < nseg - 1) fst = nullptr;
+    }
     const unsigned char *rec0 = rec_base + ((size_t)h * nslots + slot0) * KDA_REC_BYTES;
     /* record of chunk c, clamped to the last one (its reload is harmless) */
     auto rec_of = [&](int64_t c) { return rec0 + (size_t)(c < nchunk ? c : nchunk - 1) * KDA_REC_BYTES; };
@@ -210,15 +235,14 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
     if (wave == 0) {
         /* ---------------- state wave ---------------- */
         f32x4 S[8];
-        const size_t sbase = (size_t)chain * KDA_DK * KDA_DV;
 #pragma unroll
         for (int mt = 0; mt < 8; mt++) {
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const size_t idx = sbase + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
+                const size_t idx = ibase + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
                 float sv = 0.f;
-                if (init_state)
-                    sv = state_fp32 ? ((const float *)init_state)[idx] : bf2f(((const uint16_t *)init_state)[idx]);
+                if (ist)
+                    sv = ist_fp32 ? ((const float *)ist)[idx] : bf2f(((const uint16_t *)ist)[idx]);
                 S[mt][e] = sv;
             }
         }
@@ -237,15 +261,15 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
                 state_step(X, Y, S, rec_of(c + 2), ubase, ring[(c + 1) & 1], l, g);
             }
         }
-        if (final_state) {
+        if (fst) {
             const size_t sbase2 = (size_t)chain * KDA_DK * KDA_DV;
 #pragma unroll
             for (int mt = 0; mt < 8; mt++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const size_t idx = sbase2 + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
-                    if (state_fp32) ((float *)final_state)[idx] = S[mt][e];
-                    else ((uint16_t *)final_state)[idx] = f2bf_bits(S[mt][e]);
+                    if (state_fp32) ((float *)fst)[idx] = S[mt][e];
+                    else ((uint16_t *)fst)[idx] = f2bf_bits(S[mt][e]);
                 }
         }
     } else if (wave == 1) {
@@ -295,6 +319,191 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
             chunk_barrier();
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+}
+
+extern "C" __global__ void __launch_bounds__(192)
+kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
+                const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
+                uint16_t *__restrict__ out, const void *__restrict__ init_state,
+                void *__restrict__ final_state, int state_fp32, const int32_t *__restrict__ long_list)
+{
+    scan_body<false>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state, state_fp32, long_list,
+                     1, 0, nullptr);
+}
+
+/* the rescan of the segment-parallel scan: workgroup (chain, segment, tile) */
+extern "C" __global__ void __launch_bounds__(192)
+kda_scan_seg_kernel(const unsigned char *__restrict__ rec_base, int64_t nseq, int64_t T, int H, int64_t nslots,
+                    uint16_t *__restrict__ out, void *__restrict__ final_state, int state_fp32, int64_t nseg,
+                    int64_t segc, const float *__restrict__ seg_init)
+{
+    scan_body<true>(rec_base, nullptr, nullptr, nseq, T, H, nslots, out, nullptr, final_state, state_fp32, nullptr,
+                    nseg, segc, seg_init);
+}
+
+/* ------------------------------------------------------------------------- */
+/* segment-parallel scan: segment maps and their chaining                      */
+/* ------------------------------------------------------------------------- */
+/*
+ * With few chains (fixed-length batches of B * H <= 10 long sequences, e.g. one
+ * GPU's share of heads) the three-wave kernel leaves most CUs idle: each chain
+ * is one dependent walk over all its chunks. The chunk update is affine in the
+ * state, S -> (diag(e^{G_L}) - K~^T W) S + K~^T U, so a segment of chunks maps
+ * its entering state S to M S + B. kda_seg_map_kernel runs every segment but
+ * the last from the states [0 | I] (B: 8 value tiles with U; M: 8 identity
+ * tiles with U taken as 0), all segments at once; kda_seg_chain_kernel walks the
+ * G - 1 maps of a chain in fp32 to get every segment's entering state; the
+ * three-wave kernel then rescans each segment from its entering state, writing
+ * out (and, for the last segment, the final state). The maps use the same
+ * chunk arithmetic as the scan (bf16 operands, fp32 accumulation), so the
+ * result differs from the plain scan only by rounding.
+ */
+
+/* state-only chunk step: X holds chunk c, loads chunk c + 1 (at nrec) into Y */
+__device__ __forceinline__ void map_step(ScanSetS &X, ScanSetS &Y, f32x4 (&S)[8], const unsigned char *nrec,
+                                         int ubase, int l, int g, bool homog)
+{
+    load_set(Y, nrec, ubase, l, g);
+    bf16x8 sb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+    f32x4 D[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; mt++) {
+        const int o = (mt & 1) * 4;
+        const bf16x8 &u = X.U[mt >> 1];
+        D[mt] = homog ? zero4() : f32x4{(float)u[o], (float)u[o + 1], (float)u[o + 2], (float)u[o + 3]};
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++) D[mt] = mfma(X.W[mt * 4 + kb], sb[kb], D[mt]);
+#pragma unroll
+    for (int mt = 0; mt < 8; mt++) S[mt] *= X.gl[mt];
+    bf16x8 db[2];
+    db[0] = pack8(D[0], D[1]);
+    db[1] = pack8(D[2], D[3]);
+#pragma unroll
+    for (int jb = 0; jb < 2; jb++)
+#pragma unroll
+        for (int mt = 0; mt < 8; mt++) S[mt] = mfma(X.K[mt * 2 + jb], db[jb], S[mt]);
+}
+
+/* one wave per (chain, segment < G - 1, 16-column tile of [B | M]); the 16
+   tiles of a segment run on one XCD and share its L2 */
+extern "C" __global__ void __launch_bounds__(64)
+kda_seg_map_kernel(const unsigned char *rec_base, int64_t nchain, int H, int64_t nslots, int64_t cps,
+                   int64_t nseg, int64_t segc, float *seg_area)
+{
+    const int l = threadIdx.x, g = l >> 4, n16 = l & 15;
+    const int64_t b = blockIdx.x;
+    const int64_t xcd = b & 7, qd = b >> 3;
+    const int t16 = (int)(qd & 15);
+    const int64_t grp = (qd >> 4) * 8 + xcd; /* chain * (nseg - 1) + segment */
+    if (grp >= nchain * (nseg - 1)) return;
+    const int64_t chain = grp / (nseg - 1), seg = grp - chain * (nseg - 1);
+    const int64_t seq = chain / H;
+    const int h = (int)(chain - seq * H);
+    const bool homog = t16 >= 8;
+    const int nt = t16 & 7;
+    const unsigned char *rec0 = rec_base + ((size_t)h * nslots + seq * cps + seg * segc) * KDA_REC_BYTES;
+    auto rec_of = [&](int64_t c) { return rec0 + (size_t)(c < segc ? c : segc - 1) * KDA_REC_BYTES; };
+    const int ubase = KDA_REC_U + nt * 2048;
+
+    /* [B | M] starts at [0 | I]: tile nt of M holds the identity's columns 16 nt .. 16 nt + 15 */
+    f32x4 S[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) S[mt][e] = (homog && 16 * mt + 4 * g + e == 16 * nt + n16) ? 1.f : 0.f;
+    ScanSetS X, Y;
+    int64_t c = 0;
+    if (segc & 1) {
+        load_set(X, rec_of(0), ubase, l, g);
+        map_step(X, Y, S, rec_of(1), ubase, l, g, homog);
+        c = 1;
+    } else {
+        load_set(Y, rec_of(0), ubase, l, g);
+    }
+    for (; c < segc; c += 2) {
+        map_step(Y, X, S, rec_of(c + 1), ubase, l, g, homog);
+        map_step(X, Y, S, rec_of(c + 2), ubase, l, g, homog);
+    }
+    float *dst = seg_area + ((size_t)(homog ? nchain * (nseg - 1) : 0) + grp) * KDA_DK * KDA_DV;
+#pragma unroll
+    for (int mt = 0; mt < 8; mt++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) dst[(16 * mt + 4 * g + e) * KDA_DV + 16 * nt + n16] = S[mt][e];
+}
+
+__device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+/* LDS slot of row R, column j of a 128 x 16 fp32 state tile (rows 32 apart are
+   spread over the banks) */
+__host__ __device__ constexpr int chain_lds(int R, int j) { return R * 16 + (R >> 5) * 8 + j; }
+
+/* one workgroup of 4 waves per (chain, 16-column tile): S_0 = initial state,
+   S_{s+1} = M_s S_s + B_s for s < G - 1, in fp32 (v_mfma_f32_16x16x4f32); wave w
+   computes row tiles 2 w, 2 w + 1 of each product. Writes S_0 .. S_{G-1}. */
+extern "C" __global__ void __launch_bounds__(256)
+kda_seg_chain_kernel(float *seg_area, const void *init_state, int state_fp32, int64_t nchain, int64_t nseg)
+{
+    __shared__ float sS[chain_lds(127, 15) + 1];
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gq = l >> 4, r16 = l & 15;
+    const int64_t b = blockIdx.x;
+    const int64_t xcd = b & 7, qd = b >> 3;
+    const int nt = (int)(qd & 7);
+    const int64_t chain = (qd >> 3) * 8 + xcd;
+    if (chain >= nchain) return;
+    const float *segM = seg_area + (size_t)nchain * (nseg - 1) * KDA_DK * KDA_DV;
+    const float *segB = seg_area;
+    float *segS = seg_area + (size_t)2 * nchain * (nseg - 1) * KDA_DK * KDA_DV + (size_t)chain * nseg * KDA_DK * KDA_DV;
+
+    for (int i = tid; i < KDA_DK * 16; i += 256) {
+        const int R = i >> 4, j = i & 15;
+        const size_t idx = ((size_t)chain * KDA_DK + R) * KDA_DV + 16 * nt + j;
+        float v = 0.f;
+        if (init_state) v = state_fp32 ? ((const float *)init_state)[idx] : bf2f(((const uint16_t *)init_state)[idx]);
+        sS[chain_lds(R, j)] = v;
+        segS[R * KDA_DV + 16 * nt + j] = v;
+    }
+    __syncthreads();
+    for (int64_t s = 0; s < nseg - 1; s++) {
+        const size_t mo = ((size_t)chain * (nseg - 1) + s) * KDA_DK * KDA_DV;
+        f32x4 acc[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; rr++) {
+            const int rt = 2 * w + rr;
+            /* accumulator starts at B_s (rows 16 rt + 4 gq + e, column n16) */
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[rr][e] = segB[mo + (size_t)(16 * rt + 4 * gq + e) * KDA_DV + 16 * nt + r16];
+            /* A = rows 16 rt + r16 of M_s, contraction index 32 gq + k over the 4 lane groups */
+            float4 a4[8];
+            const float *mrow = segM + mo + (size_t)(16 * rt + r16) * KDA_DV + 32 * gq;
+#pragma unroll
+            for (int i = 0; i < 8; i++) a4[i] = *(const float4 *)(mrow + 4 * i);
+#pragma unroll
+            for (int k = 0; k < 32; k++) {
+                const float a = k % 4 == 0 ? a4[k / 4].x : k % 4 == 1 ? a4[k / 4].y : k % 4 == 2 ? a4[k / 4].z : a4[k / 4].w;
+                acc[rr] = mfma_f32x4(a, sS[chain_lds(32 * gq + k, r16)], acc[rr]);
+            }
+        }
+        __syncthreads(); /* every wave has read S_s */
+#pragma unroll
+        for (int rr = 0; rr < 2; rr++) {
+            const int rt = 2 * w + rr;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int R = 16 * rt + 4 * gq + e;
+                sS[chain_lds(R, r16)] = acc[rr][e];
+                segS[(size_t)(s + 1) * KDA_DK * KDA_DV + R * KDA_DV + 16 * nt + r16] = acc[rr][e];
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -520,25 +729,42 @@ kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ 
 
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
                                       int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
-                                      const void *init_state, void *final_state, int state_fp32,
-                                      hipStream_t st)
+                                      const void *init_state, void *final_state, int state_fp32, int64_t nseg,
+                                      void *seg_area, hipStream_t st)
 {
+    const unsigned char *rec = (const unsigned char *)records;
     const int64_t nchain = nseq * H;
+    if (nseg > 1) { /* segment-parallel (fixed-length batch, few chains) */
+        const int64_t cps = (T + KDA_CHUNK - 1) / KDA_CHUNK, segc = kda_seg_chunks(T, nseg);
+        float *area = (float *)seg_area;
+        const int64_t ngrp = nchain * (nseg - 1);
+        hipLaunchKernelGGL(kda_seg_map_kernel, dim3((unsigned)((ngrp + 7) / 8 * 128)), dim3(64), 0, st, rec, nchain,
+                           (int)H, nslots, cps, nseg, segc, area);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kda_seg_chain_kernel, dim3((unsigned)((nchain + 7) / 8 * 64)), dim3(256), 0, st, area,
+                           init_state, state_fp32, nchain, nseg);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kda_scan_seg_kernel, dim3((unsigned)((nchain * nseg + 7) / 8 * 64)), dim3(192), 0, st, rec,
+                           nseq, T, (int)H, nslots, (uint16_t *)out, final_state, state_fp32, nseg, segc,
+                           (const float *)(area + (size_t)2 * ngrp * KDA_DK * KDA_DV));
+        return hipGetLastError();
+    }
     if (nchain < KDA_MANY_CHAINS) {
-        hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)((nchain + 7) / 8 * 64)), dim3(192), 0, st,
-                           (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H, nslots,
-                           (uint16_t *)out, init_state, final_state, state_fp32, (const int32_t *)nullptr);
+        hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)((nchain + 7) / 8 * 64)), dim3(192), 0, st, rec, cu,
+                           chunk_off, nseq, T, (int)H, nslots, (uint16_t *)out, init_state, final_state, state_fp32,
+                           (const int32_t *)nullptr);
         return hipGetLastError();
     }
     const int64_t max_chunks = cu == nullptr ? INT64_MAX : (int64_t)KDA_MANY_MAX_CHUNKS;
-    hipLaunchKernelGGL(kda_scan_many_kernel, dim3((unsigned)nchain), dim3(512), 0, st,
-                       (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H, nslots, (uint16_t *)out,
-                       init_state, final_state, state_fp32, max_chunks);
+    hipLaunchKernelGGL(kda_scan_many_kernel, dim3((unsigned)nchain), dim3(512), 0, st, rec, cu, chunk_off, nseq, T,
+                       (int)H, nslots, (uint16_t *)out, init_state, final_state, state_fp32, max_chunks);
     const hipError_t e = hipGetLastError();
     const int64_t max_long = kda_max_long_seqs(T);
     if (e != hipSuccess || cu == nullptr || max_long == 0) return e;
-    hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)((max_long * H + 7) / 8 * 64)), dim3(192), 0, st,
-                       (const unsigned char *)records, cu, chunk_off, nseq, T, (int)H, nslots,
-                       (uint16_t *)out, init_state, final_state, state_fp32, chunk_off + nseq + 1);
+    hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)((max_long * H + 7) / 8 * 64)), dim3(192), 0, st, rec, cu,
+                       chunk_off, nseq, T, (int)H, nslots, (uint16_t *)out, init_state, final_state, state_fp32,
+                       chunk_off + nseq + 1);
     return hipGetLastError();
 }

@@ -185,6 +185,43 @@ def test_many_chain_fixed_batch():
         assert np.array_equal(ob, o[b:b + 1]) and np.array_equal(fb, f[b:b + 1]), b
 
 
+# Fixed-length batches of at most 10 long (sequence, head) chains take the
+# segment-parallel scan (segment maps M, B; their fp32 chaining; a rescan of
+# every segment). It agrees with the oracle to the same bar as the plain scan,
+# and with the plain scan that the one-sequence varlen form of the same input
+# runs, to rounding.
+@pytest.mark.parametrize("B,T,H,state", [(1, 8192, 2, "fp32"), (1, 8192 - 37, 1, "bf16"), (2, 5000, 3, "fp32"),
+                                         (1, 4096, 4, None)])
+def test_segmented_scan(B, T, H, state):
+    gu = _gpu()
+    import kimi_delta_attention_fwd_amd as kda
+    nchunk = (T + 63) // 64
+    assert B * H <= 10 and nchunk >= 48  # the sizes that select three or more segments
+    d = ki.make_inputs(B, T, H, seed=23 + T, state=state or "fp32", initial=state is not None, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=d["final"])
+    check("segmented B=%d T=%d H=%d out" % (B, T, H), o, ro)
+    if d["final"]:
+        check("segmented B=%d T=%d H=%d final" % (B, T, H), f, rf)
+    # the same batch as packed sequences (cu_seqlens): the plain scan
+    e = dict(d)
+    for key in ("q", "k", "v", "g", "beta"):
+        e[key] = np.ascontiguousarray(d[key].reshape((1, B * T) + d[key].shape[2:]))
+    e.update(B=1, T=B * T, N=B, cu_seqlens=np.arange(B + 1, dtype=np.int64) * T)
+    op, fp = gu.run_gpu(e)
+    assert oracle.rel_l2(op.reshape(o.shape), o) < 2e-3
+    if d["final"]:
+        assert oracle.rel_l2(fp, f) < 2e-3
+
+
+def test_segmented_in_place_state():
+    gu = _gpu()
+    d = ki.make_inputs(1, 6000, 2, seed=24, state="fp32", initial=True, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    o2, f2 = gu.run_gpu(d, in_place=True)
+    assert np.array_equal(o, o2) and np.array_equal(f, f2)
+
+
 def test_batch_equals_separate_bitwise():
     gu = _gpu()
     d = ki.make_inputs(3, 150, 2, seed=10, state="bf16", initial=True)
