@@ -80,8 +80,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload 0..4 (default: 3, the long prefill)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=32768,
-                    help="prefix length on which the oracle is timed (all heads)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="prefix length on which the oracle is timed, all heads (0: the whole workload)")
+    ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
+                    help="repeat the oracle over the sample until this much time has passed")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
     ap.add_argument("--decode", action="store_true",
                     help="time the single-token decode step instead (512 sequences x 64 heads, fp32 state)")
@@ -208,7 +210,7 @@ def main():
 
     if not args.no_cpu:
         import oracle
-        ts = min(args.cpu_sample_tokens, T) if cu is None else T
+        ts = T if (cu is not None or args.cpu_sample_tokens <= 0) else min(args.cpu_sample_tokens, T)
         if cu is None:
             sub = dict(d)
             for key in ("q", "k", "v", "g", "beta"):
@@ -217,15 +219,21 @@ def main():
         else:
             sub = d
         threads = oracle.max_threads()
-        tc0 = time.perf_counter()
-        ro, _ = oracle.fwd_inputs(sub, want_final=False)
-        tc = time.perf_counter() - tc0
+        tc, reps = 0.0, 0
+        while reps == 0 or tc < args.cpu_min_seconds:
+            tc0 = time.perf_counter()
+            ro, _ = oracle.fwd_inputs(sub, want_final=False)
+            tc += time.perf_counter() - tc0
+            reps += 1
         sample_th = ki.token_heads(sub)
         got = out[:, :sub["T"]].float().cpu().numpy()
-        res["cpu_baseline"] = {"value": sample_th / tc, "unit": "token*heads/s", "cores": threads,
+        res["cpu_baseline"] = {"value": reps * sample_th / tc, "unit": "token*heads/s", "cores": threads,
                                "kind": "oracle",
-                               "sample": "fp64 per-token recurrence on the first %d tokens x %d heads of the "
-                                         "same workload (%d token-heads, %.1f s)" % (sub["T"], H, sample_th, tc)}
+                               "sample": "fp64 per-token recurrence on %s (%d tokens x %d heads = %d token-heads), "
+                                         "%d passes in %.1f s" % (
+                                             "the whole workload" if sub["T"] == T else
+                                             "the first %d tokens of the workload" % sub["T"],
+                                             sub["T"], H, sample_th, reps, tc)}
         res["parity_sample"] = {"rel_l2": oracle.rel_l2(got, ro), "max_abs": oracle.max_abs(got, ro),
                                 "tokens": sub["T"]}
     print(json.dumps(res), flush=True)
@@ -296,12 +304,15 @@ def run_decode(args):
     }
     if not args.no_cpu:
         import oracle
-        tc0 = time.perf_counter()
-        ro, rf = oracle.fwd_inputs(d, want_final=True)
-        tc = time.perf_counter() - tc0
-        res["cpu_baseline"] = {"value": units / tc, "unit": "token*heads/s", "cores": oracle.max_threads(),
+        tc, reps = 0.0, 0
+        while reps == 0 or tc < args.cpu_min_seconds:
+            tc0 = time.perf_counter()
+            ro, rf = oracle.fwd_inputs(d, want_final=True)
+            tc += time.perf_counter() - tc0
+            reps += 1
+        res["cpu_baseline"] = {"value": reps * units / tc, "unit": "token*heads/s", "cores": oracle.max_threads(),
                                "kind": "oracle", "sample": "fp64 recurrence on the whole workload (%d "
-                               "token-heads, %.2f s)" % (units, tc)}
+                               "token-heads), %d passes in %.1f s" % (units, reps, tc)}
         # parity of one step from the initial state
         state.copy_(state0)
         step()
