@@ -167,6 +167,21 @@ def test_many_chain_scan(state):
         assert np.array_equal(on, o[:, a:b]) and np.array_equal(fn[0], f[n]), n
 
 
+def test_many_sequences_chunk_table():
+    """3000 packed sequences: the chunk table's prefix sums (chunk offsets and the
+    list of sequences of more than 128 chunks) carry across its 1024-thread
+    passes; long sequences sit in the second and third passes."""
+    gu = _gpu()
+    rng = np.random.default_rng(25)
+    lens = [int(x) for x in rng.integers(0, 40, 3000)]
+    lens[1500], lens[2999], lens[700] = 8300, 9000, 130
+    d = ki.make_inputs(1, sum(lens), 1, seed=25, lengths=lens, state="fp32", initial=True, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("3000 seqs out", o, ro)
+    check("3000 seqs final", f, rf)
+
+
 def test_many_chain_fixed_batch():
     """A fixed-length batch of 128 chains (eight-wave kernel) against the oracle
     and, bit for bit, against single-sequence calls (three-wave kernel)."""
