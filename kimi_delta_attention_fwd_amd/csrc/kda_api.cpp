@@ -27,7 +27,7 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
                                       int64_t nslots, void *records, hipStream_t st);
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
                                       int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
-                                      const void *init_state, void *final_state, int state_fp32, int64_t nseg,
+                                      const void *init_state, void *final_state, int state_fp32, int64_t segc,
                                       void *seg_area, hipStream_t st);
 extern "C" hipError_t kda_launch_decode(const void *q, const void *k, const void *v, const void *g,
                                         const void *beta, const float *A_log, const float *dt_bias, float scale,
@@ -208,7 +208,7 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
         ProfScope ps("kda_scan", st);
         if (kda_launch_scan(records, cu_seqlens, chunk_off, N, T, H, nslots, out,
                             state_dtype == KDA_STATE_NONE ? nullptr : initial_state, final_state,
-                            state_dtype == KDA_STATE_FP32 ? 1 : 0, kda_scan_segments(B, T, H, nseq_arg),
+                            state_dtype == KDA_STATE_FP32 ? 1 : 0, kda_seg_len(B, T, H, nseq_arg),
                             (unsigned char *)records + (size_t)nslots * (size_t)H * KDA_REC_BYTES, st) != hipSuccess)
             return KDA_ERR_HIP;
     }

@@ -73,34 +73,39 @@ static inline int64_t kda_max_chunks(int64_t B, int64_t T, int64_t num_seqs)
     return B * ((T + KDA_CHUNK - 1) / KDA_CHUNK);
 }
 
-/* Segment-parallel scan (fixed-length batches with few, long chains): the
- * chunks of each chain are cut into G segments of kda_seg_chunks chunks (the
- * last takes the rest). The state after a segment is an affine function of the
- * state entering it, S -> M S + B; M and B of every segment are computed in
- * parallel, chained in a short pass, and each segment is then rescanned from
- * its entering state. G = 1 means the plain scan. */
-static inline int64_t kda_scan_segments(int64_t B, int64_t T, int64_t H, int64_t num_seqs)
+/* Segment-parallel scan (few, long chains: B * H or num_seqs * H <= 10). The
+ * chunks of each chain are cut into segments of kda_seg_len chunks (about 32
+ * segments over all chains, at least 16 chunks each; a sequence's last segment
+ * takes the rest). The state after a segment is an affine function of the state
+ * entering it, S -> M S + B; M and B of every segment are computed in parallel,
+ * chained in a short pass, and each segment is then rescanned from its entering
+ * state. kda_seg_len returns 0 (the plain scan) unless the longest possible
+ * sequence has at least 3 segments. */
+static inline int64_t kda_seg_len(int64_t B, int64_t T, int64_t H, int64_t num_seqs)
 {
-    if (num_seqs > 0 || B <= 0 || T <= 0 || H <= 0) return 1;
-    const int64_t nchain = B * H, nchunk = (T + KDA_CHUNK - 1) / KDA_CHUNK;
-    if (nchain > 16) return 1;
-    int64_t G = 32 / nchain;           /* about 256 workgroups in the rescan */
-    if (G > nchunk / 16) G = nchunk / 16; /* segments of at least 16 chunks */
-    while (G >= 3 && (G - 1) * ((nchunk + G - 1) / G) >= nchunk) G--; /* every segment non-empty */
-    return G >= 3 ? G : 1;
+    if (B <= 0 || T <= 0 || H <= 0 || num_seqs < 0) return 0;
+    const int64_t nchain = (num_seqs > 0 ? num_seqs : B) * H;
+    if (nchain > 10) return 0;
+    const int64_t maxc = (T + KDA_CHUNK - 1) / KDA_CHUNK;   /* chunks of the longest possible sequence */
+    const int64_t total = num_seqs > 0 ? maxc : B * maxc;   /* chunks over all sequences (about) */
+    int64_t segc = (total * H + 31) / 32;
+    if (segc < 16) segc = 16;
+    return (maxc + segc - 1) / segc >= 3 ? segc : 0;
 }
-static inline int64_t kda_seg_chunks(int64_t T, int64_t G)
+/* segment slots per chain: the most segments a sequence of at most T tokens has */
+static inline int64_t kda_seg_slots(int64_t T, int64_t segc)
 {
-    const int64_t nchunk = (T + KDA_CHUNK - 1) / KDA_CHUNK;
-    return (nchunk + G - 1) / G;
+    return ((T + KDA_CHUNK - 1) / KDA_CHUNK + segc - 1) / segc;
 }
-/* segment area after the records (fp32 128 x 128 blocks): M and B of segments
- * 0 .. G-2, [B * H][G - 1] each, then the entering states of segments 0 .. G-1,
- * [B * H][G] (segment 0's is the initial state, copied) */
+/* segment area after the records (fp32 128 x 128 blocks), G = kda_seg_slots:
+ * M and B of segment slots 0 .. G-2, [chains][G - 1] each, then the entering
+ * states of slots 0 .. G-1, [chains][G] (slot 0's is the initial state, copied) */
 static inline size_t kda_seg_bytes(int64_t B, int64_t T, int64_t H, int64_t num_seqs)
 {
-    const int64_t G = kda_scan_segments(B, T, H, num_seqs);
-    return G > 1 ? (size_t)(B * H) * (size_t)(3 * G - 2) * KDA_DK * KDA_DV * 4 : 0;
+    const int64_t segc = kda_seg_len(B, T, H, num_seqs);
+    if (segc == 0) return 0;
+    const int64_t G = kda_seg_slots(T, segc), nchain = (num_seqs > 0 ? num_seqs : B) * H;
+    return (size_t)nchain * (size_t)(3 * G - 2) * KDA_DK * KDA_DV * 4;
 }
 
 #endif

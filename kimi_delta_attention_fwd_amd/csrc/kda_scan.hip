@@ -210,14 +210,16 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     }
     int64_t nchunk = (eos - bos + KDA_CHUNK - 1) / KDA_CHUNK;
     /* a segment of the segment-parallel scan: chunks seg * segc .. from the
-       entering state the combine pass left in seg_init (fp32; segment 0's is a
+       entering state the chaining pass left in seg_init (fp32; segment 0's is a
        copy of the initial state, so an in-place final state cannot race with
-       it); only the last segment writes the final state */
+       it); only the sequence's last segment writes the final state */
     const void *ist = init_state;
     int ist_fp32 = state_fp32;
     size_t ibase = (size_t)chain * KDA_DK * KDA_DV;
     void *fst = final_state;
     if (SEG) {
+        const int64_t nseg_seq = nchunk > segc ? (nchunk + segc - 1) / segc : 1;
+        if (seg >= nseg_seq) return;
         const int64_t c_first = seg * segc;
         nchunk = nchunk - c_first < segc ? nchunk - c_first : segc;
         bos += c_first * KDA_CHUNK;
@@ -225,7 +227,7 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
         ist = seg_init;
         ist_fp32 = 1;
         ibase = ((size_t)chain * nseg + seg) * KDA_DK * KDA_DV;
-        if (seg < nseg - 1) fst = nullptr;
+        if (seg < nseg_seq - 1) fst = nullptr;
     }
     const unsigned char *rec0 = rec_base + ((size_t)h * nslots + slot0) * KDA_REC_BYTES;
     /* record of chunk c, clamped to the last one (its reload is harmless) */
@@ -332,13 +334,14 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
                      1, 0, nullptr);
 }
 
-/* the rescan of the segment-parallel scan: workgroup (chain, segment, tile) */
+/* the rescan of the segment-parallel scan: workgroup (chain, segment slot, tile) */
 extern "C" __global__ void __launch_bounds__(192)
-kda_scan_seg_kernel(const unsigned char *__restrict__ rec_base, int64_t nseq, int64_t T, int H, int64_t nslots,
+kda_scan_seg_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
+                    const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
                     uint16_t *__restrict__ out, void *__restrict__ final_state, int state_fp32, int64_t nseg,
                     int64_t segc, const float *__restrict__ seg_init)
 {
-    scan_body<true>(rec_base, nullptr, nullptr, nseq, T, H, nslots, out, nullptr, final_state, state_fp32, nullptr,
+    scan_body<true>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, nullptr, final_state, state_fp32, nullptr,
                     nseg, segc, seg_init);
 }
 
@@ -390,10 +393,31 @@ __device__ __forceinline__ void map_step(ScanSetS &X, ScanSetS &Y, f32x4 (&S)[8]
         for (int mt = 0; mt < 8; mt++) S[mt] = mfma(X.K[mt * 2 + jb], db[jb], S[mt]);
 }
 
-/* one wave per (chain, segment < G - 1, 16-column tile of [B | M]); the 16
-   tiles of a segment run on one XCD and share its L2 */
+/* chunks and first chunk slot of sequence seq (fixed-length batch or packed) */
+__device__ __forceinline__ void seq_chunks(int64_t seq, const int32_t *cu, const int32_t *chunk_off, int64_t T,
+                                           int64_t &nchunk, int64_t &slot0)
+{
+    if (cu == nullptr) {
+        nchunk = (T + KDA_CHUNK - 1) / KDA_CHUNK;
+        slot0 = seq * nchunk;
+    } else {
+        nchunk = ((int64_t)cu[seq + 1] - cu[seq] + KDA_CHUNK - 1) / KDA_CHUNK;
+        slot0 = chunk_off[seq];
+    }
+}
+
+/* segments of a sequence of nchunk chunks (at least one, also when it is empty) */
+__device__ __forceinline__ int64_t seq_segments(int64_t nchunk, int64_t segc)
+{
+    return nchunk > segc ? (nchunk + segc - 1) / segc : 1;
+}
+
+/* one wave per (chain, segment slot < G - 1, 16-column tile of [B | M]); the 16
+   tiles of a segment run on one XCD and share its L2. Only segments that are
+   not their sequence's last are mapped; they hold segc full chunks. */
 extern "C" __global__ void __launch_bounds__(64)
-kda_seg_map_kernel(const unsigned char *rec_base, int64_t nchain, int H, int64_t nslots, int64_t cps,
+kda_seg_map_kernel(const unsigned char *rec_base, const int32_t *__restrict__ cu,
+                   const int32_t *__restrict__ chunk_off, int64_t nchain, int64_t T, int H, int64_t nslots,
                    int64_t nseg, int64_t segc, float *seg_area)
 {
     const int l = threadIdx.x, g = l >> 4, n16 = l & 15;
@@ -405,9 +429,12 @@ kda_seg_map_kernel(const unsigned char *rec_base, int64_t nchain, int H, int64_t
     const int64_t chain = grp / (nseg - 1), seg = grp - chain * (nseg - 1);
     const int64_t seq = chain / H;
     const int h = (int)(chain - seq * H);
+    int64_t nchunk, slot0;
+    seq_chunks(seq, cu, chunk_off, T, nchunk, slot0);
+    if (seg >= seq_segments(nchunk, segc) - 1) return;
     const bool homog = t16 >= 8;
     const int nt = t16 & 7;
-    const unsigned char *rec0 = rec_base + ((size_t)h * nslots + seq * cps + seg * segc) * KDA_REC_BYTES;
+    const unsigned char *rec0 = rec_base + ((size_t)h * nslots + slot0 + seg * segc) * KDA_REC_BYTES;
     auto rec_of = [&](int64_t c) { return rec0 + (size_t)(c < segc ? c : segc - 1) * KDA_REC_BYTES; };
     const int ubase = KDA_REC_U + nt * 2048;
 
@@ -447,10 +474,12 @@ __device__ __forceinline__ f32x4 mfma_f32x4(float a, float b, const f32x4 &c)
 __host__ __device__ constexpr int chain_lds(int R, int j) { return R * 16 + (R >> 5) * 8 + j; }
 
 /* one workgroup of 4 waves per (chain, 16-column tile): S_0 = initial state,
-   S_{s+1} = M_s S_s + B_s for s < G - 1, in fp32 (v_mfma_f32_16x16x4f32); wave w
-   computes row tiles 2 w, 2 w + 1 of each product. Writes S_0 .. S_{G-1}. */
+   S_{s+1} = M_s S_s + B_s for s below the sequence's segment count - 1, in fp32
+   (v_mfma_f32_16x16x4f32); wave w computes row tiles 2 w, 2 w + 1 of each
+   product. Writes S_0 .. S_{segments - 1} of the chain's G slots. */
 extern "C" __global__ void __launch_bounds__(256)
-kda_seg_chain_kernel(float *seg_area, const void *init_state, int state_fp32, int64_t nchain, int64_t nseg)
+kda_seg_chain_kernel(float *seg_area, const void *init_state, int state_fp32, const int32_t *__restrict__ cu,
+                     int64_t T, int H, int64_t nchain, int64_t nseg, int64_t segc)
 {
     __shared__ float sS[chain_lds(127, 15) + 1];
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, gq = l >> 4, r16 = l & 15;
@@ -459,6 +488,10 @@ kda_seg_chain_kernel(float *seg_area, const void *init_state, int state_fp32, in
     const int nt = (int)(qd & 7);
     const int64_t chain = (qd >> 3) * 8 + xcd;
     if (chain >= nchain) return;
+    const int64_t seq = chain / H;
+    const int64_t nchunk = cu == nullptr ? (T + KDA_CHUNK - 1) / KDA_CHUNK
+                                         : ((int64_t)cu[seq + 1] - cu[seq] + KDA_CHUNK - 1) / KDA_CHUNK;
+    const int64_t nsteps = seq_segments(nchunk, segc) - 1;
     const float *segM = seg_area + (size_t)nchain * (nseg - 1) * KDA_DK * KDA_DV;
     const float *segB = seg_area;
     float *segS = seg_area + (size_t)2 * nchain * (nseg - 1) * KDA_DK * KDA_DV + (size_t)chain * nseg * KDA_DK * KDA_DV;
@@ -472,7 +505,7 @@ kda_seg_chain_kernel(float *seg_area, const void *init_state, int state_fp32, in
         segS[R * KDA_DV + 16 * nt + j] = v;
     }
     __syncthreads();
-    for (int64_t s = 0; s < nseg - 1; s++) {
+    for (int64_t s = 0; s < nsteps; s++) {
         const size_t mo = ((size_t)chain * (nseg - 1) + s) * KDA_DK * KDA_DV;
         f32x4 acc[2];
 #pragma unroll
@@ -729,25 +762,25 @@ kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ 
 
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
                                       int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
-                                      const void *init_state, void *final_state, int state_fp32, int64_t nseg,
+                                      const void *init_state, void *final_state, int state_fp32, int64_t segc,
                                       void *seg_area, hipStream_t st)
 {
     const unsigned char *rec = (const unsigned char *)records;
     const int64_t nchain = nseq * H;
-    if (nseg > 1) { /* segment-parallel (fixed-length batch, few chains) */
-        const int64_t cps = (T + KDA_CHUNK - 1) / KDA_CHUNK, segc = kda_seg_chunks(T, nseg);
+    if (segc > 0) { /* segment-parallel (few long chains) */
+        const int64_t G = kda_seg_slots(T, segc);
         float *area = (float *)seg_area;
-        const int64_t ngrp = nchain * (nseg - 1);
-        hipLaunchKernelGGL(kda_seg_map_kernel, dim3((unsigned)((ngrp + 7) / 8 * 128)), dim3(64), 0, st, rec, nchain,
-                           (int)H, nslots, cps, nseg, segc, area);
+        const int64_t ngrp = nchain * (G - 1);
+        hipLaunchKernelGGL(kda_seg_map_kernel, dim3((unsigned)((ngrp + 7) / 8 * 128)), dim3(64), 0, st, rec, cu,
+                           chunk_off, nchain, T, (int)H, nslots, G, segc, area);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kda_seg_chain_kernel, dim3((unsigned)((nchain + 7) / 8 * 64)), dim3(256), 0, st, area,
-                           init_state, state_fp32, nchain, nseg);
+                           init_state, state_fp32, cu, T, (int)H, nchain, G, segc);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kda_scan_seg_kernel, dim3((unsigned)((nchain * nseg + 7) / 8 * 64)), dim3(192), 0, st, rec,
-                           nseq, T, (int)H, nslots, (uint16_t *)out, final_state, state_fp32, nseg, segc,
+        hipLaunchKernelGGL(kda_scan_seg_kernel, dim3((unsigned)((nchain * G + 7) / 8 * 64)), dim3(192), 0, st, rec,
+                           cu, chunk_off, nseq, T, (int)H, nslots, (uint16_t *)out, final_state, state_fp32, G, segc,
                            (const float *)(area + (size_t)2 * ngrp * KDA_DK * KDA_DV));
         return hipGetLastError();
     }
