@@ -1,8 +1,18 @@
 /*
- * kda_scan.hip -- gfx950 scan kernel of the chunked Kimi Delta Attention
- * forward: the sequential chunk loop per (sequence, head, 16 value columns)
- * with the fp32 state slice in MFMA accumulators. The records it consumes are
- * produced by kda_prep_kernel (layout in kda_internal.h).
+ * kda_scan.hip -- gfx950 scan kernels of the chunked Kimi Delta Attention
+ * forward: the sequential chunk loop per (sequence, head) with the fp32 state in
+ * MFMA accumulators, over the records kda_prep_kernel writes (layout in
+ * kda_internal.h). kda_launch_scan picks one of three forms from the sizes
+ * alone (no device data is read on the host):
+ *   kda_scan_kernel       3 waves per (chain, 16 value columns): fewer than 128
+ *                         chains, and the long sequences of packed batches;
+ *   kda_scan_many_kernel  8 waves per chain, the chunk's shared operands in
+ *                         LDS: 128 chains or more;
+ *   kda_seg_map_kernel, kda_seg_chain_kernel, kda_scan_seg_kernel
+ *                         segment-parallel: at most 10 long chains.
+ * All of them evaluate the same chunk update in the same order (bf16 operands,
+ * fp32 accumulation), so a chain gives the same bits on the first two; the
+ * segment-parallel form differs from them by rounding only.
  */
 #include "kda_device.h"
 
