@@ -107,6 +107,24 @@ def test_lower_bound_range(lb):
     check("lb=%g final" % lb, f, rf)
 
 
+def test_maximum_sizes():
+    """A sequence of 2^20 + 3 tokens (16,385 chunks, segment-parallel scan) and a
+    batch of 256 heads (64 KB token rows, many-chain scan), against the oracle."""
+    gu = _gpu()
+    T = (1 << 20) + 3
+    d = ki.make_inputs(1, T, 2, seed=28, state="fp32", initial=True, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("T=2^20+3 out", o, ro)
+    check("T=2^20+3 final", f, rf)
+    del d, o, ro
+    d = ki.make_inputs(1, 300, 256, seed=29, state="bf16", initial=True, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("H=256 out", o, ro)
+    check("H=256 final", f, rf)
+
+
 def test_unnormalised_inputs():
     """q and k that are not unit rows are normalised inside the kernel."""
     gu = _gpu()
