@@ -36,7 +36,7 @@ SCAN_BYTES_PER_TH = 256
 # only while the kernel's sources hash to the recorded value
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "kimi_delta_attention_fwd_amd", "csrc")
-KERNEL_SOURCES = {"kda_prep": ("kda_prep.hip", "kda_device.h", "kda_internal.h"),
+KERNEL_SOURCES = {"kda_prep": ("kda_prep.hip", "kda_device.h", "kda_internal.h", "../../include/kda.h"),
                   "kda_scan": ("kda_scan.hip", "kda_device.h", "kda_internal.h"),
                   "kda_decode": ("kda_decode.hip", "kda_device.h", "kda_internal.h")}
 # algorithmic MFMA flops per token-head with 16x16 blocks and 64-token chunks:
@@ -87,6 +87,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
     ap.add_argument("--decode", action="store_true",
                     help="time the single-token decode step instead (512 sequences x 64 heads, fp32 state)")
+    ap.add_argument("--lower-bound", type=float, default=None,
+                    help="override the workload's lower_bound (below -10 selects the wide-range chunk preparation)")
     ap.add_argument("--heads", type=int, default=0,
                     help="keep only the first N heads of the workload (one GPU's share when heads are sharded)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -120,6 +122,9 @@ def main():
             d["initial_state"] = np.ascontiguousarray(d["initial_state"][:, :nh])
         d["H"] = nh
         d["name"] = "%s_h%d" % (d["name"], nh)
+    if args.lower_bound is not None:
+        d["lower_bound"] = float(args.lower_bound)
+        d["name"] = "%s_lb%g" % (d["name"], args.lower_bound)
     print("[bench] inputs for workload %d (%s) drawn in %.1f s" % (args.config, d["name"], time.time() - t_gen),
           file=sys.stderr, flush=True)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)

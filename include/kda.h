@@ -60,8 +60,7 @@ typedef enum {
     KDA_ERR_SHAPE = 3,       /* B, T, H <= 0, num_seqs <= 0 with cu_seqlens, or
                                 B != 1 with cu_seqlens                             */
     KDA_ERR_STATE_DTYPE = 4, /* state_dtype inconsistent with the state pointers   */
-    KDA_ERR_ARG = 5,         /* scale or lower_bound non-finite, lower_bound > 0, or
-                                lower_bound < KDA_LOWER_BOUND_MIN                 */
+    KDA_ERR_ARG = 5,         /* scale or lower_bound non-finite, or lower_bound > 0 */
     KDA_ERR_WORKSPACE = 6,   /* workspace NULL, not 256-byte aligned, or smaller
                                 than kda_fwd_workspace_size                        */
     KDA_ERR_ALIAS = 7,       /* out overlaps an input, or the states overlap only
@@ -76,11 +75,14 @@ typedef enum {
     KDA_STATE_FP32 = 2
 } kda_state_dtype;
 
-/* Most negative lower_bound the chunked kernels evaluate exactly. Inside one
- * 16-token sub-chunk the decay factors are anchored at its middle token, so the
- * largest factor is exp(8 * |lower_bound|); -10 keeps it below the bf16/fp32
- * range (exp(88.7)). Smaller bounds are rejected with KDA_ERR_ARG. */
-#define KDA_LOWER_BOUND_MIN (-10.0f)
+/* Most negative lower_bound of the fast form of kda_fwd. Inside one 16-token
+ * sub-chunk the fast form anchors the decay factors at the middle token, so the
+ * largest factor is exp(8 * |lower_bound|); -10 keeps it inside the bf16/fp32
+ * range (exp(88.7)). Below it, kda_fwd builds every factor from exponents <= 0
+ * and evaluates the 16 x 16 diagonal blocks of the in-chunk matrices element by
+ * element (about 1.5 times the chunk preparation time); any finite
+ * lower_bound <= 0 is accepted. */
+#define KDA_LOWER_BOUND_NARROW (-10.0f)
 
 /*
  * kda_fwd -- chunked KDA forward (the flash_kda.fwd call of the pages).
@@ -89,8 +91,8 @@ typedef enum {
  *  scale            : multiplies the output only (finite).
  *  out              : bf16 [B, T, H, 128], written in full (round to nearest even).
  *  A_log, dt_bias   : fp32 gate parameters.
- *  lower_bound      : clamp of log a in natural-log units, in
- *                     [KDA_LOWER_BOUND_MIN, 0]; 0 means no decay.
+ *  lower_bound      : clamp of log a in natural-log units, finite and <= 0;
+ *                     0 means no decay (see KDA_LOWER_BOUND_NARROW).
  *  initial_state    : NULL (zero state) or [N, H, 128, 128] of state_dtype.
  *  final_state      : NULL (not returned) or [N, H, 128, 128] of state_dtype;
  *                     receives S after the last token of each sequence (bf16 is

@@ -17,14 +17,14 @@ import ctypes
 import os
 
 __all__ = ["fwd", "decode", "workspace_size", "status_string", "library_path", "load_library",
-           "profile_enable", "profile_read", "KDA_LOWER_BOUND_MIN", "KdaError"]
+           "profile_enable", "profile_read", "KDA_LOWER_BOUND_NARROW", "KdaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
 _lib = None
 
 KDA_STATE_NONE, KDA_STATE_BF16, KDA_STATE_FP32 = 0, 1, 2
-KDA_LOWER_BOUND_MIN = -10.0
+KDA_LOWER_BOUND_NARROW = -10.0  # below it kda_fwd takes its wide-range chunk preparation
 EXPORTED = ("kda_fwd", "kda_decode", "kda_fwd_workspace_size", "kda_status_string",
             "kda_profile_enable", "kda_profile_read")
 
@@ -116,8 +116,8 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
     """Chunked KDA forward on the current torch (ROCm) stream; fills ``out``.
 
     q, k, g: bf16 [B, T, H, 128]; v, out: bf16 [B, T, H, 128]; beta: bf16
-    [B, T, H]; A_log: fp32 [H]; dt_bias: fp32 [H, 128]; lower_bound in
-    [KDA_LOWER_BOUND_MIN, 0]; initial_state / final_state: None or
+    [B, T, H]; A_log: fp32 [H]; dt_bias: fp32 [H, 128]; lower_bound: finite,
+    <= 0; initial_state / final_state: None or
     [N, H, 128, 128] of one dtype (bf16 or fp32), final_state may be the same
     tensor as initial_state; cu_seqlens: None or int32 [N + 1] on the device
     (B must be 1). ``workspace`` (optional) is a uint8 device tensor of at least

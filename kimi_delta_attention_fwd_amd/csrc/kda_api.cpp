@@ -93,7 +93,7 @@ extern "C" const char *kda_status_string(int status)
     case KDA_ERR_STATE_DTYPE:
         return "KDA_ERR_STATE_DTYPE: state_dtype must be NONE exactly when no state is given, else BF16 or FP32";
     case KDA_ERR_ARG:
-        return "KDA_ERR_ARG: scale and lower_bound must be finite with lower_bound <= 0 (and >= -10 for kda_fwd)";
+        return "KDA_ERR_ARG: scale and lower_bound must be finite with lower_bound <= 0";
     case KDA_ERR_WORKSPACE:
         return "KDA_ERR_WORKSPACE: workspace is NULL, not 256-byte aligned, or smaller than kda_fwd_workspace_size";
     case KDA_ERR_ALIAS:
@@ -160,9 +160,7 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
     } else {
         return KDA_ERR_STATE_DTYPE;
     }
-    if (!std::isfinite(scale) || !std::isfinite(lower_bound) || lower_bound > 0.f ||
-        lower_bound < KDA_LOWER_BOUND_MIN)
-        return KDA_ERR_ARG;
+    if (!std::isfinite(scale) || !std::isfinite(lower_bound) || lower_bound > 0.f) return KDA_ERR_ARG;
     const int64_t nseq_arg = cu_seqlens ? num_seqs : 0;
     const size_t need = kda_fwd_workspace_size(B, T, H, nseq_arg);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return KDA_ERR_WORKSPACE;

@@ -11,6 +11,7 @@
  * Constraints"); the chunk algebra and the record layout are described in
  * kda_internal.h. Exponentials are taken base 2 (v_exp_f32) on log2-scaled sums.
  */
+#include "kda.h"
 #include "kda_device.h"
 
 /* ------------------------------------------------------------------------- */
@@ -123,12 +124,22 @@ __device__ __forceinline__ void store_transposed(const bf16x8 &fr, const bf16x8 
     *(uint2 *)dst1 = u1;
 }
 
-extern "C" __global__ void __launch_bounds__(256, 2)
-kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gt,
-                const uint16_t *beta, const float *__restrict__ A_log,
-                const float *__restrict__ dt_bias, float scale, float lower_bound,
-                const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
-                int64_t nseq, int64_t T, int H, int64_t nslots, unsigned char *__restrict__ rec_base)
+/* The prep body. WIDE (lower_bound below KDA_LOWER_BOUND_NARROW) builds every
+   decay factor from exponents <= 0 and evaluates the 16x16 diagonal blocks of A
+   and P element by element, so no factor overflows for any lower_bound:
+     row sides k^ 2^{c}, q^ 2^{c};  Q~ = q^ 2^{B_w + c},  R = k^ 2^{B_w + c};
+     K~ = k^ 2^{G_L - B_w - c};  off-diagonal key side k^ 2^{tot_w - c} 2^{B_i - B_{b+1}};
+     diagonal (r, j <= r): sum_c k^_r k^_j 2^{min(c_r - c_j, 0)} (partner token j's
+     values from the lanes of the same channel group).
+   (c = in-sub-chunk inclusive cumsum, tot_w = its value at the sub-chunk's last
+   row, B_w = G before sub-chunk w, all log2.) */
+template <bool WIDE>
+__device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gt,
+                                          const uint16_t *beta, const float *__restrict__ A_log,
+                                          const float *__restrict__ dt_bias, float scale, float lower_bound,
+                                          const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
+                                          int64_t nseq, int64_t T, int H, int64_t nslots,
+                                          unsigned char *__restrict__ rec_base)
 {
     __shared__ PrepShared sh;
     const int64_t slot = blockIdx.x / H;
@@ -227,10 +238,15 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
             if (m < ww) B += tm;
             GL += tm;
         }
-        const float gm = B + sh.u.p1.mid[ww][ch];
-        sh.u.p1.fq[ww][ch] = exp2_fast(gm);
-        sh.u.p1.fk[ww][ch] = exp2_fast(GL - gm);
-        sh.u.p1.fm[ww][ch] = exp2_fast(sh.u.p1.mid[ww][ch]);
+        if constexpr (WIDE) { /* log2 values: B_w and G_L - B_w */
+            sh.u.p1.fq[ww][ch] = B;
+            sh.u.p1.fk[ww][ch] = GL - B;
+        } else {
+            const float gm = B + sh.u.p1.mid[ww][ch];
+            sh.u.p1.fq[ww][ch] = exp2_fast(gm);
+            sh.u.p1.fk[ww][ch] = exp2_fast(GL - gm);
+            sh.u.p1.fm[ww][ch] = exp2_fast(sh.u.p1.mid[ww][ch]);
+        }
         if (ww == 0) ((float *)(rec + KDA_REC_GL))[ch] = exp2_fast(GL);
     }
     for (int p = tid; p < 6 * KDA_DK; p += 256) {
@@ -243,7 +259,8 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
             Bi += tm;
             if (m < b) Bb += tm;
         }
-        sh.u.p1.fy[pp][ch] = exp2_fast(Bi - (Bb + sh.u.p1.mid[b][ch]));
+        if constexpr (WIDE) sh.u.p1.fy[pp][ch] = exp2_fast(Bi - (Bb + sh.u.p1.tot[b][ch])); /* 2^{B_i - B_{b+1}} */
+        else sh.u.p1.fy[pp][ch] = exp2_fast(Bi - (Bb + sh.u.p1.mid[b][ch]));
     }
     __syncthreads();
 
@@ -263,19 +280,32 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
             for (int i = 0; i < 8; i++) {
                 const int j = kb * 8 + i;
                 const int ch = 32 * kb + kperm(g, i);
-                const float d = la[j] - sh.u.p1.mid[w][ch];
-                const float e1 = exp2_fast(d), e2 = exp2_fast(-d);
-                const float kh = kf[j] * ik;
-                const float xk = kh * e1, xq = qf[j] * iq * e1, ykv = kh * e2;
-                const float fq = sh.u.p1.fq[w][ch], fm = sh.u.p1.fm[w][ch];
-                xok_f[kb][i] = (__bf16)(xk * fm); /* k^ 2^{c}: anchored at the sub-chunk start */
-                xoq_f[kb][i] = (__bf16)(xq * fm);
-                xdk_f[kb][i] = (__bf16)xk;
-                xdq_f[kb][i] = (__bf16)xq;
-                yd_f[kb][i] = (__bf16)ykv;
-                qt_f[kb][i] = (__bf16)(xq * fq);
-                rf[i] = (__bf16)(xk * fq);
-                kt[i] = (__bf16)(ykv * sh.u.p1.fk[w][ch]);
+                if constexpr (WIDE) {
+                    const float c = la[j];
+                    const float kh = kf[j] * ik, qh = qf[j] * iq;
+                    const float ec = exp2_fast(c), eg = exp2_fast(sh.u.p1.fq[w][ch] + c);
+                    const float ek = exp2_fast(sh.u.p1.fk[w][ch] - c), ey = exp2_fast(sh.u.p1.tot[w][ch] - c);
+                    xok_f[kb][i] = (__bf16)(kh * ec);
+                    xoq_f[kb][i] = (__bf16)(qh * ec);
+                    yd_f[kb][i] = (__bf16)(kh * ey);
+                    qt_f[kb][i] = (__bf16)(qh * eg);
+                    rf[i] = (__bf16)(kh * eg);
+                    kt[i] = (__bf16)(kh * ek);
+                } else {
+                    const float d = la[j] - sh.u.p1.mid[w][ch];
+                    const float e1 = exp2_fast(d), e2 = exp2_fast(-d);
+                    const float kh = kf[j] * ik;
+                    const float xk = kh * e1, xq = qf[j] * iq * e1, ykv = kh * e2;
+                    const float fq = sh.u.p1.fq[w][ch], fm = sh.u.p1.fm[w][ch];
+                    xok_f[kb][i] = (__bf16)(xk * fm); /* k^ 2^{c}: anchored at the sub-chunk start */
+                    xoq_f[kb][i] = (__bf16)(xq * fm);
+                    xdk_f[kb][i] = (__bf16)xk;
+                    xdq_f[kb][i] = (__bf16)xq;
+                    yd_f[kb][i] = (__bf16)ykv;
+                    qt_f[kb][i] = (__bf16)(xq * fq);
+                    rf[i] = (__bf16)(xk * fq);
+                    kt[i] = (__bf16)(ykv * sh.u.p1.fk[w][ch]);
+                }
             }
             sh.u.p1.yd[w][kb][l] = yd_f[kb];
             /* key tiles 2 kb and 2 kb + 1 of R, V and K~ */
@@ -296,10 +326,43 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
     for (int b = 0; b < 4; b++) { at[b] = zero4(); pt[b] = zero4(); }
     {
         f32x4 ad = zero4(), pd = zero4();
+        if constexpr (WIDE) {
+            /* partial sums over this lane's 32 channels for partner token jj of the
+               sub-chunk (lane 16 g + jj holds the same channels), then the sum over
+               the 4 channel groups; lane (g, r16) keeps partners 4 g .. 4 g + 3 */
+            float sa[16], sp[16];
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++) {
-            ad = mfma(yd_f[kb], xdk_f[kb], ad);
-            pd = mfma(yd_f[kb], xdq_f[kb], pd);
+            for (int jj = 0; jj < 16; jj++) { sa[jj] = 0.f; sp[jj] = 0.f; }
+#pragma unroll
+            for (int j = 0; j < 32; j++) {
+                const float kh = kf[j] * ik, qh = qf[j] * iq, c = la[j];
+#pragma unroll
+                for (int jj = 0; jj < 16; jj++) {
+                    const int src = (l & 48) | jj;
+                    const float kp = __shfl(kh, src), cp = __shfl(c, src);
+                    const float t = kp * exp2_fast(fminf(c - cp, 0.f));
+                    sa[jj] += kh * t;
+                    sp[jj] += qh * t;
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < 16; jj++) {
+                sa[jj] += __shfl_xor(sa[jj], 16);
+                sa[jj] += __shfl_xor(sa[jj], 32);
+                sp[jj] += __shfl_xor(sp[jj], 16);
+                sp[jj] += __shfl_xor(sp[jj], 32);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+#pragma unroll
+                for (int jj = 0; jj < 16; jj++)
+                    if (jj == 4 * g + e) { ad[e] = sa[jj]; pd[e] = sp[jj]; }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; kb++) {
+                ad = mfma(yd_f[kb], xdk_f[kb], ad);
+                pd = mfma(yd_f[kb], xdq_f[kb], pd);
+            }
         }
         for (int b = 0; b < w; b++) {
             /* key side k^_j 2^{m_b - c_j} 2^{B_w - Gm_b} = k^_j 2^{B_w - G_j} <= 1 */
@@ -490,6 +553,29 @@ kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const u
     }
 }
 
+extern "C" __global__ void __launch_bounds__(256, 2)
+kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gt,
+                const uint16_t *beta, const float *__restrict__ A_log,
+                const float *__restrict__ dt_bias, float scale, float lower_bound,
+                const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
+                int64_t nseq, int64_t T, int H, int64_t nslots, unsigned char *__restrict__ rec_base)
+{
+    prep_body<false>(q, k, v, gt, beta, A_log, dt_bias, scale, lower_bound, cu, chunk_off, nseq, T, H, nslots,
+                     rec_base);
+}
+
+/* lower_bound below KDA_LOWER_BOUND_NARROW */
+extern "C" __global__ void __launch_bounds__(256, 2)
+kda_prep_wide_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gt,
+                     const uint16_t *beta, const float *__restrict__ A_log,
+                     const float *__restrict__ dt_bias, float scale, float lower_bound,
+                     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
+                     int64_t nseq, int64_t T, int H, int64_t nslots, unsigned char *__restrict__ rec_base)
+{
+    prep_body<true>(q, k, v, gt, beta, A_log, dt_bias, scale, lower_bound, cu, chunk_off, nseq, T, H, nslots,
+                    rec_base);
+}
+
 /* ------------------------------------------------------------------------- */
 /* launchers (called by kda_api.cpp after validation)                          */
 /* ------------------------------------------------------------------------- */
@@ -507,7 +593,8 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
                                       int64_t nslots, void *records, hipStream_t st)
 {
     const int64_t blocks = nslots * H;
-    hipLaunchKernelGGL(kda_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+    hipLaunchKernelGGL(lower_bound < KDA_LOWER_BOUND_NARROW ? kda_prep_wide_kernel : kda_prep_kernel,
+                       dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
                        (const uint16_t *)g, (const uint16_t *)beta, A_log, dt_bias, scale,
                        lower_bound, cu, chunk_off, nseq, T, (int)H, nslots, (unsigned char *)records);

@@ -97,8 +97,10 @@ def test_no_state_and_final_only():
     assert f2 is None and np.array_equal(o2, o)
 
 
-@pytest.mark.parametrize("lb", [0.0, -1.0, -10.0])
+@pytest.mark.parametrize("lb", [0.0, -1.0, -10.0, -10.5, -20.0, -60.0, -1000.0])
 def test_lower_bound_range(lb):
+    """Below -10 the chunk preparation builds every decay factor from exponents
+    <= 0 and sums the diagonal blocks element by element (any finite bound)."""
     gu = _gpu()
     d = ki.make_inputs(1, 256, 2, seed=7, lower_bound=lb, state="fp32", initial=True, sigma=0.05)
     o, f = gu.run_gpu(d)
@@ -413,7 +415,7 @@ def test_errors_raise():
     with pytest.raises(ValueError, match="KDA_ERR_ARG"):
         kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], out, t["A_log"], t["dt_bias"], 0.5)
     with pytest.raises(ValueError, match="KDA_ERR_ARG"):
-        kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], out, t["A_log"], t["dt_bias"], -11.0)
+        kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], out, t["A_log"], t["dt_bias"], float("nan"))
     with pytest.raises(ValueError, match="KDA_ERR_ALIAS"):
         kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], t["v"], t["A_log"], t["dt_bias"], -5.0)
     s32 = torch.zeros((1, 1, 128, 128), dtype=torch.float32, device=gu.DEV)

@@ -67,7 +67,7 @@ def rel(a, b):
     return oracle.rel_l2(a, b)
 
 
-@pytest.mark.parametrize("lb", [-5.0, -3.0, -10.0])
+@pytest.mark.parametrize("lb", [-5.0, -3.0, -10.0, -20.0, -200.0])
 def test_records_match_chunk_twin(lb):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
