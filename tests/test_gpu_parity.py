@@ -296,6 +296,42 @@ def test_segmented_exact_invariants():
         assert err < 2e-2, (t, err)
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_segmented_long_memory(packed):
+    """Weak decay (A_log = -12, a per-token decay of about e^-4e-6) and small beta
+    (at most 0.02): the state keeps its memory across all segments, so the
+    segment maps M are far from zero and their chaining is exercised (with the
+    default inputs the state forgets its start within a segment and M underflows
+    to 0). Against the oracle, and against the plain scan of the same sequences."""
+    gu = _gpu()
+    lens = [8192, 3000]
+    d = ki.make_inputs(1, sum(lens), 2, seed=32, lengths=lens if packed else None, state="fp32", initial=True,
+                       sigma=0.5) if packed else \
+        ki.make_inputs(1, 8192, 2, seed=32, state="fp32", initial=True, sigma=0.5)
+    d["A_log"][:] = -12.0
+    d["beta"] = ki.f32_to_bf16_bits(ki.bf16_bits_to_f32(d["beta"]) * np.float32(0.02))
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("long-memory %s out" % ("packed" if packed else "batch"), o, ro)
+    check("long-memory %s final" % ("packed" if packed else "batch"), f, rf)
+    # the plain scan: the same sequences plus 5 one-token sequences (more than 10 chains)
+    ls = lens if packed else [8192]
+    n, t = len(ls), sum(ls)
+    e = ki.make_inputs(1, t + 5, 2, seed=33, lengths=ls + [1] * 5, state="fp32", initial=True, sigma=0.5)
+    for key in ("q", "k", "v", "g", "beta"):
+        e[key][:, :t] = d[key].reshape(e[key][:, :t].shape)
+    for key in ("A_log", "dt_bias"):
+        e[key] = d[key]
+    e["initial_state"][:n] = d["initial_state"]
+    o2, f2 = gu.run_gpu(e)
+    assert oracle.rel_l2(o2[:, :t].reshape(o.shape), o) < 2e-3 and oracle.rel_l2(f2[:n], f) < 2e-3
+    # the first chunk's state really persists: the final state still depends on it
+    d0 = dict(d)
+    d0["initial_state"] = np.zeros_like(d["initial_state"])
+    _, f0 = gu.run_gpu(d0)
+    assert oracle.rel_l2(f0, f) > 1e-2
+
+
 def test_segmented_in_place_state():
     gu = _gpu()
     d = ki.make_inputs(1, 6000, 2, seed=24, state="fp32", initial=True, sigma=0.05)
