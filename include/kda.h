@@ -57,8 +57,9 @@ typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL = 1,        /* a required pointer is NULL                         */
     KDA_ERR_HEAD_DIM = 2,    /* K != 128 or V != 128                               */
-    KDA_ERR_SHAPE = 3,       /* B, T, H <= 0, num_seqs <= 0 with cu_seqlens, or
-                                B != 1 with cu_seqlens                             */
+    KDA_ERR_SHAPE = 3,       /* B, T, H <= 0, num_seqs <= 0 with cu_seqlens,
+                                B != 1 with cu_seqlens, or sizes past the limits
+                                below (KDA_MAX_HEADS, 32-bit grids and offsets)     */
     KDA_ERR_STATE_DTYPE = 4, /* state_dtype inconsistent with the state pointers   */
     KDA_ERR_ARG = 5,         /* scale or lower_bound non-finite, or lower_bound > 0 */
     KDA_ERR_WORKSPACE = 6,   /* workspace NULL, not 256-byte aligned, or smaller
@@ -74,6 +75,12 @@ typedef enum {
     KDA_STATE_BF16 = 1,
     KDA_STATE_FP32 = 2
 } kda_state_dtype;
+
+/* Size limits (checked, KDA_ERR_SHAPE): H <= KDA_MAX_HEADS (a chunk's rows are
+ * addressed with 32-bit byte offsets); with cu_seqlens, T <= INT32_MAX (int32
+ * offsets); for kda_fwd, (chunk slots) * H and 8 * N * H at most INT32_MAX, and for
+ * kda_decode N * H at most INT32_MAX (launch grids). */
+#define KDA_MAX_HEADS 65536
 
 /* Most negative lower_bound of the fast form of kda_fwd. Inside one 16-token
  * sub-chunk the fast form anchors the decay factors at the middle token, so the

@@ -17,7 +17,7 @@ import ctypes
 import os
 
 __all__ = ["fwd", "decode", "workspace_size", "status_string", "library_path", "load_library",
-           "profile_enable", "profile_read", "KDA_LOWER_BOUND_NARROW", "KdaError"]
+           "profile_enable", "profile_read", "KDA_LOWER_BOUND_NARROW", "KDA_MAX_HEADS", "KdaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -25,6 +25,7 @@ _lib = None
 
 KDA_STATE_NONE, KDA_STATE_BF16, KDA_STATE_FP32 = 0, 1, 2
 KDA_LOWER_BOUND_NARROW = -10.0  # below it kda_fwd takes its wide-range chunk preparation
+KDA_MAX_HEADS = 65536  # H limit of kda_fwd and kda_decode (KDA_ERR_SHAPE above it)
 EXPORTED = ("kda_fwd", "kda_decode", "kda_fwd_workspace_size", "kda_status_string",
             "kda_profile_enable", "kda_profile_read")
 

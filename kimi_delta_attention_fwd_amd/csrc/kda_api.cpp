@@ -89,7 +89,7 @@ extern "C" const char *kda_status_string(int status)
     case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
     case KDA_ERR_HEAD_DIM: return "KDA_ERR_HEAD_DIM: K and V must both be 128";
     case KDA_ERR_SHAPE:
-        return "KDA_ERR_SHAPE: B, T, H must be positive; with cu_seqlens B must be 1 and num_seqs positive";
+        return "KDA_ERR_SHAPE: B, T, H must be positive and within the size limits (KDA_MAX_HEADS, 32-bit grids); with cu_seqlens B must be 1 and num_seqs positive";
     case KDA_ERR_STATE_DTYPE:
         return "KDA_ERR_STATE_DTYPE: state_dtype must be NONE exactly when no state is given, else BF16 or FP32";
     case KDA_ERR_ARG:
@@ -103,10 +103,23 @@ extern "C" const char *kda_status_string(int status)
     }
 }
 
+/* the size limits of kda.h (KDA_MAX_HEADS, 32-bit grids and offsets) */
+static bool fwd_sizes_ok(int64_t B, int64_t T, int64_t H, int64_t num_seqs)
+{
+    if (H > KDA_MAX_HEADS) return false;
+    if (num_seqs > 0 && T > INT32_MAX) return false;
+    if (B > INT32_MAX || T > ((int64_t)1 << 40)) return false; /* keeps the products below in range */
+    const int64_t N = num_seqs > 0 ? num_seqs : B;
+    if (N > INT32_MAX || 8 * N * H > INT32_MAX) return false;
+    if (num_seqs == 0 && (T + KDA_CHUNK - 1) / KDA_CHUNK > INT32_MAX / B) return false;
+    return kda_max_chunks(B, T, num_seqs) * H <= INT32_MAX;
+}
+
 extern "C" size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t num_seqs)
 {
     if (B <= 0 || T <= 0 || H <= 0 || num_seqs < 0) return 0;
     if (num_seqs > 0 && B != 1) return 0;
+    if (!fwd_sizes_ok(B, T, H, num_seqs)) return 0;
     const int64_t nslots = kda_max_chunks(B, T, num_seqs);
     return kda_chunk_map_bytes(num_seqs, T) + (size_t)nslots * (size_t)H * KDA_REC_BYTES +
            kda_seg_bytes(B, T, H, num_seqs);
@@ -152,6 +165,7 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
     if (K != KDA_DK || V != KDA_DV) return KDA_ERR_HEAD_DIM;
     if (B <= 0 || T <= 0 || H <= 0) return KDA_ERR_SHAPE;
     if (cu_seqlens && (B != 1 || num_seqs <= 0)) return KDA_ERR_SHAPE;
+    if (!fwd_sizes_ok(B, T, H, cu_seqlens ? num_seqs : 0)) return KDA_ERR_SHAPE;
     if (!q || !k || !v || !g || !beta || !out || !A_log || !dt_bias) return KDA_ERR_NULL;
     if (state_dtype == KDA_STATE_NONE) {
         if (initial_state || final_state) return KDA_ERR_STATE_DTYPE;
@@ -220,6 +234,7 @@ extern "C" int kda_decode(const void *q, const void *k, const void *v, const voi
     /* ---- validation (host only, nothing enqueued yet) ---- */
     if (K != KDA_DK || V != KDA_DV) return KDA_ERR_HEAD_DIM;
     if (N <= 0 || H <= 0) return KDA_ERR_SHAPE;
+    if (H > KDA_MAX_HEADS || N > INT32_MAX || N * H > INT32_MAX) return KDA_ERR_SHAPE;
     if (!q || !k || !v || !g || !beta || !out || !A_log || !dt_bias || !state) return KDA_ERR_NULL;
     if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP32) return KDA_ERR_STATE_DTYPE;
     if (!std::isfinite(scale) || !std::isfinite(lower_bound) || lower_bound > 0.f) return KDA_ERR_ARG;

@@ -92,6 +92,14 @@ def test_rejects_shapes(fb):
     cu = fb.addr["cu"]
     assert fb.call(lib, B=2, cu=cu, nseq=2) == 3          # cu_seqlens needs B = 1
     assert fb.call(lib, cu=cu, nseq=0) == 3
+    # size limits: heads, 32-bit grids, int32 token offsets with cu_seqlens
+    assert fb.call(lib, H=kda.KDA_MAX_HEADS + 1) == 3
+    assert fb.call(lib, T=1 << 31, H=64) == 3                # chunk slots x H past INT32_MAX
+    assert fb.call(lib, B=1 << 20, T=64, H=512) == 3          # 8 N H past INT32_MAX
+    assert fb.call(lib, T=1 << 31, cu=cu, nseq=2) == 3        # int32 offsets
+    assert fb.call(lib, B=1 << 40, T=1 << 40) == 3            # no overflow in the checks
+    assert kda.workspace_size(1, 1 << 31, 64) == 0
+    assert kda.workspace_size(1, 100, kda.KDA_MAX_HEADS + 1) == 0
 
 
 def test_rejects_null(fb):
@@ -153,6 +161,8 @@ def test_decode_rejects_bad_arguments():
     assert _decode_call(lib, {"K": 64}) == 2
     assert _decode_call(lib, {"N": 0}) == 3
     assert _decode_call(lib, {"H": -2}) == 3
+    assert _decode_call(lib, {"H": kda.KDA_MAX_HEADS + 1}) == 3
+    assert _decode_call(lib, {"N": 1 << 31}) == 3
     for n in ["q", "k", "v", "g", "beta", "out", "A_log", "dt_bias", "state"]:
         assert _decode_call(lib, {"p_" + n: None}) == 1, n
     assert _decode_call(lib, {"sd": 0}) == 4                 # a state is required
