@@ -168,16 +168,21 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     const float bt = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)r * H * 2, 0, 0));
     const float decay_rate = __expf(A_log[h]);
     const float lb2 = lower_bound * LOG2E_F;
-    u32x2 uqa[8], uka[8], uga[8], uva[8];
+    u32x2 uqa[8], uka[8], uga[8];
+    u32x4 uva[4];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
         const uint32_t o = voff + (uint32_t)(32 * (i >> 1) + 16 * (i & 1) + 4 * g) * 2;
         uqa[i] = __builtin_amdgcn_raw_buffer_load_b64(rq, o, 0, 0);
         uka[i] = __builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, 0);
         uga[i] = __builtin_amdgcn_raw_buffer_load_b64(rg, o, 0, 0);
-        uva[i] = __builtin_amdgcn_raw_buffer_load_b64(rv, o, 0, 0);
+
     }
-    /* All 33 loads are in flight before any of them is consumed. (The activation
+    /* v in natural channel order, 16 bytes per lane: channels 32 kb + 8 g .. + 7 (it is
+       only transposed, and its selectors follow this order) */
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) uva[kb] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + (uint32_t)(32 * kb + 8 * g) * 2, 0, 0);
+    /* All 29 loads are in flight before any of them is consumed. (The activation
        pointers are deliberately not __restrict__: loads through restrict const
        pointers count as invariant, and the compiler then re-issues some of them
        next to their late first use, which costs a second memory round trip.) */
@@ -206,7 +211,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
             }
         }
         /* v stays in bf16: its two 4-channel pieces are operand slots 0..3 and 4..7 */
-        vfr[kb] = __builtin_bit_cast(bf16x8, u32x4{uva[2 * kb][0], uva[2 * kb][1], uva[2 * kb + 1][0], uva[2 * kb + 1][1]});
+        vfr[kb] = __builtin_bit_cast(bf16x8, uva[kb]);
     }
     float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -267,11 +272,14 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     /* ---- phase C: decay-scaled operands (R-form), transposes ---- */
     bf16x8 xdk_f[4], xdq_f[4], yd_f[4], qt_f[4], xok_f[4], xoq_f[4];
     {
-        bf16x8 sel[2];
+        bf16x8 sel[2], selv[2];
 #pragma unroll
         for (int hh = 0; hh < 2; hh++)
 #pragma unroll
-            for (int i = 0; i < 8; i++) sel[hh][i] = (__bf16)(kperm(g, i) == 16 * hh + r16 ? 1.f : 0.f);
+            for (int i = 0; i < 8; i++) {
+                sel[hh][i] = (__bf16)(kperm(g, i) == 16 * hh + r16 ? 1.f : 0.f);
+                selv[hh][i] = (__bf16)(8 * g + i == 16 * hh + r16 ? 1.f : 0.f);
+            }
         const int jb = w >> 1, jh = w & 1;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++) {
@@ -311,7 +319,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
             /* key tiles 2 kb and 2 kb + 1 of R, V and K~ */
             store_transposed(rf, sel, (uint16_t *)&sh.rt[2 * kb][jb][l] + 4 * jh,
                              (uint16_t *)&sh.rt[2 * kb + 1][jb][l] + 4 * jh);
-            store_transposed(vfr[kb], sel, (uint16_t *)&sh.vt[2 * kb][jb][l] + 4 * jh,
+            store_transposed(vfr[kb], selv, (uint16_t *)&sh.vt[2 * kb][jb][l] + 4 * jh,
                              (uint16_t *)&sh.vt[2 * kb + 1][jb][l] + 4 * jh);
             store_transposed(kt, sel,
                              (uint16_t *)(rec + KDA_REC_KT + ((size_t)((2 * kb) * 2 + jb) * 64 + l) * 16 + jh * 8),
