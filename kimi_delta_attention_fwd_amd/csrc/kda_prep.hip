@@ -61,7 +61,9 @@ kda_chunk_map_kernel(const int32_t *__restrict__ cu, int64_t nseq, int32_t *__re
 /* ------------------------------------------------------------------------- */
 /*
  * Wave w owns tokens 16 w .. 16 w + 15 of the chunk (sub-chunk w); lane l holds
- * token 16 w + l % 16 and the 32 key channels 32 kb + kperm(l / 16, i).
+ * token 16 w + l % 16 and the 32 key channels 32 kb + 8 (l / 16) + i, i < 8
+ * (natural order: the loads are 16 bytes per lane; where an operand must be in
+ * the accumulator-pair order kperm, a 0/1 selector MFMA reorders it).
  *
  * Decay factors (log2 units; c = in-sub-chunk inclusive cumsum, m_w = c at the
  * sub-chunk's 8th token, B_w = G before sub-chunk w, Gm_w = B_w + m_w):
@@ -168,49 +170,41 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     const float bt = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)r * H * 2, 0, 0));
     const float decay_rate = __expf(A_log[h]);
     const float lb2 = lower_bound * LOG2E_F;
-    u32x2 uqa[8], uka[8], uga[8];
-    u32x4 uva[4];
+    /* 16 bytes per lane and tensor: operand slot i of key block kb holds channel
+       32 kb + 8 g + i (natural order) */
+    u32x4 uqa[4], uka[4], uga[4], uva[4];
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const uint32_t o = voff + (uint32_t)(32 * (i >> 1) + 16 * (i & 1) + 4 * g) * 2;
-        uqa[i] = __builtin_amdgcn_raw_buffer_load_b64(rq, o, 0, 0);
-        uka[i] = __builtin_amdgcn_raw_buffer_load_b64(rk, o, 0, 0);
-        uga[i] = __builtin_amdgcn_raw_buffer_load_b64(rg, o, 0, 0);
-
+    for (int kb = 0; kb < 4; kb++) {
+        const uint32_t o = voff + (uint32_t)(32 * kb + 8 * g) * 2;
+        uqa[kb] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
+        uka[kb] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
+        uga[kb] = __builtin_amdgcn_raw_buffer_load_b128(rg, o, 0, 0);
+        uva[kb] = __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0);
     }
-    /* v in natural channel order, 16 bytes per lane: channels 32 kb + 8 g .. + 7 (it is
-       only transposed, and its selectors follow this order) */
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++) uva[kb] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff + (uint32_t)(32 * kb + 8 * g) * 2, 0, 0);
-    /* All 29 loads are in flight before any of them is consumed. (The activation
+    /* All 17 loads are in flight before any of them is consumed. (The activation
        pointers are deliberately not __restrict__: loads through restrict const
        pointers count as invariant, and the compiler then re-issues some of them
        next to their late first use, which costs a second memory round trip.) */
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
+        const float *dbp = dt_bias + (size_t)h * KDA_DK + 32 * kb + 8 * g;
+        const float4 db0 = *(const float4 *)dbp, db1 = *(const float4 *)(dbp + 4);
+        const float dbs[8] = {db0.x, db0.y, db0.z, db0.w, db1.x, db1.y, db1.z, db1.w};
 #pragma unroll
-        for (int half = 0; half < 2; half++) {
-            const int ch0 = 32 * kb + 16 * half + 4 * g;
-            const int j0 = kb * 8 + half * 4;
-            const u32x2 uq = uqa[2 * kb + half], uk = uka[2 * kb + half], ug = uga[2 * kb + half];
-            const float4 db = *(const float4 *)(dt_bias + (size_t)h * KDA_DK + ch0);
-            const uint32_t wq[2] = {uq[0], uq[1]}, wk[2] = {uk[0], uk[1]}, wg[2] = {ug[0], ug[1]};
-            const float dbs[4] = {db.x, db.y, db.z, db.w};
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const int sh16 = (e & 1) * 16;
-                qf[j0 + e] = bf2f((uint16_t)(wq[e >> 1] >> sh16));
-                kf[j0 + e] = bf2f((uint16_t)(wk[e >> 1] >> sh16));
-                /* log2 a = max(-exp(A_log) softplus(x) log2(e), lower_bound log2(e)) with
-                   softplus(x) log2(e) = max(t, 0) + log2(1 + 2^{-|t|}),  t = x log2(e) */
-                const float t = (bf2f((uint16_t)(wg[e >> 1] >> sh16)) + dbs[e]) * LOG2E_F;
-                const float sp2 = fmaxf(t, 0.f) + log2_fast(1.f + exp2_fast(-fabsf(t)));
-                const float l2 = fmaxf(-decay_rate * sp2, lb2);
-                la[j0 + e] = valid ? l2 : 0.f; /* padded rows: no decay */
-            }
+        for (int i = 0; i < 8; i++) {
+            const int sh16 = (i & 1) * 16, wi = i >> 1;
+            const int j = kb * 8 + i;
+            qf[j] = bf2f((uint16_t)(uqa[kb][wi] >> sh16));
+            kf[j] = bf2f((uint16_t)(uka[kb][wi] >> sh16));
+            /* log2 a = max(-exp(A_log) softplus(x) log2(e), lower_bound log2(e)) with
+               softplus(x) log2(e) = max(t, 0) + log2(1 + 2^{-|t|}),  t = x log2(e) */
+            const float t = (bf2f((uint16_t)(uga[kb][wi] >> sh16)) + dbs[i]) * LOG2E_F;
+            const float sp2 = fmaxf(t, 0.f) + log2_fast(1.f + exp2_fast(-fabsf(t)));
+            const float l2 = fmaxf(-decay_rate * sp2, lb2);
+            la[j] = valid ? l2 : 0.f; /* padded rows: no decay */
         }
-        /* v stays in bf16: its two 4-channel pieces are operand slots 0..3 and 4..7 */
+        /* v stays in bf16 */
         vfr[kb] = __builtin_bit_cast(bf16x8, uva[kb]);
     }
     float sq = 0.f, sk = 0.f;
@@ -225,8 +219,8 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
         float *dst = (r16 == 15) ? sh.u.p1.tot[w] : sh.u.p1.mid[w];
 #pragma unroll
         for (int kb = 0; kb < 4; kb++) {
-            *(float4 *)&dst[32 * kb + 4 * g] = make_float4(la[8 * kb], la[8 * kb + 1], la[8 * kb + 2], la[8 * kb + 3]);
-            *(float4 *)&dst[32 * kb + 16 + 4 * g] =
+            *(float4 *)&dst[32 * kb + 8 * g] = make_float4(la[8 * kb], la[8 * kb + 1], la[8 * kb + 2], la[8 * kb + 3]);
+            *(float4 *)&dst[32 * kb + 8 * g + 4] =
                 make_float4(la[8 * kb + 4], la[8 * kb + 5], la[8 * kb + 6], la[8 * kb + 7]);
         }
     }
@@ -271,15 +265,12 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
 
     /* ---- phase C: decay-scaled operands (R-form), transposes ---- */
     bf16x8 xdk_f[4], xdq_f[4], yd_f[4], qt_f[4], xok_f[4], xoq_f[4];
+    bf16x8 sel[2]; /* 0/1 selectors: slot i of lane group g is channel 8 g + i of a 32-wide block */
     {
-        bf16x8 sel[2], selv[2];
 #pragma unroll
         for (int hh = 0; hh < 2; hh++)
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                sel[hh][i] = (__bf16)(kperm(g, i) == 16 * hh + r16 ? 1.f : 0.f);
-                selv[hh][i] = (__bf16)(8 * g + i == 16 * hh + r16 ? 1.f : 0.f);
-            }
+            for (int i = 0; i < 8; i++) sel[hh][i] = (__bf16)(8 * g + i == 16 * hh + r16 ? 1.f : 0.f);
         const int jb = w >> 1, jh = w & 1;
 #pragma unroll
         for (int kb = 0; kb < 4; kb++) {
@@ -287,7 +278,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const int j = kb * 8 + i;
-                const int ch = 32 * kb + kperm(g, i);
+                const int ch = 32 * kb + 8 * g + i;
                 if constexpr (WIDE) {
                     const float c = la[j];
                     const float kh = kf[j] * ik, qh = qf[j] * iq;
@@ -319,7 +310,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
             /* key tiles 2 kb and 2 kb + 1 of R, V and K~ */
             store_transposed(rf, sel, (uint16_t *)&sh.rt[2 * kb][jb][l] + 4 * jh,
                              (uint16_t *)&sh.rt[2 * kb + 1][jb][l] + 4 * jh);
-            store_transposed(vfr[kb], selv, (uint16_t *)&sh.vt[2 * kb][jb][l] + 4 * jh,
+            store_transposed(vfr[kb], sel, (uint16_t *)&sh.vt[2 * kb][jb][l] + 4 * jh,
                              (uint16_t *)&sh.vt[2 * kb + 1][jb][l] + 4 * jh);
             store_transposed(kt, sel,
                              (uint16_t *)(rec + KDA_REC_KT + ((size_t)((2 * kb) * 2 + jb) * 64 + l) * 16 + jh * 8),
@@ -381,7 +372,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
                 const bf16x8 yb = sh.u.p1.yd[b][kb][l];
                 bf16x8 ys;
 #pragma unroll
-                for (int i = 0; i < 8; i++) ys[i] = (__bf16)((float)yb[i] * fy[32 * kb + kperm(g, i)]);
+                for (int i = 0; i < 8; i++) ys[i] = (__bf16)((float)yb[i] * fy[32 * kb + 8 * g + i]);
                 ta = mfma(ys, xok_f[kb], ta);
                 tp = mfma(ys, xoq_f[kb], tp);
             }
@@ -548,9 +539,9 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     /* Q' = Q~ - (P TB) R, lane = token, regs = key channel */
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) {
-        f32x4 d0, d1;
-#pragma unroll
-        for (int e = 0; e < 4; e++) { d0[e] = (float)qt_f[kb][e]; d1[e] = (float)qt_f[kb][4 + e]; }
+        /* Q~ into the accumulator layout (rows = channels 32 kb + 16 hh + 4 g + e,
+           column = token) by 0/1 selector MFMAs (exact) */
+        f32x4 d0 = mfma(sel[0], qt_f[kb], zero4()), d1 = mfma(sel[1], qt_f[kb], zero4());
 #pragma unroll
         for (int jb = 0; jb < 2; jb++)
             if (jb < nkb) {
