@@ -89,3 +89,63 @@ def test_mutant_is_caught(name, monkeypatch):
                     failed.append(fn.__name__)
                     break
         assert failed, "mutant %s passed every pin" % name
+
+
+# ---------------------------------------------------------------------------
+# the backward oracle (oracle/backward.py): plant a slip, run the B pins on it
+# ---------------------------------------------------------------------------
+import importlib.util
+
+from tests import test_oracle_backward as bpins
+
+BWD_SRC = os.path.join(os.path.dirname(oracle.__file__), "backward.py")
+
+BWD_MUTANTS = {
+    "dbeta_sign": ("dbeta[bos + t, h] = kn[t] @ dSu", "dbeta[bos + t, h] = -(kn[t] @ dSu)"),
+    "key_grad_no_erase_term": ("dkn[t] = bb[t] * dSu - X @ du", "dkn[t] = bb[t] * dSu"),
+    "output_grad_no_scale": ("dS += scale * np.outer(qn[t], do[t])", "dS += np.outer(qn[t], do[t])"),
+    "query_reads_previous_state": ("dqn[t] = scale * (states[t + 1] @ do[t])",
+                                   "dqn[t] = scale * (states[t] @ do[t])"),
+    "state_grad_no_erase": ("dX = dS - np.outer(kn[t], du)", "dX = dS"),
+    "state_grad_no_decay": ("dS = a[t][:, None] * dX", "dS = dX"),
+    "gate_sigmoid_sign": ("sig = 0.5 * (1.0 + np.tanh(0.5 * x))", "sig = 0.5 * (1.0 - np.tanh(0.5 * x))"),
+    "clamp_passes_gradient": ("dla_free = np.where(clamped, 0.0, dla)", "dla_free = dla"),
+    "A_log_grad_uses_rate": ("dA_log[h] += np.sum(dla_free * la_free)", "dA_log[h] += np.sum(dla_free * rate)"),
+    "norm_grad_no_projection": ("(dxn - xn * np.sum(xn * dxn, axis=-1, keepdims=True)) / n[:, None]",
+                                "dxn / n[:, None]"),
+    "final_grad_ignored": ("dS = np.zeros((K, V)) if dfin is None else dfin[n, h].copy()",
+                           "dS = np.zeros((K, V))"),
+    "decay_grad_uses_new_state": ("dla[t] = a[t] * np.sum(dX * states[t], axis=1)",
+                                  "dla[t] = a[t] * np.sum(dX * states[t + 1], axis=1)"),
+    "value_grad_no_beta": ("du = bb[t] * (dS.T @ kn[t])", "du = dS.T @ kn[t]"),
+}
+
+BWD_PINS = [
+    (bpins.test_b1_finite_differences, [(8, 8, 7, 2, 2)]),
+    (bpins.test_b1_finite_differences_packed, [()]),
+    (bpins.test_b2_one_token_closed_form, [()]),
+    (bpins.test_b3_frozen_state_closed_form, [()]),
+    (bpins.test_b4_clamp_blocks_gate_gradient, [()]),
+]
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name, monkeypatch):
+    old, new = BWD_MUTANTS[name]
+    with open(BWD_SRC) as fh:
+        src = fh.read()
+    assert src.count(old) == 1, "mutation site not unique: %s" % name
+    spec = importlib.util.spec_from_loader("oracle._bwd_mutant", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__package__ = "oracle"
+    exec(compile(src.replace(old, new), BWD_SRC + ":" + name, "exec"), mod.__dict__)
+    monkeypatch.setattr(bpins, "obwd", mod)
+    failed = []
+    for fn, params in BWD_PINS:
+        for p in params:
+            try:
+                fn(*p)
+            except (AssertionError, ValueError, FloatingPointError):
+                failed.append(fn.__name__)
+                break
+    assert failed, "backward mutant %s passed every pin" % name
