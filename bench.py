@@ -44,6 +44,16 @@ KERNEL_SOURCES = {"kda_prep": ("kda_prep.hip", "kda_device.h", "kda_internal.h",
 FLOPS_PER_TH = 6 * 128 * 128 + 2 * 64 * (3 * 128 + 2 * 128)
 
 
+# backward: published fp32 vector peak of MI355X, and algorithmic flops per
+# token-head of the gradient kernel (64-token chunks, K = V = 128):
+# its products per (chunk, head) are 5 of 64x128x128 and 8 of 64x64x128 (or
+# 64x128x64), T^T dT (64^3) and the lower triangle of X1 T^T (64^3 / 2), 2 flops
+# per multiply-add; the two pairwise passes take 17 flops per (i, j <= i, channel)
+PEAK_FP32_TFLOPS = 157.3
+BWD_GRAD_FLOPS_PER_TH = (2 * (5 * 64 * 128 * 128 + 8 * 64 * 64 * 128 + 64 ** 3 + 64 ** 3 // 2)
+                         + 17 * (64 * 65 // 2) * 128) / 64.0
+
+
 def state_bytes(d):
     if d["state_dtype"] is None:
         return 0
@@ -87,6 +97,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
     ap.add_argument("--decode", action="store_true",
                     help="time the single-token decode step instead (512 sequences x 64 heads, fp32 state)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time kda_bwd (gradients) on the workload instead of the forward")
     ap.add_argument("--lower-bound", type=float, default=None,
                     help="override the workload's lower_bound (below -10 selects the wide-range chunk preparation)")
     ap.add_argument("--heads", type=int, default=0,
@@ -109,6 +121,8 @@ def main():
     kda.load_library()
     if args.decode:
         return run_decode(args)
+    if args.backward:
+        return run_backward(args)
     dev = "cuda:0"
     t_gen = time.time()
     d = ki.config_inputs(args.config)
@@ -324,6 +338,104 @@ def run_decode(args):
         torch.cuda.synchronize()
         res["parity_sample"] = {"rel_l2": oracle.rel_l2(out.float().cpu().numpy(), ro[0]),
                                 "state_rel_l2": oracle.rel_l2(state.cpu().numpy(), rf)}
+    print(json.dumps(res), flush=True)
+
+
+def run_backward(args):
+    """One kda_bwd call per step on a workload of the forward (default: the long
+    prefill), with a seeded bf16 output gradient and an fp32 final-state gradient
+    where the workload returns a final state."""
+    import numpy as np
+    import torch
+
+    import kda_inputs as ki
+    import kimi_delta_attention_fwd_amd as kda
+
+    dev = "cuda:0"
+    d = ki.config_inputs(args.config)
+    if 0 < args.heads < d["H"]:
+        nh = args.heads
+        for key in ("q", "k", "v", "g", "beta"):
+            d[key] = np.ascontiguousarray(d[key][:, :, :nh])
+        for key in ("A_log", "dt_bias"):
+            d[key] = np.ascontiguousarray(d[key][:nh])
+        if d["initial_state"] is not None:
+            d["initial_state"] = np.ascontiguousarray(d["initial_state"][:, :nh])
+        d["H"] = nh
+        d["name"] = "%s_h%d" % (d["name"], nh)
+    B, T, H, N = d["B"], d["T"], d["H"], d["N"]
+    rng = np.random.default_rng(1234)
+    dout_np = ki.f32_to_bf16_bits(rng.standard_normal((B, T, H, 128), dtype=np.float32))
+    dfin_np = (rng.standard_normal((N, H, 128, 128), dtype=np.float32) * np.float32(0.1)) if d["final"] else None
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v, g, beta, dout = bf(d["q"]), bf(d["k"]), bf(d["v"]), bf(d["g"]), bf(d["beta"]), bf(dout_np)
+    A_log = torch.from_numpy(d["A_log"]).to(dev)
+    dt_bias = torch.from_numpy(d["dt_bias"]).to(dev)
+    init = None
+    if d["initial_state"] is not None:
+        init = torch.from_numpy(d["initial_state"]).to(dev) if d["state_dtype"] == "fp32" else bf(d["initial_state"])
+    dfin = None if dfin_np is None else torch.from_numpy(dfin_np).to(dev)
+    cu = None if d["cu_seqlens"] is None else torch.from_numpy(d["cu_seqlens"]).to(dev)
+    nseq = 0 if cu is None else N
+    ws = torch.empty(kda.bwd_workspace_size(B, T, H, nseq), dtype=torch.uint8, device=dev)
+    f32 = torch.float32
+    grads = dict(dq=torch.empty((B, T, H, 128), dtype=f32, device=dev),
+                 dk=torch.empty((B, T, H, 128), dtype=f32, device=dev),
+                 dv=torch.empty((B, T, H, 128), dtype=f32, device=dev),
+                 dg=torch.empty((B, T, H, 128), dtype=f32, device=dev),
+                 dbeta=torch.empty((B, T, H), dtype=f32, device=dev),
+                 dA_log=torch.empty((H,), dtype=f32, device=dev),
+                 ddt_bias=torch.empty((H, 128), dtype=f32, device=dev),
+                 dinitial_state=torch.empty((N, H, 128, 128), dtype=f32, device=dev))
+
+    def step():
+        kda.bwd(q, k, v, g, beta, d["scale"], dout, A_log, dt_bias, d["lower_bound"], initial_state=init,
+                dfinal_state=dfin, cu_seqlens=cu, grads=grads, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kda.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kda.profile_enable(False)
+    prof = kda.profile_read()
+    kern = {name: ms / n for name, (ms, n) in prof.items()}
+    units = ki.token_heads(d)
+    grad_ms = kern["kda_bwd_grad"]
+    achieved = units * BWD_GRAD_FLOPS_PER_TH / (grad_ms * 1e-3) / 1e12
+    res = {
+        "metric": "KDA bwd tokens*heads/s (gradients of q, k, v, g, beta, A_log, dt_bias, initial state)",
+        "value": units * args.steps / wall, "unit": "token*heads/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded numpy draws)",
+        "config": {"workload": "%s backward: B=%d T=%d H=%d, bf16 inputs, fp32 gradients" % (d["name"], B, T, H),
+                   "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU"},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None, "kernel": "kda_bwd_grad",
+                     "kernel_ms": grad_ms, "alg_flops_per_launch": units * BWD_GRAD_FLOPS_PER_TH},
+        "kernels_ms": kern,
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import backward as obwd
+        ts = min(T, 256)
+        sub = lambda a: None if a is None else np.ascontiguousarray(a[:, :ts])
+        tc, reps = 0.0, 0
+        with threadpool_limits(1):
+            while reps == 0 or tc < args.cpu_min_seconds:
+                tc0 = time.perf_counter()
+                obwd.bwd(sub(d["q"][:1]), sub(d["k"][:1]), sub(d["v"][:1]), sub(d["g"][:1]), sub(d["beta"][:1]),
+                         d["scale"], d["A_log"], d["dt_bias"], d["lower_bound"], sub(dout_np[:1]))
+                tc += time.perf_counter() - tc0
+                reps += 1
+        res["cpu_baseline"] = {"value": reps * ts * H / tc, "unit": "token*heads/s", "cores": 1, "kind": "oracle",
+                               "sample": "fp64 per-token reverse pass on the first %d tokens of sequence 0, all %d "
+                               "heads, %d passes in %.1f s" % (ts, H, reps, tc)}
     print(json.dumps(res), flush=True)
 
 

@@ -158,6 +158,46 @@ KDA_API int kda_decode(const void *q, const void *k, const void *v, const void *
                const float *dt_bias, float lower_bound, void *state, int state_dtype,
                int64_t N, int64_t H, int64_t K, int64_t V, void *stream);
 
+/*
+ * kda_bwd -- gradients of the forward above (the pages show only the forward;
+ * this is its derivative, for training). For
+ *   L = sum(dout * out) + sum(dfinal_state * final_state)
+ * with out and final_state the results of kda_fwd on the same inputs, it
+ * writes dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta, dL/dA_log, dL/ddt_bias and
+ * dL/dinitial_state. lower_bound clamps: an element whose unclamped
+ * -exp(A_log) softplus(g + dt_bias) lies below lower_bound passes no gradient
+ * to g, dt_bias or A_log. Arithmetic is fp32 throughout.
+ *
+ *  q, k, v, g, beta, scale, A_log, dt_bias, lower_bound, cu_seqlens, num_seqs,
+ *  B, T, H, K, V : as for kda_fwd (any finite lower_bound <= 0).
+ *  dout          : bf16 [B, T, H, 128], the gradient of out.
+ *  initial_state : NULL (zero state) or [N, H, 128, 128] of state_dtype
+ *                  (KDA_STATE_NONE iff NULL).
+ *  dfinal_state  : NULL (zero) or fp32 [N, H, 128, 128], the gradient of the
+ *                  final state.
+ *  dq, dk, dv, dg: fp32 [B, T, H, 128];  dbeta : fp32 [B, T, H];
+ *  dA_log        : fp32 [H];  ddt_bias : fp32 [H, 128] (sums over all tokens).
+ *  dinitial_state: NULL (not returned) or fp32 [N, H, 128, 128].
+ *  All outputs are written in full and may not overlap an input, each other or
+ *  the workspace. The per-head sums are taken in a fixed order (deterministic).
+ *  workspace     : at least kda_bwd_workspace_size(...) bytes, 256-byte
+ *                  aligned (per chunk and head: 258 KiB of chunk quantities and
+ *                  the fp32 state and state gradient at the chunk's ends).
+ * Errors as for kda_fwd.
+ */
+KDA_API int kda_bwd(const void *q, const void *k, const void *v, const void *g,
+            const void *beta, float scale, const void *dout, const float *A_log,
+            const float *dt_bias, float lower_bound, const void *initial_state,
+            int state_dtype, const float *dfinal_state, const int32_t *cu_seqlens,
+            int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+            float *dq, float *dk, float *dv, float *dg, float *dbeta, float *dA_log,
+            float *ddt_bias, float *dinitial_state, void *workspace,
+            size_t workspace_bytes, void *stream);
+
+/* kda_bwd_workspace_size -- bytes of workspace kda_bwd needs (host only); sizes
+ * as for kda_fwd_workspace_size, 0 for invalid sizes. */
+KDA_API size_t kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t num_seqs);
+
 /* Static, NUL-terminated description of a kda_status code (host only). */
 KDA_API const char *kda_status_string(int status);
 

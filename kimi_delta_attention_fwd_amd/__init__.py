@@ -16,7 +16,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "decode", "workspace_size", "status_string", "library_path", "load_library",
+__all__ = ["fwd", "decode", "bwd", "workspace_size", "bwd_workspace_size", "status_string", "library_path", "load_library",
            "profile_enable", "profile_read", "KDA_LOWER_BOUND_NARROW", "KDA_MAX_HEADS", "KdaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +27,7 @@ KDA_STATE_NONE, KDA_STATE_BF16, KDA_STATE_FP32 = 0, 1, 2
 KDA_LOWER_BOUND_NARROW = -10.0  # below it kda_fwd takes its wide-range chunk preparation
 KDA_MAX_HEADS = 65536  # H limit of kda_fwd and kda_decode (KDA_ERR_SHAPE above it)
 EXPORTED = ("kda_fwd", "kda_decode", "kda_fwd_workspace_size", "kda_status_string",
-            "kda_profile_enable", "kda_profile_read")
+            "kda_profile_enable", "kda_profile_read", "kda_bwd", "kda_bwd_workspace_size")
 
 
 class KdaError(RuntimeError):
@@ -54,6 +54,11 @@ def load_library():
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_float, P, ctypes.c_int,
                                I64, I64, I64, I64, P]
+    lib.kda_bwd.restype = ctypes.c_int
+    lib.kda_bwd.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_float, P, ctypes.c_int, P,
+                            P, I64, I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.kda_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.kda_bwd_workspace_size.argtypes = [I64, I64, I64, I64]
     lib.kda_fwd_workspace_size.restype = ctypes.c_size_t
     lib.kda_fwd_workspace_size.argtypes = [I64, I64, I64, I64]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -74,6 +79,11 @@ def status_string(code: int) -> str:
 def workspace_size(B: int, T: int, H: int, num_seqs: int = 0) -> int:
     """Bytes of device workspace ``fwd`` needs (num_seqs = 0: no cu_seqlens)."""
     return int(load_library().kda_fwd_workspace_size(int(B), int(T), int(H), int(num_seqs)))
+
+
+def bwd_workspace_size(B: int, T: int, H: int, num_seqs: int = 0) -> int:
+    """Bytes of device workspace ``bwd`` needs (num_seqs = 0: no cu_seqlens)."""
+    return int(load_library().kda_bwd_workspace_size(int(B), int(T), int(H), int(num_seqs)))
 
 
 def profile_enable(on: bool = True) -> None:
@@ -248,6 +258,97 @@ def decode(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, state):
                         ctypes.c_void_p(stream))
     if rc == 0:
         return out
+    msg = lib.kda_status_string(rc).decode()
+    if rc == 8:
+        raise KdaError(msg)
+    raise ValueError(msg)
+
+
+def bwd(q, k, v, g, beta, scale, dout, A_log, dt_bias, lower_bound, initial_state=None,
+        dfinal_state=None, cu_seqlens=None, grads=None, workspace=None):
+    """Gradients of sum(dout * out) + sum(dfinal_state * final_state) for the forward.
+
+    Inputs as for ``fwd``; dout: bf16 [B, T, H, 128]; dfinal_state: None or fp32
+    [N, H, 128, 128]. Returns a dict of fp32 tensors dq, dk, dv, dg [B, T, H, 128],
+    dbeta [B, T, H], dA_log [H], ddt_bias [H, 128] and dinitial_state
+    [N, H, 128, 128]. ``grads`` (optional) is a dict of preallocated outputs with
+    those names. Raises ValueError for invalid arguments and KdaError for HIP
+    failures.
+    """
+    import torch
+    lib = load_library()
+    bf16 = torch.bfloat16
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("dout", dout)):
+        if t.dtype != bf16:
+            raise ValueError("%s must be bfloat16 (got %s)" % (name, t.dtype))
+    for name, t in (("A_log", A_log), ("dt_bias", dt_bias)):
+        if t.dtype != torch.float32:
+            raise ValueError("%s must be float32 (got %s)" % (name, t.dtype))
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, K]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    for name, t in (("k", k), ("g", g)):
+        if tuple(t.shape) != (B, T, H, K):
+            raise ValueError("%s must have the shape of q" % name)
+    if tuple(v.shape) != (B, T, H, V) or tuple(dout.shape) != (B, T, H, V):
+        raise ValueError("v and dout must be [B, T, H, V]")
+    if tuple(beta.shape) != (B, T, H):
+        raise ValueError("beta must be [B, T, H]")
+    if A_log.numel() != H or dt_bias.numel() != H * K:
+        raise ValueError("A_log must have H elements and dt_bias H*K")
+    num_seqs = 0
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise ValueError("cu_seqlens must be int32")
+        num_seqs = cu_seqlens.numel() - 1
+        if num_seqs <= 0:
+            raise ValueError("cu_seqlens must have at least 2 entries")
+    N = num_seqs if cu_seqlens is not None else B
+    sd = KDA_STATE_NONE
+    if initial_state is not None:
+        if initial_state.dtype == torch.float32:
+            sd = KDA_STATE_FP32
+        elif initial_state.dtype == bf16:
+            sd = KDA_STATE_BF16
+        else:
+            raise ValueError("initial_state must be bfloat16 or float32")
+        if tuple(initial_state.shape) != (N, H, K, V):
+            raise ValueError("initial_state must be [N, H, K, V] = %s" % ((N, H, K, V),))
+    if dfinal_state is not None:
+        if dfinal_state.dtype != torch.float32 or tuple(dfinal_state.shape) != (N, H, K, V):
+            raise ValueError("dfinal_state must be float32 [N, H, K, V] = %s" % ((N, H, K, V),))
+    dev = q.device
+    f32 = torch.float32
+    shapes = dict(dq=(B, T, H, K), dk=(B, T, H, K), dv=(B, T, H, V), dg=(B, T, H, K), dbeta=(B, T, H),
+                  dA_log=(H,), ddt_bias=(H, K), dinitial_state=(N, H, K, V))
+    if grads is None:
+        grads = {n: torch.empty(shp, dtype=f32, device=dev) for n, shp in shapes.items()}
+    else:
+        for n, shp in shapes.items():
+            t = grads.get(n)
+            if t is None or t.dtype != f32 or tuple(t.shape) != shp:
+                raise ValueError("grads[%r] must be float32 %s" % (n, shp))
+    tensors = [q, k, v, g, beta, dout, A_log, dt_bias, initial_state, dfinal_state, cu_seqlens, workspace,
+               *grads.values()]
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    need = lib.kda_bwd_workspace_size(B, T, H, num_seqs)
+    ws = _workspace(need, dev) if workspace is None else workspace
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(dout),
+                     _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state), sd,
+                     _ptr(dfinal_state), _ptr(cu_seqlens), num_seqs, B, T, H, K, V,
+                     _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dg"]),
+                     _ptr(grads["dbeta"]), _ptr(grads["dA_log"]), _ptr(grads["ddt_bias"]),
+                     _ptr(grads["dinitial_state"]), _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
+    if rc == 0:
+        return grads
     msg = lib.kda_status_string(rc).decode()
     if rc == 8:
         raise KdaError(msg)

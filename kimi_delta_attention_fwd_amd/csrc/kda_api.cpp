@@ -29,6 +29,14 @@ extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, co
                                       int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
                                       const void *init_state, void *final_state, int state_fp32, int64_t segc,
                                       void *seg_area, hipStream_t st);
+extern "C" hipError_t kda_launch_bwd(int stage, const void *q, const void *k, const void *v, const void *g,
+                                     const void *beta, const void *dout, const float *A_log,
+                                     const float *dt_bias, float scale, float lower_bound,
+                                     const void *init, int init_fp32, const float *dfinal,
+                                     const int32_t *cu, const int32_t *chunk_off, int64_t nseq, int64_t T,
+                                     int64_t H, int64_t nslots, unsigned char *area, float *dq, float *dk,
+                                     float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias,
+                                     float *dinit, hipStream_t st);
 extern "C" hipError_t kda_launch_decode(const void *q, const void *k, const void *v, const void *g,
                                         const void *beta, const float *A_log, const float *dt_bias, float scale,
                                         float lower_bound, void *state, int state_fp32, void *out, int64_t N,
@@ -252,5 +260,84 @@ extern "C" int kda_decode(const void *q, const void *k, const void *v, const voi
     if (kda_launch_decode(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound, state,
                           state_dtype == KDA_STATE_FP32 ? 1 : 0, out, N, H, st) != hipSuccess)
         return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+/* ---- backward ---- */
+extern "C" size_t kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t num_seqs)
+{
+    if (B <= 0 || T <= 0 || H <= 0 || num_seqs < 0) return 0;
+    if (num_seqs > 0 && B != 1) return 0;
+    if (!fwd_sizes_ok(B, T, H, num_seqs)) return 0;
+    const int64_t items = kda_max_chunks(B, T, num_seqs) * H;
+    return kda_chunk_map_bytes(num_seqs, T) + (size_t)items * KDA_BR_FLOATS * 4 +
+           2 * (size_t)items * KDA_DK * KDA_DV * 4 + kda_bwd_part_bytes(items) +
+           kda_bwd_grad_wgs(items) * (size_t)KDA_BWD_SCR_FLOATS * 4;
+}
+
+extern "C" int kda_bwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                       float scale, const void *dout, const float *A_log, const float *dt_bias,
+                       float lower_bound, const void *initial_state, int state_dtype,
+                       const float *dfinal_state, const int32_t *cu_seqlens, int64_t num_seqs, int64_t B,
+                       int64_t T, int64_t H, int64_t K, int64_t V, float *dq, float *dk, float *dv, float *dg,
+                       float *dbeta, float *dA_log, float *ddt_bias, float *dinitial_state, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    if (K != KDA_DK || V != KDA_DV) return KDA_ERR_HEAD_DIM;
+    if (B <= 0 || T <= 0 || H <= 0) return KDA_ERR_SHAPE;
+    if (cu_seqlens && (B != 1 || num_seqs <= 0)) return KDA_ERR_SHAPE;
+    if (!fwd_sizes_ok(B, T, H, cu_seqlens ? num_seqs : 0)) return KDA_ERR_SHAPE;
+    if (!q || !k || !v || !g || !beta || !dout || !A_log || !dt_bias) return KDA_ERR_NULL;
+    if (!dq || !dk || !dv || !dg || !dbeta || !dA_log || !ddt_bias) return KDA_ERR_NULL;
+    if (state_dtype == KDA_STATE_NONE) {
+        if (initial_state) return KDA_ERR_STATE_DTYPE;
+    } else if (state_dtype == KDA_STATE_BF16 || state_dtype == KDA_STATE_FP32) {
+        if (!initial_state) return KDA_ERR_STATE_DTYPE;
+    } else {
+        return KDA_ERR_STATE_DTYPE;
+    }
+    if (!std::isfinite(scale) || !std::isfinite(lower_bound) || lower_bound > 0.f) return KDA_ERR_ARG;
+    const int64_t nseq_arg = cu_seqlens ? num_seqs : 0;
+    const size_t need = kda_bwd_workspace_size(B, T, H, nseq_arg);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return KDA_ERR_WORKSPACE;
+
+    const int64_t N = cu_seqlens ? num_seqs : B;
+    const size_t act = (size_t)B * T * H * KDA_DK * 2, g32 = 2 * act, fstate = (size_t)N * H * KDA_DK * KDA_DV * 4;
+    const size_t sbytes = (size_t)N * H * KDA_DK * KDA_DV * (state_dtype == KDA_STATE_FP32 ? 4 : 2);
+    const Range inputs[] = {rng(q, act), rng(k, act), rng(v, act), rng(g, act), rng(beta, (size_t)B * T * H * 2),
+                            rng(dout, act), rng(A_log, (size_t)H * 4), rng(dt_bias, (size_t)H * KDA_DK * 4),
+                            rng(cu_seqlens, cu_seqlens ? (size_t)(num_seqs + 1) * 4 : 0),
+                            rng(initial_state, initial_state ? sbytes : 0),
+                            rng(dfinal_state, dfinal_state ? fstate : 0)};
+    const Range outputs[] = {rng(dq, g32), rng(dk, g32), rng(dv, g32), rng(dg, g32),
+                             rng(dbeta, (size_t)B * T * H * 4), rng(dA_log, (size_t)H * 4),
+                             rng(ddt_bias, (size_t)H * KDA_DK * 4),
+                             rng(dinitial_state, dinitial_state ? fstate : 0), rng(workspace, need)};
+    for (const Range &o : outputs) {
+        for (const Range &in : inputs)
+            if (overlap(o, in)) return KDA_ERR_ALIAS;
+        for (const Range &o2 : outputs)
+            if (&o2 != &o && overlap(o, o2)) return KDA_ERR_ALIAS;
+    }
+
+    hipStream_t st = (hipStream_t)stream;
+    unsigned char *ws = (unsigned char *)workspace;
+    int32_t *chunk_off = nullptr;
+    if (cu_seqlens) {
+        chunk_off = (int32_t *)ws;
+        ProfScope ps("kda_chunk_map", st);
+        if (kda_launch_chunk_map(cu_seqlens, num_seqs, T, chunk_off, st) != hipSuccess) return KDA_ERR_HIP;
+    }
+    unsigned char *area = ws + kda_chunk_map_bytes(nseq_arg, T);
+    const int64_t nslots = kda_max_chunks(B, T, nseq_arg);
+    static const char *names[4] = {"kda_bwd_chunk", "kda_bwd_scan", "kda_bwd_grad", "kda_bwd_reduce"};
+    for (int stage = 0; stage < 4; stage++) {
+        ProfScope ps(names[stage], st);
+        if (kda_launch_bwd(stage, q, k, v, g, beta, dout, A_log, dt_bias, scale, lower_bound, initial_state,
+                           state_dtype == KDA_STATE_FP32 ? 1 : 0, dfinal_state, cu_seqlens, chunk_off, N, T, H,
+                           nslots, area, dq, dk, dv, dg, dbeta, dA_log, ddt_bias, dinitial_state,
+                           st) != hipSuccess)
+            return KDA_ERR_HIP;
+    }
     return KDA_OK;
 }

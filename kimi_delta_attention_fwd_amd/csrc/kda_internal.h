@@ -108,4 +108,44 @@ static inline size_t kda_seg_bytes(int64_t B, int64_t T, int64_t H, int64_t num_
     return (size_t)nchain * (size_t)(3 * G - 2) * KDA_DK * KDA_DV * 4;
 }
 
+/* ---- backward (kda_bwd) ----
+ * Per (chunk, head) fp32 area written by the chunk kernel, offsets in floats,
+ * rows are the chunk's 64 token positions (rows past the chunk's end are 0):
+ *   W, U, Q' (scale included), K~ = k^ o e^{G_L - G}, q^, k^, G   [64][128] each,
+ *   T = (I + A)^-1 and P (scale included, j <= i)                  [64][64] each,
+ *   e^{G_L} [128], beta [64], |q| and |k| norms sqrt(|x|^2 + 1e-6) [64] each.
+ * Areas are head-major like the forward records: (h * nslots + slot). */
+#define KDA_BR_W 0
+#define KDA_BR_U 8192
+#define KDA_BR_QP 16384
+#define KDA_BR_KT 24576
+#define KDA_BR_QN 32768
+#define KDA_BR_KN 40960
+#define KDA_BR_G 49152
+#define KDA_BR_T 57344
+#define KDA_BR_P 61440
+#define KDA_BR_GL 65536
+#define KDA_BR_BETA 65664
+#define KDA_BR_NQ 65728
+#define KDA_BR_NK 65792
+#define KDA_BR_FLOATS 66048
+/* per (chunk, head) gate partials: d dt_bias [128], then d A_log */
+#define KDA_BWD_PART_FLOATS 132
+/* scratch of one gradient workgroup: 14 [64][128] and 3 [64][64] fp32 matrices */
+#define KDA_BWD_SCR_FLOATS (14 * 8192 + 3 * 4096)
+/* at most this many gradient workgroups (each loops over (chunk, head) items) */
+#define KDA_BWD_GRAD_WGS 1024
+
+/* backward workspace = [chunk table][chunk areas][S at each chunk start]
+ * [dS at each chunk end][gate partials][gradient scratch]; every part is a
+ * multiple of 256 bytes */
+static inline size_t kda_bwd_grad_wgs(int64_t items)
+{
+    return (size_t)(items < KDA_BWD_GRAD_WGS ? items : KDA_BWD_GRAD_WGS);
+}
+static inline size_t kda_bwd_part_bytes(int64_t items)
+{
+    return ((size_t)items * KDA_BWD_PART_FLOATS * 4 + 255) / 256 * 256;
+}
+
 #endif
