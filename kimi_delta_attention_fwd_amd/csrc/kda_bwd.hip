@@ -6,13 +6,14 @@
  * The FlashKDA pages show only the forward ("Core Kernel API / flash_kda.fwd",
  * ccm-staging page); these are the derivatives of the forward recurrence
  * described in kda.h, taken through its chunked form (kda_internal.h). All
- * arithmetic is fp32 on the vector ALUs:
+ * arithmetic is fp32: the matrix products of the scan and of the gradient
+ * kernel on fp32 MFMA (v_mfma_f32_16x16x4f32), the rest on the vector ALUs:
  *
  *   kda_bwd_chunk_kernel  one workgroup per (chunk, head): q^, k^, log a, G, A, P,
  *                         T = (I + A)^-1 (forward substitution), W, U, Q', K~,
  *                         e^{G_L}, stored as fp32 per-chunk areas.
- *   kda_bwd_scan_kernel   one workgroup per (sequence, head, 16 value columns);
- *                         value columns are independent in both directions:
+ *   kda_bwd_scan_kernel   one workgroup per (sequence, head, 16 value columns),
+ *                         fp32 MFMA; value columns are independent in both directions:
  *                         forward  S <- diag(e^{G_L}) S + K~^T (U - W S), storing S
  *                                  at every chunk start;
  *                         reverse  dS <- diag(e^{G_L}) dS - W^T (K~ dS) + Q'^T dout,
@@ -64,24 +65,83 @@ __device__ __forceinline__ void bwd_seq(int64_t seq, const int32_t *cu, const in
     }
 }
 
-/* C[i][j] = (acc ? C[i][j] : 0) + alpha * sum_k a(i, k) b(k, j) for i < M, j < N,
- * with a(i, k) = TA ? A[k][i] : A[i][k] and b(k, j) = TB ? B[j][k] : B[k][j]
- * (row strides lda, ldb, ldc). N is a power of two. Callers separate products
- * that share an output or read one another's output with a barrier. */
-template <bool TA, bool TB>
-__device__ __forceinline__ void wg_gemm(float *C, int ldc, const float *A, int lda, const float *B, int ldb,
-                                        int M, int N, int Kd, float alpha, bool acc)
+__device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4 &c)
 {
-    for (int e = threadIdx.x; e < M * N; e += NT) {
-        const int i = e / N, j = e - i * N;
-        float s = 0.f;
-        for (int kk = 0; kk < Kd; kk++) {
-            const float a = TA ? A[kk * lda + i] : A[i * lda + kk];
-            const float b = TB ? B[j * ldb + kk] : B[kk * ldb + j];
-            s = fmaf(a, b, s);
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+/* x[s] = p[s * STRIDE] for s < 16; p is 16-byte aligned when STRIDE is 1 */
+template <int STRIDE>
+__device__ __forceinline__ void load16(float *x, const float *p)
+{
+    if (STRIDE == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float4 f = *(const float4 *)(p + 4 * i);
+            x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
         }
-        C[i * ldc + j] = acc ? C[i * ldc + j] + alpha * s : alpha * s;
+    } else {
+#pragma unroll
+        for (int s = 0; s < 16; s++) x[s] = p[s * STRIDE];
     }
+}
+
+/* C[i][j] = (acc ? C[i][j] : 0) + alpha * sum_k a(i, k) b(k, j) for i < 64, j < N,
+ * with a(i, k) = TA ? A[k][i] : A[i][k] and b(k, j) = TB ? B[j][k] : B[k][j], on fp32 MFMA (16 x 16 x 4 blocks). Wave w holds
+ * row blocks 2 (w % 2) + {0, 1} and N / 32 column blocks starting at
+ * (w / 2) N / 32; in each 64-wide slice of the contraction, lane group gq
+ * (lanes 16 gq .. 16 gq + 15) takes contraction indices 16 gq .. 16 gq + 15, so
+ * operands contiguous along it load as 16-byte pieces. Every row stride and
+ * base is a multiple of 4 floats. Callers separate products that share an
+ * output or read one another's output with a barrier. */
+template <bool TA, bool TB, int N, int KD>
+__device__ __forceinline__ void wg_gemm(float *C, const float *A, const float *B, float alpha, bool acc)
+{
+    static_assert(N % 32 == 0 && KD % 64 == 0, "block shape");
+    /* dense row-major operands: A is [64][KD] ([KD][64] if TA), B is [KD][N] ([N][KD] if TB), C is [64][N] */
+    constexpr int lda = TA ? 64 : KD, ldb = TB ? KD : N, ldc = N;
+    constexpr int NBW = N / 32;
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6, gq = l >> 4, r16 = l & 15;
+    const int rb0 = 2 * (w & 1), cb0 = (w >> 1) * NBW;
+    __builtin_amdgcn_sched_barrier(0); /* products are not interleaved: each holds 128 registers */
+    f32x4 d[2][NBW];
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+        for (int cb = 0; cb < NBW; cb++) d[rb][cb] = zero4();
+#pragma unroll 1
+    for (int kc = 0; kc < KD; kc += 64) {
+        const int kb = kc + 16 * gq;
+        float a[2][16], b[NBW][16];
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            const int i = 16 * (rb0 + rb) + r16;
+            if (TA) load16<lda>(a[rb], A + kb * lda + i);
+            else load16<1>(a[rb], A + i * lda + kb);
+        }
+#pragma unroll
+        for (int cb = 0; cb < NBW; cb++) {
+            const int j = 16 * (cb0 + cb) + r16;
+            if (TB) load16<1>(b[cb], B + j * ldb + kb);
+            else load16<ldb>(b[cb], B + kb * ldb + j);
+        }
+#pragma unroll
+        for (int s = 0; s < 16; s++)
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+                for (int cb = 0; cb < NBW; cb++) d[rb][cb] = mfma4(a[rb][s], b[cb][s], d[rb][cb]);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+        for (int cb = 0; cb < NBW; cb++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                float *c = C + (16 * (rb0 + rb) + 4 * gq + e) * ldc + 16 * (cb0 + cb) + r16;
+                *c = acc ? *c + alpha * d[rb][cb][e] : alpha * d[rb][cb][e];
+            }
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 } // namespace
@@ -263,10 +323,19 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
 }
 
 /* ------------------------------------------------------------------------- */
-/* state checkpoints and state gradients: one workgroup per (sequence, head,  */
-/* 16 value columns), grid N * H * 8. Thread t owns column 16 tile + t % 16   */
-/* and key rows t / 16 + 16 m (m < 8) of S and dS.                            */
+/* state checkpoints and state gradients: one workgroup of 4 waves per        */
+/* (sequence, head, 16 value columns), grid N * H * 8, on fp32 MFMA. Lane      */
+/* (r16, gq) of wave w holds rows 16 (2 w + rb) + 4 gq + e (rb < 2, e < 4),    */
+/* column 16 tile + r16 of S and dS (the 16 x 16 accumulator layout). Record   */
+/* rows past a chunk's last token are zero, so every product runs over all 64. */
 /* ------------------------------------------------------------------------- */
+
+/* LDS slot of row r, column j of the 128 x 16 state tile and of the 64 x 16
+ * chunk tile: the four lane groups read rows 32 (resp. 16) apart, which the
+ * row offsets spread over the banks */
+__host__ __device__ constexpr int s_lds(int r, int j) { return r * 16 + (r >> 5) * 8 + j; }
+__host__ __device__ constexpr int d_lds(int i, int j) { return i * 16 + (i >> 4) * 8 + j; }
+
 extern "C" __global__ void __launch_bounds__(NT)
 kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ cu,
                     const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
@@ -274,7 +343,7 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
                     const uint16_t *__restrict__ dout, float *__restrict__ ckpt, float *__restrict__ dse,
                     float *__restrict__ dinit)
 {
-    __shared__ float sS[KDA_DK * 16], sD[KDA_CHUNK * 16], sO[KDA_CHUNK * 16];
+    __shared__ float sS[s_lds(127, 15) + 1], sD[d_lds(63, 15) + 1];
     const int tile = blockIdx.x & 7;
     const int64_t chain = blockIdx.x >> 3;
     const int64_t seq = chain / H;
@@ -282,90 +351,141 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
     if (seq >= nseq) return;
     int64_t nchunk, slot0, row0, len;
     bwd_seq(seq, cu, chunk_off, T, nchunk, slot0, row0, len);
-    const int t = threadIdx.x, j = t & 15, rb = t >> 4, col = tile * 16 + j;
+    const int t = threadIdx.x, w = t >> 6, l = t & 63, gq = l >> 4, r16 = l & 15, col = tile * 16 + r16;
     const int64_t sbase = (seq * H + h) * (int64_t)(KDA_DK * KDA_DV);
 
-    float S[8];
+    f32x4 S[2];
 #pragma unroll
-    for (int m = 0; m < 8; m++) {
-        const int64_t o = sbase + (int64_t)(rb + 16 * m) * KDA_DV + col;
-        S[m] = init == nullptr ? 0.f
-             : init_fp32 ? ((const float *)init)[o] : bf2f(((const uint16_t *)init)[o]);
-    }
+    for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int64_t o = sbase + (int64_t)(16 * (2 * w + rb) + 4 * gq + e) * KDA_DV + col;
+            S[rb][e] = init == nullptr ? 0.f
+                     : init_fp32 ? ((const float *)init)[o] : bf2f(((const uint16_t *)init)[o]);
+        }
+
+    /* forward: S_c is stored, D = U - W S_c, S_{c+1} = diag(e^{G_L}) S_c + K~^T D */
     for (int64_t c = 0; c < nchunk; c++) {
         const int64_t item = (int64_t)h * nslots + slot0 + c;
         const float *R = brec + item * KDA_BR_FLOATS;
         float *ck = ckpt + item * (int64_t)(KDA_DK * KDA_DV);
+        float4 wv[8];  /* W row 16 w + r16, columns 32 gq .. 32 gq + 31 */
+        float kt[2][16]; /* K~[16 gq + s][16 (2 w + rb) + r16] */
+        f32x4 dacc, gl[2];
+        const float *wrow = R + KDA_BR_W + (16 * w + r16) * KDA_DK + 32 * gq;
 #pragma unroll
-        for (int m = 0; m < 8; m++) {
-            const int r = rb + 16 * m;
-            ck[r * KDA_DV + col] = S[m];
-            sS[r * 16 + j] = S[m];
-        }
+        for (int i = 0; i < 8; i++) wv[i] = *(const float4 *)(wrow + 4 * i);
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int s = 0; s < 16; s++) kt[rb][s] = R[KDA_BR_KT + (16 * gq + s) * KDA_DK + 16 * (2 * w + rb) + r16];
+#pragma unroll
+        for (int e = 0; e < 4; e++) dacc[e] = R[KDA_BR_U + (16 * w + 4 * gq + e) * KDA_DV + col];
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) gl[rb][e] = R[KDA_BR_GL + 16 * (2 * w + rb) + 4 * gq + e];
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = 16 * (2 * w + rb) + 4 * gq + e;
+                ck[r * KDA_DV + col] = S[rb][e];
+                sS[s_lds(r, r16)] = S[rb][e];
+            }
         __syncthreads();
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            const int i = rb + 16 * m;
-            float s = R[KDA_BR_U + i * KDA_DV + col];
-            for (int r = 0; r < KDA_DK; r++) s = fmaf(-R[KDA_BR_W + i * KDA_DK + r], sS[r * 16 + j], s);
-            sD[i * 16 + j] = s;
+        for (int s = 0; s < 32; s++) {
+            const float4 f = wv[s >> 2];
+            const float a = (s & 3) == 0 ? f.x : (s & 3) == 1 ? f.y : (s & 3) == 2 ? f.z : f.w;
+            dacc = mfma4(-a, sS[s_lds(32 * gq + s, r16)], dacc);
         }
+#pragma unroll
+        for (int e = 0; e < 4; e++) sD[d_lds(16 * w + 4 * gq + e, r16)] = dacc[e];
         __syncthreads();
 #pragma unroll
-        for (int m = 0; m < 8; m++) {
-            const int r = rb + 16 * m;
-            float s = R[KDA_BR_GL + r] * S[m];
-            for (int i = 0; i < KDA_CHUNK; i++) s = fmaf(R[KDA_BR_KT + i * KDA_DK + r], sD[i * 16 + j], s);
-            S[m] = s;
+        for (int rb = 0; rb < 2; rb++) {
+            f32x4 acc = gl[rb] * S[rb];
+#pragma unroll
+            for (int s = 0; s < 16; s++) acc = mfma4(kt[rb][s], sD[d_lds(16 * gq + s, r16)], acc);
+            S[rb] = acc;
         }
-        __syncthreads();
     }
 
-    float dS[8];
+    /* reverse: dS_{c+1} is stored, dD = K~ dS_{c+1},
+     * dS_c = diag(e^{G_L}) dS_{c+1} - W^T dD + Q'^T dout_c */
+    f32x4 dS[2];
 #pragma unroll
-    for (int m = 0; m < 8; m++)
-        dS[m] = dfinal == nullptr ? 0.f : dfinal[sbase + (int64_t)(rb + 16 * m) * KDA_DV + col];
+    for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            dS[rb][e] = dfinal == nullptr ? 0.f
+                      : dfinal[sbase + (int64_t)(16 * (2 * w + rb) + 4 * gq + e) * KDA_DV + col];
     for (int64_t c = nchunk - 1; c >= 0; c--) {
         const int64_t item = (int64_t)h * nslots + slot0 + c;
         const float *R = brec + item * KDA_BR_FLOATS;
         float *dk = dse + item * (int64_t)(KDA_DK * KDA_DV);
         const int64_t rem = len - c * KDA_CHUNK;
         const int L = (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
+        float4 kv[8];  /* K~ row 16 w + r16, columns 32 gq .. 32 gq + 31 */
+        float wt[2][16], qt[2][16], o[16];
+        f32x4 gl[2];
+        const float *krow = R + KDA_BR_KT + (16 * w + r16) * KDA_DK + 32 * gq;
 #pragma unroll
-        for (int m = 0; m < 8; m++) {
-            const int r = rb + 16 * m;
-            dk[r * KDA_DV + col] = dS[m];
-            sS[r * 16 + j] = dS[m];
-        }
+        for (int i = 0; i < 8; i++) kv[i] = *(const float4 *)(krow + 4 * i);
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            const int i = rb + 16 * m;
-            sO[i * 16 + j] = i < L ? bf2f(dout[((row0 + c * KDA_CHUNK + i) * H + h) * KDA_DV + col]) : 0.f;
-        }
-        __syncthreads();
+        for (int rb = 0; rb < 2; rb++)
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            const int i = rb + 16 * m;
-            float s = 0.f;
-            for (int r = 0; r < KDA_DK; r++) s = fmaf(R[KDA_BR_KT + i * KDA_DK + r], sS[r * 16 + j], s);
-            sD[i * 16 + j] = s;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < 8; m++) {
-            const int r = rb + 16 * m;
-            float s = R[KDA_BR_GL + r] * dS[m];
-            for (int i = 0; i < L; i++) {
-                s = fmaf(-R[KDA_BR_W + i * KDA_DK + r], sD[i * 16 + j], s);
-                s = fmaf(R[KDA_BR_QP + i * KDA_DK + r], sO[i * 16 + j], s);
+            for (int s = 0; s < 16; s++) {
+                const int idx = (16 * gq + s) * KDA_DK + 16 * (2 * w + rb) + r16;
+                wt[rb][s] = R[KDA_BR_W + idx];
+                qt[rb][s] = R[KDA_BR_QP + idx];
             }
-            dS[m] = s;
+#pragma unroll
+        for (int s = 0; s < 16; s++) {
+            const int i = 16 * gq + s;
+            o[s] = i < L ? bf2f(dout[((row0 + c * KDA_CHUNK + i) * H + h) * KDA_DV + col]) : 0.f;
         }
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) gl[rb][e] = R[KDA_BR_GL + 16 * (2 * w + rb) + 4 * gq + e];
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int r = 16 * (2 * w + rb) + 4 * gq + e;
+                dk[r * KDA_DV + col] = dS[rb][e];
+                sS[s_lds(r, r16)] = dS[rb][e];
+            }
         __syncthreads();
+        f32x4 dacc = zero4();
+#pragma unroll
+        for (int s = 0; s < 32; s++) {
+            const float4 f = kv[s >> 2];
+            const float a = (s & 3) == 0 ? f.x : (s & 3) == 1 ? f.y : (s & 3) == 2 ? f.z : f.w;
+            dacc = mfma4(a, sS[s_lds(32 * gq + s, r16)], dacc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; e++) sD[d_lds(16 * w + 4 * gq + e, r16)] = dacc[e];
+        __syncthreads();
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++) {
+            f32x4 acc = gl[rb] * dS[rb];
+#pragma unroll
+            for (int s = 0; s < 16; s++) {
+                acc = mfma4(-wt[rb][s], sD[d_lds(16 * gq + s, r16)], acc);
+                acc = mfma4(qt[rb][s], o[s], acc);
+            }
+            dS[rb] = acc;
+        }
     }
     if (dinit != nullptr) {
 #pragma unroll
-        for (int m = 0; m < 8; m++) dinit[sbase + (int64_t)(rb + 16 * m) * KDA_DV + col] = dS[m];
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                dinit[sbase + (int64_t)(16 * (2 * w + rb) + 4 * gq + e) * KDA_DV + col] = dS[rb][e];
     }
 }
 
@@ -387,12 +507,7 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
     __shared__ float sdA[KDA_CHUNK * LDT], sdP[KDA_CHUNK * LDT];
     __shared__ float sBeta[KDA_CHUNK], sGL[KDA_DK], sGL2[KDA_DK], sRed[KDA_DK];
 
-    float *scr = scratch + (size_t)blockIdx.x * KDA_BWD_SCR_FLOATS;
-    float *D = scr, *dD = scr + 8192, *dQp = scr + 2 * 8192, *dW = scr + 3 * 8192, *dKt = scr + 4 * 8192;
-    float *dU = scr + 5 * 8192, *XW = scr + 6 * 8192, *XU = scr + 7 * 8192, *dXW = scr + 8 * 8192;
-    float *dXU = scr + 9 * 8192, *dqn = scr + 10 * 8192, *dkn = scr + 11 * 8192, *dG = scr + 12 * 8192;
-    float *DO = scr + 13 * 8192;
-    float *dP = scr + 14 * 8192, *dT = dP + 4096, *X1 = dP + 2 * 4096;
+    float *const scr0 = scratch + (size_t)blockIdx.x * KDA_BWD_SCR_FLOATS;
 
     const int t = threadIdx.x, c = t & 127, half = t >> 7;
     const int64_t nitems = (int64_t)H * nslots;
@@ -405,6 +520,16 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         const float *R = brec + item * KDA_BR_FLOATS;
         const float *S0 = ckpt + item * (int64_t)(KDA_DK * KDA_DV);
         const float *dS = dse + item * (int64_t)(KDA_DK * KDA_DV);
+        /* the scratch base is re-derived per item (opaque to the compiler), so the
+         * per-lane operand addresses of the products are not hoisted out of the item
+         * loop, where they would hold hundreds of registers */
+        float *scr = scr0;
+        asm volatile("" : "+s"(scr));
+        float *D = scr, *dD = scr + 8192, *dQp = scr + 2 * 8192, *dW = scr + 3 * 8192, *dKt = scr + 4 * 8192;
+        float *dU = scr + 5 * 8192, *XW = scr + 6 * 8192, *XU = scr + 7 * 8192, *dXW = scr + 8 * 8192;
+        float *dXU = scr + 9 * 8192, *dqn = scr + 10 * 8192, *dkn = scr + 11 * 8192, *dG = scr + 12 * 8192;
+        float *DO = scr + 13 * 8192;
+        float *dP = scr + 14 * 8192, *dT = dP + 4096, *X1 = dP + 2 * 4096;
         const float rate = expf(A_log[h]);
 
         /* s0: dout, X_W, X_U, D <- U; LDS copies of G and k^ */
@@ -425,53 +550,52 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         __syncthreads();
 
         /* s1: D = U - W S, dD = K~ dS, dQ' = dout S^T */
-        wg_gemm<false, false>(D, KDA_DV, R + KDA_BR_W, KDA_DK, S0, KDA_DV, KDA_CHUNK, KDA_DV, KDA_DK, -1.f, true);
-        wg_gemm<false, false>(dD, KDA_DV, R + KDA_BR_KT, KDA_DK, dS, KDA_DV, KDA_CHUNK, KDA_DV, KDA_DK, 1.f, false);
-        wg_gemm<false, true>(dQp, KDA_DK, DO, KDA_DV, S0, KDA_DV, KDA_CHUNK, KDA_DK, KDA_DV, 1.f, false);
+        wg_gemm<false, false, KDA_DV, KDA_DK>(D, R + KDA_BR_W, S0, -1.f, true);
+        wg_gemm<false, false, KDA_DV, KDA_DK>(dD, R + KDA_BR_KT, dS, 1.f, false);
+        wg_gemm<false, true, KDA_DK, KDA_DV>(dQp, DO, S0, 1.f, false);
         __syncthreads();
 
         /* s2: dW = -dD S^T, dK~ = D dS^T, dP = dout U^T, dU = P^T dout */
-        wg_gemm<false, true>(dW, KDA_DK, dD, KDA_DV, S0, KDA_DV, KDA_CHUNK, KDA_DK, KDA_DV, -1.f, false);
-        wg_gemm<false, true>(dKt, KDA_DK, D, KDA_DV, dS, KDA_DV, KDA_CHUNK, KDA_DK, KDA_DV, 1.f, false);
-        wg_gemm<false, true>(dP, KDA_CHUNK, DO, KDA_DV, R + KDA_BR_U, KDA_DV, KDA_CHUNK, KDA_CHUNK, KDA_DV, 1.f, false);
-        wg_gemm<true, false>(dU, KDA_DV, R + KDA_BR_P, KDA_CHUNK, DO, KDA_DV, KDA_CHUNK, KDA_DV, KDA_CHUNK, 1.f, false);
+        wg_gemm<false, true, KDA_DK, KDA_DV>(dW, dD, S0, -1.f, false);
+        wg_gemm<false, true, KDA_DK, KDA_DV>(dKt, D, dS, 1.f, false);
+        wg_gemm<false, true, KDA_CHUNK, KDA_DV>(dP, DO, R + KDA_BR_U, 1.f, false);
+        wg_gemm<true, false, KDA_DV, KDA_CHUNK>(dU, R + KDA_BR_P, DO, 1.f, false);
         __syncthreads();
 
         /* s3: Q' = scale q^ e^G - P W: dP -= dQ' W^T, dW -= P^T dQ'; dU += dD */
-        wg_gemm<false, true>(dP, KDA_CHUNK, dQp, KDA_DK, R + KDA_BR_W, KDA_DK, KDA_CHUNK, KDA_CHUNK, KDA_DK, -1.f, true);
-        wg_gemm<true, false>(dW, KDA_DK, R + KDA_BR_P, KDA_CHUNK, dQp, KDA_DK, KDA_CHUNK, KDA_DK, KDA_CHUNK, -1.f, true);
+        wg_gemm<false, true, KDA_CHUNK, KDA_DK>(dP, dQp, R + KDA_BR_W, -1.f, true);
+        wg_gemm<true, false, KDA_DK, KDA_CHUNK>(dW, R + KDA_BR_P, dQp, -1.f, true);
         for (int e = t; e < KDA_CHUNK * KDA_DV; e += NT) dU[e] += dD[e];
         __syncthreads();
 
         /* s4: dT = dW X_W^T (+ dU X_U^T below), dX_W = T^T dW, dX_U = T^T dU; masked dP to LDS */
-        wg_gemm<false, true>(dT, KDA_CHUNK, dW, KDA_DK, XW, KDA_DK, KDA_CHUNK, KDA_CHUNK, KDA_DK, 1.f, false);
-        wg_gemm<true, false>(dXW, KDA_DK, R + KDA_BR_T, KDA_CHUNK, dW, KDA_DK, KDA_CHUNK, KDA_DK, KDA_CHUNK, 1.f, false);
-        wg_gemm<true, false>(dXU, KDA_DV, R + KDA_BR_T, KDA_CHUNK, dU, KDA_DV, KDA_CHUNK, KDA_DV, KDA_CHUNK, 1.f, false);
+        wg_gemm<false, true, KDA_CHUNK, KDA_DK>(dT, dW, XW, 1.f, false);
+        wg_gemm<true, false, KDA_DK, KDA_CHUNK>(dXW, R + KDA_BR_T, dW, 1.f, false);
+        wg_gemm<true, false, KDA_DV, KDA_CHUNK>(dXU, R + KDA_BR_T, dU, 1.f, false);
         for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NT) {
             const int i = e >> 6, jj = e & 63;
             sdP[i * LDT + jj] = jj <= i ? dP[e] : 0.f;
         }
         __syncthreads();
-        wg_gemm<false, true>(dT, KDA_CHUNK, dU, KDA_DV, XU, KDA_DV, KDA_CHUNK, KDA_CHUNK, KDA_DV, 1.f, true);
+        wg_gemm<false, true, KDA_CHUNK, KDA_DV>(dT, dU, XU, 1.f, true);
         __syncthreads();
 
         /* s5: X1 = T^T dT */
-        wg_gemm<true, false>(X1, KDA_CHUNK, R + KDA_BR_T, KDA_CHUNK, dT, KDA_CHUNK, KDA_CHUNK, KDA_CHUNK, KDA_CHUNK, 1.f, false);
+        wg_gemm<true, false, KDA_CHUNK, KDA_CHUNK>(X1, R + KDA_BR_T, dT, 1.f, false);
         __syncthreads();
 
-        /* s6: dA = -X1 T^T on the strict lower triangle */
-        for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NT) {
-            const int i = e >> 6, jj = e & 63;
-            float s = 0.f;
-            if (jj < i)
-                for (int n = 0; n < KDA_CHUNK; n++) s = fmaf(X1[i * KDA_CHUNK + n], R[KDA_BR_T + jj * KDA_CHUNK + n], s);
-            sdA[i * LDT + jj] = -s;
-        }
+        /* s6: dA = -X1 T^T (into dT, which is no longer needed), kept on the strict lower triangle */
+        wg_gemm<false, true, KDA_CHUNK, KDA_CHUNK>(dT, X1, R + KDA_BR_T, -1.f, false);
         /* s6b: d G_L from the carried decay: e^{G_L} sum_j dS[c][j] S[c][j] */
         if (half == 0) {
             float s = 0.f;
             for (int jj = 0; jj < KDA_DV; jj++) s = fmaf(dS[c * KDA_DV + jj], S0[c * KDA_DV + jj], s);
             sGL[c] = R[KDA_BR_GL + c] * s;
+        }
+        __syncthreads();
+        for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NT) {
+            const int i = e >> 6, jj = e & 63;
+            sdA[i * LDT + jj] = jj < i ? dT[e] : 0.f;
         }
         __syncthreads();
 
