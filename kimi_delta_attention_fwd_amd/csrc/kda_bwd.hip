@@ -246,7 +246,7 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
         float a = 0.f, p = 0.f;
         if (i < L) {
             for (int c = 0; c < KDA_DK; c++) {
-                const float E = expf(sG[i * LDK + c] - sG[j * LDK + c]);
+                const float E = exp2_fast((sG[i * LDK + c] - sG[j * LDK + c]) * LOG2E_F);
                 const float kj = sK[j * LDK + c] * E;
                 a = fmaf(sK[i * LDK + c], kj, a);
                 p = fmaf(sQ[i * LDK + c], kj, p);
@@ -292,24 +292,39 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
     float acc[KDA_CHUNK];
 #pragma unroll
     for (int i = 0; i < KDA_CHUNK; i++) acc[i] = 0.f;
-    for (int m = 0; m < L; m++) {
-        const float x = half == 0 ? sB[m] * sK[m * LDK + c] * expf(sG[m * LDK + c])
-                                  : sB[m] * bf2f(v[((t0 + m) * H + h) * KDA_DV + c]);
+    /* rows m >= L contribute nothing (beta_m = 0 there, and v is not read) */
+#pragma unroll 1
+    for (int m0 = 0; m0 < KDA_CHUNK; m0 += 8) {
+        float x[8];
 #pragma unroll
-        for (int i = 0; i < KDA_CHUNK; i++) acc[i] = fmaf(sT[i * LDT + m], x, acc[i]);
+        for (int u = 0; u < 8; u++) {
+            const int m = m0 + u;
+            x[u] = half == 0 ? sB[m] * sK[m * LDK + c] * expf(sG[m * LDK + c])
+                             : (m < L ? sB[m] * bf2f(v[((t0 + m) * H + h) * KDA_DV + c]) : 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+#pragma unroll
+            for (int i = 0; i < KDA_CHUNK; i++) acc[i] = fmaf(sT[i * LDT + m0 + u], x[u], acc[i]);
     }
     float *dst = R + (half == 0 ? KDA_BR_W : KDA_BR_U);
 #pragma unroll
     for (int i = 0; i < KDA_CHUNK; i++) dst[i * KDA_DK + c] = acc[i];
     if (half == 0) {
-        /* acc holds column c of W: Q'[i][c] = scale q^ e^G - sum_m P[i][m] W[m][c] */
+        /* Q'[i][c] = scale q^ e^G - sum_m P[i][m] W[m][c] */
         float qp[KDA_CHUNK];
 #pragma unroll
         for (int i = 0; i < KDA_CHUNK; i++) qp[i] = scale * sQ[i * LDK + c] * expf(sG[i * LDK + c]);
-        for (int m = 0; m < L; m++) {
-            const float wm = R[KDA_BR_W + m * KDA_DK + c];
+        /* column c of W back from the record (this thread's own stores), eight rows per pass */
+#pragma unroll 1
+        for (int m0 = 0; m0 < KDA_CHUNK; m0 += 8) {
+            float wm[8];
 #pragma unroll
-            for (int i = 0; i < KDA_CHUNK; i++) qp[i] = fmaf(-sP[i * LDT + m], wm, qp[i]);
+            for (int u = 0; u < 8; u++) wm[u] = R[KDA_BR_W + (m0 + u) * KDA_DK + c];
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+#pragma unroll
+                for (int i = 0; i < KDA_CHUNK; i++) qp[i] = fmaf(-sP[i * LDT + m0 + u], wm[u], qp[i]);
         }
 #pragma unroll
         for (int i = 0; i < KDA_CHUNK; i++) R[KDA_BR_QP + i * KDA_DK + c] = qp[i];
@@ -503,9 +518,9 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
                     float *__restrict__ scratch, float *__restrict__ dq, float *__restrict__ dk,
                     float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta)
 {
-    __shared__ float sG[KDA_CHUNK * LDK], sK[KDA_CHUNK * LDK];
+    __shared__ float sG[KDA_CHUNK * LDK], sK[KDA_CHUNK * LDK], sQ[KDA_CHUNK * LDK];
     __shared__ float sdA[KDA_CHUNK * LDT], sdP[KDA_CHUNK * LDT];
-    __shared__ float sBeta[KDA_CHUNK], sGL[KDA_DK], sGL2[KDA_DK], sRed[KDA_DK];
+    __shared__ float sBeta[KDA_CHUNK], sGL[KDA_DK], sGL2[KDA_DK], sRed[KDA_DK], sX[2 * KDA_DK];
 
     float *const scr0 = scratch + (size_t)blockIdx.x * KDA_BWD_SCR_FLOATS;
 
@@ -532,19 +547,35 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         float *dP = scr + 14 * 8192, *dT = dP + 4096, *X1 = dP + 2 * 4096;
         const float rate = expf(A_log[h]);
 
-        /* s0: dout, X_W, X_U, D <- U; LDS copies of G and k^ */
-        for (int e = t; e < KDA_CHUNK * KDA_DK; e += NT) {
-            const int i = e >> 7, cc = e & 127;
-            const float b = R[KDA_BR_BETA + i];
-            const bool ok = i < L;
-            const int64_t row = ((t0 + i) * H + h) * KDA_DV + cc;
-            DO[e] = ok ? bf2f(dout[row]) : 0.f;
-            XU[e] = ok ? b * bf2f(v[row]) : 0.f;
-            const float gg = R[KDA_BR_G + e], kk = R[KDA_BR_KN + e];
-            XW[e] = b * kk * expf(gg);
-            D[e] = R[KDA_BR_U + e];
-            sG[i * LDK + cc] = gg;
-            sK[i * LDK + cc] = kk;
+        /* s0: dout, X_W, X_U, D <- U; LDS copies of G (in log2 units), k^ and q^. Eight
+         * elements per pass with all their loads issued before any store (the scratch
+         * stores could otherwise alias the record loads for the compiler) */
+        for (int e0 = t; e0 < KDA_CHUNK * KDA_DK; e0 += 8 * NT) {
+            float xb[8], xo[8], xv[8], xg[8], xk[8], xu[8], xq[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int e = e0 + u * NT, i = e >> 7, cc = e & 127;
+                const bool ok = i < L;
+                const int64_t row = ((t0 + i) * H + h) * KDA_DV + cc;
+                xb[u] = R[KDA_BR_BETA + i];
+                xo[u] = ok ? bf2f(dout[row]) : 0.f;
+                xv[u] = ok ? bf2f(v[row]) : 0.f;
+                xg[u] = R[KDA_BR_G + e];
+                xk[u] = R[KDA_BR_KN + e];
+                xu[u] = R[KDA_BR_U + e];
+                xq[u] = R[KDA_BR_QN + e];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int e = e0 + u * NT, i = e >> 7, cc = e & 127;
+                DO[e] = xo[u];
+                XU[e] = xb[u] * xv[u];
+                XW[e] = xb[u] * xk[u] * exp2_fast(xg[u] * LOG2E_F);
+                D[e] = xu[u];
+                sG[i * LDK + cc] = xg[u] * LOG2E_F;
+                sK[i * LDK + cc] = xk[u];
+                sQ[i * LDK + cc] = xq[u];
+            }
         }
         if (t < KDA_CHUNK) sBeta[t] = R[KDA_BR_BETA + t];
         __syncthreads();
@@ -574,7 +605,7 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         wg_gemm<true, false, KDA_DV, KDA_CHUNK>(dXU, R + KDA_BR_T, dU, 1.f, false);
         for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NT) {
             const int i = e >> 6, jj = e & 63;
-            sdP[i * LDT + jj] = jj <= i ? dP[e] : 0.f;
+            sdP[i * LDT + jj] = jj <= i ? scale * dP[e] : 0.f; /* scale folded in */
         }
         __syncthreads();
         wg_gemm<false, true, KDA_CHUNK, KDA_DV>(dT, dU, XU, 1.f, true);
@@ -586,11 +617,23 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
 
         /* s6: dA = -X1 T^T (into dT, which is no longer needed), kept on the strict lower triangle */
         wg_gemm<false, true, KDA_CHUNK, KDA_CHUNK>(dT, X1, R + KDA_BR_T, -1.f, false);
-        /* s6b: d G_L from the carried decay: e^{G_L} sum_j dS[c][j] S[c][j] */
-        if (half == 0) {
+        /* s6b: d G_L from the carried decay: e^{G_L} sum_j dS[r][j] S[r][j]; thread t takes
+         * row t / 2, columns 64 (t % 2) .. + 63 as 16-byte pieces */
+        {
+            const int r = t >> 1, hf = t & 1;
+            const float4 *a4 = (const float4 *)(dS + r * KDA_DV + 64 * hf);
+            const float4 *b4 = (const float4 *)(S0 + r * KDA_DV + 64 * hf);
             float s = 0.f;
-            for (int jj = 0; jj < KDA_DV; jj++) s = fmaf(dS[c * KDA_DV + jj], S0[c * KDA_DV + jj], s);
-            sGL[c] = R[KDA_BR_GL + c] * s;
+#pragma unroll
+            for (int jj = 0; jj < 16; jj++) {
+                const float4 x = a4[jj], y = b4[jj];
+                s = fmaf(x.x, y.x, s);
+                s = fmaf(x.y, y.y, s);
+                s = fmaf(x.z, y.z, s);
+                s = fmaf(x.w, y.w, s);
+            }
+            s += __shfl_xor(s, 1);
+            if (hf == 0) sGL[r] = R[KDA_BR_GL + r] * s;
         }
         __syncthreads();
         for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NT) {
@@ -599,29 +642,44 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         }
         __syncthreads();
 
-        /* s7: per-element terms (Q', K~, X_W, X_U); thread (c, half) takes rows of parity half */
+        /* s7: per-element terms (Q', K~, X_W, X_U); thread (c, half) takes rows of parity
+         * half, four rows per pass with all their loads issued first */
         {
             const float gl = sG[(L - 1) * LDK + c];
             float glacc = 0.f;
-            for (int i = half; i < L; i += 2) {
-                const int e = i * KDA_DK + c;
-                const float gam = expf(sG[i * LDK + c]), kn = sK[i * LDK + c], qn = R[KDA_BR_QN + e];
-                const float b = sBeta[i];
-                float aq = scale * dQp[e] * gam;
-                float ag = scale * qn * gam * dQp[e];
-                const float kt = R[KDA_BR_KT + e], dkt = dKt[e];
-                float ak = dkt * expf(gl - sG[i * LDK + c]);
-                ag -= dkt * kt;
-                glacc = fmaf(dkt, kt, glacc);
-                const float dxw = dXW[e], dxu = dXU[e];
-                ak = fmaf(b * gam, dxw, ak);
-                ag = fmaf(b * kn * gam, dxw, ag);
-                const float vv = bf2f(v[((t0 + i) * H + h) * KDA_DV + c]);
-                dv[((t0 + i) * H + h) * KDA_DV + c] = b * dxu;
-                XU[e] = kn * gam * dxw + vv * dxu;   /* d beta partial of (i, c); X_U is no longer needed */
-                dqn[e] = aq;
-                dkn[e] = ak;
-                dG[e] = ag;
+            for (int i0 = half; i0 < L; i0 += 8) {
+                float xdq[4], xkt[4], xdkt[4], xdxw[4], xdxu[4], xv[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const int i = i0 + 2 * u, e = i * KDA_DK + c;
+                    const bool ok = i < L;
+                    xdq[u] = ok ? dQp[e] : 0.f;
+                    xkt[u] = ok ? R[KDA_BR_KT + e] : 0.f;
+                    xdkt[u] = ok ? dKt[e] : 0.f;
+                    xdxw[u] = ok ? dXW[e] : 0.f;
+                    xdxu[u] = ok ? dXU[e] : 0.f;
+                    xv[u] = ok ? bf2f(v[((t0 + i) * H + h) * KDA_DV + c]) : 0.f;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const int i = i0 + 2 * u, e = i * KDA_DK + c;
+                    if (i < L) {
+                        const float gam = exp2_fast(sG[i * LDK + c]), kn = sK[i * LDK + c], qn = sQ[i * LDK + c];
+                        const float b = sBeta[i];
+                        float aq = scale * xdq[u] * gam;
+                        float ag = scale * qn * gam * xdq[u];
+                        float ak = xdkt[u] * exp2_fast(gl - sG[i * LDK + c]);
+                        ag -= xdkt[u] * xkt[u];
+                        glacc = fmaf(xdkt[u], xkt[u], glacc);
+                        ak = fmaf(b * gam, xdxw[u], ak);
+                        ag = fmaf(b * kn * gam, xdxw[u], ag);
+                        dv[((t0 + i) * H + h) * KDA_DV + c] = b * xdxu[u];
+                        XU[e] = kn * gam * xdxw[u] + xv[u] * xdxu[u]; /* d beta partial of (i, c); X_U is no longer needed */
+                        dqn[e] = aq;
+                        dkn[e] = ak;
+                        dG[e] = ag;
+                    }
+                }
             }
             if (half == 1) sGL2[c] = glacc;
             __syncthreads();
@@ -629,61 +687,111 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         }
         __syncthreads();
 
-        /* s8: pairwise factors, row side: rows i of parity half, j <= i */
+        /* s8: pairwise factors, row side: rows i of parity half, j <= i. With
+         * E = e^{G_i - G_j} per channel, SA = sum_j dA_ij k^_j E and SP = sum_j scale dP_ij k^_j E
+         * give every row-side term: d k^_i += beta_i SA, d q^_i += SP,
+         * dG_i += beta_i k^_i SA + q^_i SP, and the d beta partial k^_i SA */
         for (int i = half; i < L; i += 2) {
             const int e = i * KDA_DK + c;
-            const float gi = sG[i * LDK + c], kni = sK[i * LDK + c], qni = R[KDA_BR_QN + e];
-            const float bi = sBeta[i];
-            float ag = 0.f, ak = 0.f, aq = 0.f, ab = 0.f;
-            for (int jj = 0; jj <= i; jj++) {
-                const float E = expf(gi - sG[jj * LDK + c]);
-                const float knj = sK[jj * LDK + c] * E;
-                const float a = sdA[i * LDT + jj], p = sdP[i * LDT + jj];
-                const float ta = a * bi * kni * knj, tp = p * scale * qni * knj;
-                ag += ta + tp;
-                ak = fmaf(a * bi, knj, ak);
-                aq = fmaf(p * scale, knj, aq);
-                ab = fmaf(a * kni, knj, ab);
+            const float g0 = dG[e], k0 = dkn[e], q0 = dqn[e], b0 = XU[e];
+            const float gi = sG[i * LDK + c];
+            float sa = 0.f, sp = 0.f;
+            /* blocks of 8 partners with all LDS reads first; partners past i have
+             * dA = dP = 0 there and a clamped (finite) factor, so they add exactly 0 */
+            for (int j0 = 0; j0 <= i; j0 += 8) {
+                float xg[8], xk[8], xa[8], xp[8];
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    xg[u] = sG[(j0 + u) * LDK + c];
+                    xk[u] = sK[(j0 + u) * LDK + c];
+                    xa[u] = sdA[i * LDT + j0 + u];
+                    xp[u] = sdP[i * LDT + j0 + u];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const float knj = xk[u] * exp2_fast(fminf(gi - xg[u], 0.f));
+                    sa = fmaf(xa[u], knj, sa);
+                    sp = fmaf(xp[u], knj, sp);
+                }
             }
-            dG[e] += ag;
-            dkn[e] += ak;
-            dqn[e] += aq;
-            XU[e] += ab;
+            const float kni = sK[i * LDK + c], qni = sQ[i * LDK + c], bi = sBeta[i];
+            dG[e] = g0 + fmaf(bi * kni, sa, qni * sp);
+            dkn[e] = k0 + bi * sa;
+            dqn[e] = q0 + sp;
+            XU[e] = b0 + kni * sa;
         }
         __syncthreads();
 
-        /* s9: pairwise factors, column side: rows j of parity half, i >= j */
+        /* s9: pairwise factors, column side: rows j of parity half, i >= j:
+         * CT = sum_i (dA_ij beta_i k^_i + scale dP_ij q^_i) E; d k^_j += CT, dG_j -= k^_j CT */
         for (int jj = half; jj < L; jj += 2) {
             const int e = jj * KDA_DK + c;
+            const float g0 = dG[e], k0 = dkn[e];
             const float gj = sG[jj * LDK + c], knj = sK[jj * LDK + c];
-            float ag = 0.f, ak = 0.f;
-            for (int i = jj; i < L; i++) {
-                const float E = expf(sG[i * LDK + c] - gj);
-                const float a = sdA[i * LDT + jj], p = sdP[i * LDT + jj];
-                const float tt = (a * sBeta[i] * sK[i * LDK + c] + p * scale * R[KDA_BR_QN + i * KDA_DK + c]) * E;
-                ak += tt;
-                ag = fmaf(-tt, knj, ag);
+            float ct = 0.f;
+            /* blocks of 8 rows from the one holding jj, LDS reads first; rows before jj
+             * or past the chunk have dA = dP = 0 there and add exactly 0 */
+            for (int i0 = jj & ~7; i0 < L; i0 += 8) {
+                float xg[8], xk[8], xq[8], xb[8], xa[8], xp[8];
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const int i = i0 + u;
+                    xg[u] = sG[i * LDK + c];
+                    xk[u] = sK[i * LDK + c];
+                    xq[u] = sQ[i * LDK + c];
+                    xb[u] = sBeta[i];
+                    xa[u] = sdA[i * LDT + jj];
+                    xp[u] = sdP[i * LDT + jj];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; u++) {
+                    const float coef = fmaf(xa[u] * xb[u], xk[u], xp[u] * xq[u]);
+                    ct = fmaf(coef, exp2_fast(fminf(xg[u] - gj, 0.f)), ct);
+                }
             }
-            dG[e] += ag;
-            dkn[e] += ak;
+            dG[e] = fmaf(-knj, ct, g0);
+            dkn[e] = k0 + ct;
         }
         __syncthreads();
 
-        /* s10: d log a = reverse cumsum of dG (G_L's gradient on the last row), then the gate */
-        if (half == 0) {
-            float run = sGL[c], pdt = 0.f, pa = 0.f;
-            for (int i = L - 1; i >= 0; i--) {
-                run += dG[i * KDA_DK + c];
-                const float x = bf2f(g[((t0 + i) * H + h) * KDA_DK + c]) + dt_bias[h * KDA_DK + c];
-                const float free_la = -rate * softplus_f(x);
-                const float dla = free_la < lower_bound ? 0.f : run;
-                const float dx = -dla * rate * sigmoid_f(x);
-                dg[((t0 + i) * H + h) * KDA_DK + c] = dx;
-                pdt += dx;
-                pa = fmaf(dla, free_la, pa);
+        /* s10: d log a = reverse cumsum of dG (G_L's gradient on the last row), then the
+         * gate; thread (c, half) takes rows 32 half .. 32 half + 31, and the lower half
+         * starts from the upper half's total */
+        {
+            const int r0 = 32 * half, n = L - r0; /* rows of this half: u < n */
+            float xg[32], tot = 0.f;
+#pragma unroll
+            for (int u = 0; u < 32; u++) {
+                xg[u] = u < n ? dG[(r0 + u) * KDA_DK + c] : 0.f;
+                tot += xg[u];
             }
-            part[item * KDA_BWD_PART_FLOATS + c] = pdt;
-            sRed[c] = pa;
+            if (half == 1) sGL2[c] = tot;
+            __syncthreads();
+            float run = sGL[c] + (half == 0 ? sGL2[c] : 0.f), pdt = 0.f, pa = 0.f;
+            const float bias = dt_bias[h * KDA_DK + c];
+#pragma unroll
+            for (int u = 31; u >= 0; u--) {
+                if (u < n) {
+                    const int i = r0 + u;
+                    run += xg[u];
+                    const float x = bf2f(g[((t0 + i) * H + h) * KDA_DK + c]) + bias;
+                    const float free_la = -rate * softplus_f(x);
+                    const float dla = free_la < lower_bound ? 0.f : run;
+                    const float dx = -dla * rate * sigmoid_f(x);
+                    dg[((t0 + i) * H + h) * KDA_DK + c] = dx;
+                    pdt += dx;
+                    pa = fmaf(dla, free_la, pa);
+                }
+            }
+            if (half == 1) {
+                sX[c] = pdt;
+                sX[KDA_DK + c] = pa;
+            }
+            __syncthreads();
+            if (half == 0) {
+                part[item * KDA_BWD_PART_FLOATS + c] = pdt + sX[c];
+                sRed[c] = pa + sX[KDA_DK + c];
+            }
         }
         __syncthreads();
         if (t == 0) {
@@ -692,17 +800,30 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
             part[item * KDA_BWD_PART_FLOATS + KDA_DK] = s;
         }
 
-        /* s11: through the L2 norms; thread t: row t / 4, channels 32 (t % 4) + [0, 32) */
+        /* s11: through the L2 norms; thread t: row t / 4, channels 16 m + 4 (t % 4) + [0, 4)
+         * for m < 8 (16-byte pieces of the scratch rows) */
         {
-            const int i = t >> 2, c0 = (t & 3) * 32;
+            const int i = t >> 2, q4 = t & 3;
+            float xq[8][4], xk[8][4];
             float sq = 0.f, sk = 0.f, sb = 0.f;
             if (i < L) {
-                for (int cc = 0; cc < 32; cc++) {
-                    const int e = i * KDA_DK + c0 + cc;
-                    sq = fmaf(R[KDA_BR_QN + e], dqn[e], sq);
-                    sk = fmaf(R[KDA_BR_KN + e], dkn[e], sk);
-                    sb += XU[e];
+#pragma unroll
+                for (int m = 0; m < 8; m++) {
+                    const int e = i * KDA_DK + 16 * m + 4 * q4;
+                    const float4 fq = *(const float4 *)(dqn + e), fk = *(const float4 *)(dkn + e);
+                    const float4 fb = *(const float4 *)(XU + e);
+                    xq[m][0] = fq.x; xq[m][1] = fq.y; xq[m][2] = fq.z; xq[m][3] = fq.w;
+                    xk[m][0] = fk.x; xk[m][1] = fk.y; xk[m][2] = fk.z; xk[m][3] = fk.w;
+                    sb += (fb.x + fb.y) + (fb.z + fb.w);
                 }
+#pragma unroll
+                for (int m = 0; m < 8; m++)
+#pragma unroll
+                    for (int u = 0; u < 4; u++) {
+                        const int cc = 16 * m + 4 * q4 + u;
+                        sq = fmaf(sQ[i * LDK + cc], xq[m][u], sq);
+                        sk = fmaf(sK[i * LDK + cc], xk[m][u], sk);
+                    }
             }
             /* xor butterflies: every lane of a quad adds the same pairs (deterministic) */
             sq += __shfl_xor(sq, 1);
@@ -713,13 +834,16 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
             sb += __shfl_xor(sb, 2);
             if (i < L) {
                 const float inq = 1.f / R[KDA_BR_NQ + i], ink = 1.f / R[KDA_BR_NK + i];
-                const int64_t row = ((t0 + i) * H + h) * KDA_DK + c0;
-                for (int cc = 0; cc < 32; cc++) {
-                    const int e = i * KDA_DK + c0 + cc;
-                    dq[row + cc] = (dqn[e] - R[KDA_BR_QN + e] * sq) * inq;
-                    dk[row + cc] = (dkn[e] - R[KDA_BR_KN + e] * sk) * ink;
-                }
-                if ((t & 3) == 0) dbeta[(t0 + i) * H + h] = sb;
+                const int64_t row = ((t0 + i) * H + h) * KDA_DK;
+#pragma unroll
+                for (int m = 0; m < 8; m++)
+#pragma unroll
+                    for (int u = 0; u < 4; u++) {
+                        const int cc = 16 * m + 4 * q4 + u;
+                        dq[row + cc] = (xq[m][u] - sQ[i * LDK + cc] * sq) * inq;
+                        dk[row + cc] = (xk[m][u] - sK[i * LDK + cc] * sk) * ink;
+                    }
+                if (q4 == 0) dbeta[(t0 + i) * H + h] = sb;
             }
         }
         __syncthreads();
