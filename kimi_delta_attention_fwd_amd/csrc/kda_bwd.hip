@@ -257,19 +257,49 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
     }
     __syncthreads();
 
-    /* 4. T = (I + A)^-1, row by row: T[r][j] = delta_rj - sum_{j <= m < r} A[r][m] T[m][j] */
-    for (int r = 0; r < KDA_CHUNK; r++) {
-        if (t < KDA_CHUNK) {
-            const int j = t;
-            float s = 0.f;
-            if (j == r) {
-                s = 1.f;
-            } else if (j < r) {
-                for (int m = j; m < r; m++) s = fmaf(-sA[r * LDT + m], sT[m * LDT + j], s);
-            }
-            sT[r * LDT + j] = s;
+    /* 4. T = (I + A)^-1 by forward substitution in blocks of 16 rows: wave w inverts
+     *    the diagonal block (I + A_ww) with column j in registers of lanes j, j + 16, ...
+     *    (T_ww[r][j] = delta_rj - sum_{m < r} A_ww[r][m] T_ww[m][j]); then, for
+     *    i - b = 1, 2, 3, T_ib = -T_ii sum_{b <= m < i} A_im T_mb on fp32 MFMA, wave b
+     *    taking block (b + d, b) */
+    {
+        const int w = t >> 6, l = t & 63, gq = l >> 4, r16 = l & 15;
+        float tc[16];
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            float s = r == r16 ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < r; m++) s = fmaf(-sA[(16 * w + r) * LDT + 16 * w + m], tc[m], s);
+            tc[r] = s;
+        }
+        if (gq == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) sT[(16 * w + r) * LDT + 16 * w + r16] = tc[r];
         }
         __syncthreads();
+        for (int d = 1; d < 4; d++) {
+            const int bb = w, ib = w + d;
+            if (ib < 4) {
+                /* X = sum_m A_im T_mb: contraction index 16 m + 4 s + gq at step s */
+                f32x4 x = zero4();
+                for (int m = bb; m < ib; m++) {
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; s4++) {
+                        const int kk = 16 * m + 4 * s4 + gq;
+                        x = mfma4(sA[(16 * ib + r16) * LDT + kk], sT[kk * LDT + 16 * bb + r16], x);
+                    }
+                }
+                /* T_ib = -T_ii X; X in accumulator layout is the B operand for the
+                 * contraction index 4 gq + s at step s */
+                f32x4 y = zero4();
+#pragma unroll
+                for (int s4 = 0; s4 < 4; s4++)
+                    y = mfma4(-sT[(16 * ib + r16) * LDT + 16 * ib + 4 * gq + s4], x[s4], y);
+#pragma unroll
+                for (int e = 0; e < 4; e++) sT[(16 * ib + 4 * gq + e) * LDT + 16 * bb + r16] = y[e];
+            }
+            __syncthreads();
+        }
     }
 
     /* 5. store T, P, q^, k^, G */
@@ -285,56 +315,81 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
         R[KDA_BR_G + e] = sG[i * LDK + c];
     }
 
-    /* 6. W = T X_W (X_W = beta k^ e^G) in threads 0-127, U = T X_U (X_U = beta v) in
-     *    128-255, one channel column each; then Q' = scale q^ e^G - P W (first half)
-     *    and K~, e^{G_L} (second half) */
-    const int c = t & 127, half = t >> 7;
-    float acc[KDA_CHUNK];
+    /* 6. W = T X_W (X_W = beta k^ e^G), U = T X_U (X_U = beta v) and
+     *    Q' = scale q^ e^G - P W on fp32 MFMA: wave w takes columns 32 w .. 32 w + 31
+     *    (two 16-column blocks) of all 64 rows; the contraction index of the first two
+     *    products is 16 kb + 4 s + gq at step s, and W's accumulators serve as the B
+     *    operand of P W (contraction index 16 kb + 4 gq + s). Rows m >= L contribute
+     *    nothing (beta_m = 0 there, and v is not read). Then K~ and e^{G_L}. */
+    {
+        const int w = t >> 6, l = t & 63, gq = l >> 4, r16 = l & 15;
+        f32x4 wacc[4][2], uacc[4][2];
 #pragma unroll
-    for (int i = 0; i < KDA_CHUNK; i++) acc[i] = 0.f;
-    /* rows m >= L contribute nothing (beta_m = 0 there, and v is not read) */
-#pragma unroll 1
-    for (int m0 = 0; m0 < KDA_CHUNK; m0 += 8) {
-        float x[8];
+        for (int rb = 0; rb < 4; rb++)
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int m = m0 + u;
-            x[u] = half == 0 ? sB[m] * sK[m * LDK + c] * expf(sG[m * LDK + c])
-                             : (m < L ? sB[m] * bf2f(v[((t0 + m) * H + h) * KDA_DV + c]) : 0.f);
+            for (int cbi = 0; cbi < 2; cbi++) {
+                wacc[rb][cbi] = zero4();
+                uacc[rb][cbi] = zero4();
+            }
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
+#pragma unroll
+            for (int s4 = 0; s4 < 4; s4++) {
+                const int m = 16 * kb + 4 * s4 + gq;
+                float ta[4];
+#pragma unroll
+                for (int rb = 0; rb < 4; rb++) ta[rb] = sT[(16 * rb + r16) * LDT + m];
+#pragma unroll
+                for (int cbi = 0; cbi < 2; cbi++) {
+                    const int c = 32 * w + 16 * cbi + r16;
+                    const float xw = sB[m] * sK[m * LDK + c] * expf(sG[m * LDK + c]);
+                    const float xu = m < L ? sB[m] * bf2f(v[((t0 + m) * H + h) * KDA_DV + c]) : 0.f;
+#pragma unroll
+                    for (int rb = 0; rb < 4; rb++) {
+                        wacc[rb][cbi] = mfma4(ta[rb], xw, wacc[rb][cbi]);
+                        uacc[rb][cbi] = mfma4(ta[rb], xu, uacc[rb][cbi]);
+                    }
+                }
+            }
+        }
+        f32x4 qacc[4][2];
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+            for (int cbi = 0; cbi < 2; cbi++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int row = 16 * rb + 4 * gq + e, c = 32 * w + 16 * cbi + r16;
+                    R[KDA_BR_W + row * KDA_DK + c] = wacc[rb][cbi][e];
+                    R[KDA_BR_U + row * KDA_DV + c] = uacc[rb][cbi][e];
+                    qacc[rb][cbi][e] = scale * sQ[row * LDK + c] * expf(sG[row * LDK + c]);
+                }
+#pragma unroll
+        for (int kb = 0; kb < 4; kb++) {
+#pragma unroll
+            for (int s4 = 0; s4 < 4; s4++) {
+                const int m = 16 * kb + 4 * gq + s4;
+#pragma unroll
+                for (int ib = 0; ib < 4; ib++) {
+                    const float pa = -sP[(16 * ib + r16) * LDT + m];
+#pragma unroll
+                    for (int cbi = 0; cbi < 2; cbi++) qacc[ib][cbi] = mfma4(pa, wacc[kb][cbi][s4], qacc[ib][cbi]);
+                }
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 8; u++)
+        for (int rb = 0; rb < 4; rb++)
 #pragma unroll
-            for (int i = 0; i < KDA_CHUNK; i++) acc[i] = fmaf(sT[i * LDT + m0 + u], x[u], acc[i]);
+            for (int cbi = 0; cbi < 2; cbi++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    R[KDA_BR_QP + (16 * rb + 4 * gq + e) * KDA_DK + 32 * w + 16 * cbi + r16] = qacc[rb][cbi][e];
     }
-    float *dst = R + (half == 0 ? KDA_BR_W : KDA_BR_U);
-#pragma unroll
-    for (int i = 0; i < KDA_CHUNK; i++) dst[i * KDA_DK + c] = acc[i];
-    if (half == 0) {
-        /* Q'[i][c] = scale q^ e^G - sum_m P[i][m] W[m][c] */
-        float qp[KDA_CHUNK];
-#pragma unroll
-        for (int i = 0; i < KDA_CHUNK; i++) qp[i] = scale * sQ[i * LDK + c] * expf(sG[i * LDK + c]);
-        /* column c of W back from the record (this thread's own stores), eight rows per pass */
-#pragma unroll 1
-        for (int m0 = 0; m0 < KDA_CHUNK; m0 += 8) {
-            float wm[8];
-#pragma unroll
-            for (int u = 0; u < 8; u++) wm[u] = R[KDA_BR_W + (m0 + u) * KDA_DK + c];
-#pragma unroll
-            for (int u = 0; u < 8; u++)
-#pragma unroll
-                for (int i = 0; i < KDA_CHUNK; i++) qp[i] = fmaf(-sP[i * LDT + m0 + u], wm[u], qp[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < KDA_CHUNK; i++) R[KDA_BR_QP + i * KDA_DK + c] = qp[i];
-    } else {
-        const float gl = sG[(L - 1) * LDK + c];
-#pragma unroll
-        for (int i = 0; i < KDA_CHUNK; i++)
-            R[KDA_BR_KT + i * KDA_DK + c] = sK[i * LDK + c] * expf(gl - sG[i * LDK + c]);
-        R[KDA_BR_GL + c] = expf(gl);
+    for (int e = t; e < KDA_CHUNK * KDA_DK; e += NT) {
+        const int i = e >> 7, c = e & 127;
+        R[KDA_BR_KT + e] = sK[i * LDK + c] * expf(sG[(L - 1) * LDK + c] - sG[i * LDK + c]);
     }
+    if (t < KDA_DK) R[KDA_BR_GL + t] = expf(sG[(L - 1) * LDK + t]);
 }
 
 /* ------------------------------------------------------------------------- */
