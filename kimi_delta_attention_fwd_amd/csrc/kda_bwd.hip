@@ -343,7 +343,10 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
                 for (int cbi = 0; cbi < 2; cbi++) {
                     const int c = 32 * w + 16 * cbi + r16;
                     const float xw = sB[m] * sK[m * LDK + c] * expf(sG[m * LDK + c]);
-                    const float xu = m < L ? sB[m] * bf2f(v[((t0 + m) * H + h) * KDA_DV + c]) : 0.f;
+                    /* unconditional load from a row inside the chunk, then a select:
+                     * a load under a branch would wait for every outstanding load */
+                    const float vm = bf2f(v[((t0 + (m < L ? m : L - 1)) * H + h) * KDA_DV + c]);
+                    const float xu = m < L ? sB[m] * vm : 0.f;
 #pragma unroll
                     for (int rb = 0; rb < 4; rb++) {
                         wacc[rb][cbi] = mfma4(ta[rb], xw, wacc[rb][cbi]);
@@ -464,21 +467,33 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
                 sS[s_lds(r, r16)] = S[rb][e];
             }
         __syncthreads();
+        /* B operands read from LDS in one batch, then the MFMAs (four chains) */
+        float bs[32];
+#pragma unroll
+        for (int s = 0; s < 32; s++) bs[s] = sS[s_lds(32 * gq + s, r16)];
+        f32x4 dp[4] = {dacc, zero4(), zero4(), zero4()};
 #pragma unroll
         for (int s = 0; s < 32; s++) {
             const float4 f = wv[s >> 2];
             const float a = (s & 3) == 0 ? f.x : (s & 3) == 1 ? f.y : (s & 3) == 2 ? f.z : f.w;
-            dacc = mfma4(-a, sS[s_lds(32 * gq + s, r16)], dacc);
+            dp[s & 3] = mfma4(-a, bs[s], dp[s & 3]);
         }
+        dacc = (dp[0] + dp[1]) + (dp[2] + dp[3]);
 #pragma unroll
         for (int e = 0; e < 4; e++) sD[d_lds(16 * w + 4 * gq + e, r16)] = dacc[e];
         __syncthreads();
+        float bd[16];
+#pragma unroll
+        for (int s = 0; s < 16; s++) bd[s] = sD[d_lds(16 * gq + s, r16)];
 #pragma unroll
         for (int rb = 0; rb < 2; rb++) {
-            f32x4 acc = gl[rb] * S[rb];
+            f32x4 acc0 = gl[rb] * S[rb], acc1 = zero4();
 #pragma unroll
-            for (int s = 0; s < 16; s++) acc = mfma4(kt[rb][s], sD[d_lds(16 * gq + s, r16)], acc);
-            S[rb] = acc;
+            for (int s = 0; s < 16; s += 2) {
+                acc0 = mfma4(kt[rb][s], bd[s], acc0);
+                acc1 = mfma4(kt[rb][s + 1], bd[s + 1], acc1);
+            }
+            S[rb] = acc0 + acc1;
         }
     }
 
@@ -514,7 +529,10 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
 #pragma unroll
         for (int s = 0; s < 16; s++) {
             const int i = 16 * gq + s;
-            o[s] = i < L ? bf2f(dout[((row0 + c * KDA_CHUNK + i) * H + h) * KDA_DV + col]) : 0.f;
+            /* unconditional load from a row inside the chunk, then a select (a load under
+             * a branch would wait for every outstanding load) */
+            const float x = bf2f(dout[((row0 + c * KDA_CHUNK + (i < L ? i : L - 1)) * H + h) * KDA_DV + col]);
+            o[s] = i < L ? x : 0.f;
         }
 #pragma unroll
         for (int rb = 0; rb < 2; rb++)
@@ -529,25 +547,32 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
                 sS[s_lds(r, r16)] = dS[rb][e];
             }
         __syncthreads();
-        f32x4 dacc = zero4();
+        float bs[32];
+#pragma unroll
+        for (int s = 0; s < 32; s++) bs[s] = sS[s_lds(32 * gq + s, r16)];
+        f32x4 dp[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
         for (int s = 0; s < 32; s++) {
             const float4 f = kv[s >> 2];
             const float a = (s & 3) == 0 ? f.x : (s & 3) == 1 ? f.y : (s & 3) == 2 ? f.z : f.w;
-            dacc = mfma4(a, sS[s_lds(32 * gq + s, r16)], dacc);
+            dp[s & 3] = mfma4(a, bs[s], dp[s & 3]);
         }
+        const f32x4 dacc = (dp[0] + dp[1]) + (dp[2] + dp[3]);
 #pragma unroll
         for (int e = 0; e < 4; e++) sD[d_lds(16 * w + 4 * gq + e, r16)] = dacc[e];
         __syncthreads();
+        float bd[16];
+#pragma unroll
+        for (int s = 0; s < 16; s++) bd[s] = sD[d_lds(16 * gq + s, r16)];
 #pragma unroll
         for (int rb = 0; rb < 2; rb++) {
-            f32x4 acc = gl[rb] * dS[rb];
+            f32x4 acc0 = gl[rb] * dS[rb], acc1 = zero4();
 #pragma unroll
             for (int s = 0; s < 16; s++) {
-                acc = mfma4(-wt[rb][s], sD[d_lds(16 * gq + s, r16)], acc);
-                acc = mfma4(qt[rb][s], o[s], acc);
+                acc0 = mfma4(-wt[rb][s], bd[s], acc0);
+                acc1 = mfma4(qt[rb][s], o[s], acc1);
             }
-            dS[rb] = acc;
+            dS[rb] = acc0 + acc1;
         }
     }
     if (dinit != nullptr) {
@@ -611,10 +636,12 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
             for (int u = 0; u < 8; u++) {
                 const int e = e0 + u * NT, i = e >> 7, cc = e & 127;
                 const bool ok = i < L;
-                const int64_t row = ((t0 + i) * H + h) * KDA_DV + cc;
+                /* loads are unconditional (rows clamped into the chunk) and selected after */
+                const int64_t row = ((t0 + (ok ? i : L - 1)) * H + h) * KDA_DV + cc;
                 xb[u] = R[KDA_BR_BETA + i];
-                xo[u] = ok ? bf2f(dout[row]) : 0.f;
-                xv[u] = ok ? bf2f(v[row]) : 0.f;
+                const float fo = bf2f(dout[row]), fv = bf2f(v[row]);
+                xo[u] = ok ? fo : 0.f;
+                xv[u] = ok ? fv : 0.f;
                 xg[u] = R[KDA_BR_G + e];
                 xk[u] = R[KDA_BR_KN + e];
                 xu[u] = R[KDA_BR_U + e];
@@ -706,14 +733,15 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
                 float xdq[4], xkt[4], xdkt[4], xdxw[4], xdxu[4], xv[4];
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
-                    const int i = i0 + 2 * u, e = i * KDA_DK + c;
-                    const bool ok = i < L;
-                    xdq[u] = ok ? dQp[e] : 0.f;
-                    xkt[u] = ok ? R[KDA_BR_KT + e] : 0.f;
-                    xdkt[u] = ok ? dKt[e] : 0.f;
-                    xdxw[u] = ok ? dXW[e] : 0.f;
-                    xdxu[u] = ok ? dXU[e] : 0.f;
-                    xv[u] = ok ? bf2f(v[((t0 + i) * H + h) * KDA_DV + c]) : 0.f;
+                    /* unconditional loads from a row clamped into the chunk (rows past it
+                     * are not used) */
+                    const int i = i0 + 2 * u, ic = i < L ? i : L - 1, e = ic * KDA_DK + c;
+                    xdq[u] = dQp[e];
+                    xkt[u] = R[KDA_BR_KT + e];
+                    xdkt[u] = dKt[e];
+                    xdxw[u] = dXW[e];
+                    xdxu[u] = dXU[e];
+                    xv[u] = bf2f(v[((t0 + ic) * H + h) * KDA_DV + c]);
                 }
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
@@ -817,19 +845,26 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
             float xg[32], tot = 0.f;
 #pragma unroll
             for (int u = 0; u < 32; u++) {
-                xg[u] = u < n ? dG[(r0 + u) * KDA_DK + c] : 0.f;
+                const float x = dG[(r0 + u) * KDA_DK + c]; /* row < 64: always inside the scratch tile */
+                xg[u] = u < n ? x : 0.f;
                 tot += xg[u];
             }
             if (half == 1) sGL2[c] = tot;
             __syncthreads();
             float run = sGL[c] + (half == 0 ? sGL2[c] : 0.f), pdt = 0.f, pa = 0.f;
             const float bias = dt_bias[h * KDA_DK + c];
+            float xx[32]; /* gate inputs, loaded unconditionally from rows clamped into the chunk */
+#pragma unroll
+            for (int u = 0; u < 32; u++) {
+                const int ic = r0 + u < L ? r0 + u : L - 1;
+                xx[u] = bf2f(g[((t0 + ic) * H + h) * KDA_DK + c]);
+            }
 #pragma unroll
             for (int u = 31; u >= 0; u--) {
                 if (u < n) {
                     const int i = r0 + u;
                     run += xg[u];
-                    const float x = bf2f(g[((t0 + i) * H + h) * KDA_DK + c]) + bias;
+                    const float x = xx[u] + bias;
                     const float free_la = -rate * softplus_f(x);
                     const float dla = free_la < lower_bound ? 0.f : run;
                     const float dx = -dla * rate * sigmoid_f(x);
