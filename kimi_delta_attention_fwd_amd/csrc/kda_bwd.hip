@@ -409,6 +409,63 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
 __host__ __device__ constexpr int s_lds(int r, int j) { return r * 16 + (r >> 5) * 8 + j; }
 __host__ __device__ constexpr int d_lds(int i, int j) { return i * 16 + (i >> 4) * 8 + j; }
 
+/* one chunk's operands of the forward state pass, for lane (r16, gq) of wave w:
+ * W row 16 w + r16, columns 32 gq .. 32 gq + 31; K~[16 gq + s][16 (2 w + rb) + r16];
+ * U rows 16 w + 4 gq + e, column col; e^{G_L} of rows 16 (2 w + rb) + 4 gq + e */
+struct FwdOps {
+    float4 wv[8];
+    float kt[2][16];
+    f32x4 u, gl[2];
+};
+
+__device__ __forceinline__ void load_fwd(FwdOps &o, const float *R, int w, int gq, int r16, int col)
+{
+    const float *wrow = R + KDA_BR_W + (16 * w + r16) * KDA_DK + 32 * gq;
+#pragma unroll
+    for (int i = 0; i < 8; i++) o.wv[i] = *(const float4 *)(wrow + 4 * i);
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+        for (int s = 0; s < 16; s++) o.kt[rb][s] = R[KDA_BR_KT + (16 * gq + s) * KDA_DK + 16 * (2 * w + rb) + r16];
+#pragma unroll
+    for (int e = 0; e < 4; e++) o.u[e] = R[KDA_BR_U + (16 * w + 4 * gq + e) * KDA_DV + col];
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) o.gl[rb][e] = R[KDA_BR_GL + 16 * (2 * w + rb) + 4 * gq + e];
+}
+
+/* one chunk's early operands of the reverse pass: K~ row 16 w + r16, columns
+ * 32 gq .. 32 gq + 31; dout rows 16 gq + s (zero past the chunk's L rows; the
+ * load itself is unconditional, from a row clamped into the chunk, because a
+ * load under a branch waits for every outstanding load), column col; e^{G_L}
+ * of the lane's state rows */
+struct RevOps {
+    float4 kv[8];
+    float o[16];
+    f32x4 gl[2];
+};
+
+__device__ __forceinline__ void load_rev(RevOps &o, const float *R, const uint16_t *dout, int64_t row0, int64_t len,
+                                         int64_t c, int H, int h, int w, int gq, int r16, int col)
+{
+    const float *krow = R + KDA_BR_KT + (16 * w + r16) * KDA_DK + 32 * gq;
+#pragma unroll
+    for (int i = 0; i < 8; i++) o.kv[i] = *(const float4 *)(krow + 4 * i);
+    const int64_t rem = len - c * KDA_CHUNK;
+    const int L = (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
+#pragma unroll
+    for (int s = 0; s < 16; s++) {
+        const int i = 16 * gq + s;
+        const float x = bf2f(dout[((row0 + c * KDA_CHUNK + (i < L ? i : L - 1)) * H + h) * KDA_DV + col]);
+        o.o[s] = i < L ? x : 0.f;
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) o.gl[rb][e] = R[KDA_BR_GL + 16 * (2 * w + rb) + 4 * gq + e];
+}
+
 extern "C" __global__ void __launch_bounds__(NT)
 kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ cu,
                     const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
@@ -437,27 +494,14 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
                      : init_fp32 ? ((const float *)init)[o] : bf2f(((const uint16_t *)init)[o]);
         }
 
-    /* forward: S_c is stored, D = U - W S_c, S_{c+1} = diag(e^{G_L}) S_c + K~^T D */
-    for (int64_t c = 0; c < nchunk; c++) {
+    /* forward: S_c is stored, D = U - W S_c, S_{c+1} = diag(e^{G_L}) S_c + K~^T D.
+     * Two operand sets with fixed roles: the next chunk's are loaded while this one
+     * is computed. */
+    FwdOps opA, opB;
+    auto fwd_step = [&](const FwdOps &cur, FwdOps &nxt, int64_t c) {
         const int64_t item = (int64_t)h * nslots + slot0 + c;
-        const float *R = brec + item * KDA_BR_FLOATS;
         float *ck = ckpt + item * (int64_t)(KDA_DK * KDA_DV);
-        float4 wv[8];  /* W row 16 w + r16, columns 32 gq .. 32 gq + 31 */
-        float kt[2][16]; /* K~[16 gq + s][16 (2 w + rb) + r16] */
-        f32x4 dacc, gl[2];
-        const float *wrow = R + KDA_BR_W + (16 * w + r16) * KDA_DK + 32 * gq;
-#pragma unroll
-        for (int i = 0; i < 8; i++) wv[i] = *(const float4 *)(wrow + 4 * i);
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++)
-#pragma unroll
-            for (int s = 0; s < 16; s++) kt[rb][s] = R[KDA_BR_KT + (16 * gq + s) * KDA_DK + 16 * (2 * w + rb) + r16];
-#pragma unroll
-        for (int e = 0; e < 4; e++) dacc[e] = R[KDA_BR_U + (16 * w + 4 * gq + e) * KDA_DV + col];
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) gl[rb][e] = R[KDA_BR_GL + 16 * (2 * w + rb) + 4 * gq + e];
+        if (c + 1 < nchunk) load_fwd(nxt, brec + (item + 1) * KDA_BR_FLOATS, w, gq, r16, col);
 #pragma unroll
         for (int rb = 0; rb < 2; rb++)
 #pragma unroll
@@ -471,14 +515,14 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
         float bs[32];
 #pragma unroll
         for (int s = 0; s < 32; s++) bs[s] = sS[s_lds(32 * gq + s, r16)];
-        f32x4 dp[4] = {dacc, zero4(), zero4(), zero4()};
+        f32x4 dp[4] = {cur.u, zero4(), zero4(), zero4()};
 #pragma unroll
         for (int s = 0; s < 32; s++) {
-            const float4 f = wv[s >> 2];
+            const float4 f = cur.wv[s >> 2];
             const float a = (s & 3) == 0 ? f.x : (s & 3) == 1 ? f.y : (s & 3) == 2 ? f.z : f.w;
             dp[s & 3] = mfma4(-a, bs[s], dp[s & 3]);
         }
-        dacc = (dp[0] + dp[1]) + (dp[2] + dp[3]);
+        const f32x4 dacc = (dp[0] + dp[1]) + (dp[2] + dp[3]);
 #pragma unroll
         for (int e = 0; e < 4; e++) sD[d_lds(16 * w + 4 * gq + e, r16)] = dacc[e];
         __syncthreads();
@@ -487,18 +531,25 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
         for (int s = 0; s < 16; s++) bd[s] = sD[d_lds(16 * gq + s, r16)];
 #pragma unroll
         for (int rb = 0; rb < 2; rb++) {
-            f32x4 acc0 = gl[rb] * S[rb], acc1 = zero4();
+            f32x4 acc0 = cur.gl[rb] * S[rb], acc1 = zero4();
 #pragma unroll
             for (int s = 0; s < 16; s += 2) {
-                acc0 = mfma4(kt[rb][s], bd[s], acc0);
-                acc1 = mfma4(kt[rb][s + 1], bd[s + 1], acc1);
+                acc0 = mfma4(cur.kt[rb][s], bd[s], acc0);
+                acc1 = mfma4(cur.kt[rb][s + 1], bd[s + 1], acc1);
             }
             S[rb] = acc0 + acc1;
         }
+    };
+    if (nchunk > 0) load_fwd(opA, brec + ((int64_t)h * nslots + slot0) * KDA_BR_FLOATS, w, gq, r16, col);
+    for (int64_t c = 0; c < nchunk; c += 2) {
+        fwd_step(opA, opB, c);
+        if (c + 1 < nchunk) fwd_step(opB, opA, c + 1);
     }
 
     /* reverse: dS_{c+1} is stored, dD = K~ dS_{c+1},
-     * dS_c = diag(e^{G_L}) dS_{c+1} - W^T dD + Q'^T dout_c */
+     * dS_c = diag(e^{G_L}) dS_{c+1} - W^T dD + Q'^T dout_c. K~, dout and e^{G_L}
+     * are loaded one chunk ahead; W and Q' at the top of the chunk (they are first
+     * needed after the dD product). */
     f32x4 dS[2];
 #pragma unroll
     for (int rb = 0; rb < 2; rb++)
@@ -506,18 +557,12 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
         for (int e = 0; e < 4; e++)
             dS[rb][e] = dfinal == nullptr ? 0.f
                       : dfinal[sbase + (int64_t)(16 * (2 * w + rb) + 4 * gq + e) * KDA_DV + col];
-    for (int64_t c = nchunk - 1; c >= 0; c--) {
+    RevOps rA, rB;
+    auto rev_step = [&](const RevOps &rcur, RevOps &rnxt, int64_t c) {
         const int64_t item = (int64_t)h * nslots + slot0 + c;
         const float *R = brec + item * KDA_BR_FLOATS;
         float *dk = dse + item * (int64_t)(KDA_DK * KDA_DV);
-        const int64_t rem = len - c * KDA_CHUNK;
-        const int L = (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
-        float4 kv[8];  /* K~ row 16 w + r16, columns 32 gq .. 32 gq + 31 */
-        float wt[2][16], qt[2][16], o[16];
-        f32x4 gl[2];
-        const float *krow = R + KDA_BR_KT + (16 * w + r16) * KDA_DK + 32 * gq;
-#pragma unroll
-        for (int i = 0; i < 8; i++) kv[i] = *(const float4 *)(krow + 4 * i);
+        float wt[2][16], qt[2][16];
 #pragma unroll
         for (int rb = 0; rb < 2; rb++)
 #pragma unroll
@@ -526,18 +571,7 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
                 wt[rb][s] = R[KDA_BR_W + idx];
                 qt[rb][s] = R[KDA_BR_QP + idx];
             }
-#pragma unroll
-        for (int s = 0; s < 16; s++) {
-            const int i = 16 * gq + s;
-            /* unconditional load from a row inside the chunk, then a select (a load under
-             * a branch would wait for every outstanding load) */
-            const float x = bf2f(dout[((row0 + c * KDA_CHUNK + (i < L ? i : L - 1)) * H + h) * KDA_DV + col]);
-            o[s] = i < L ? x : 0.f;
-        }
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++)
-#pragma unroll
-            for (int e = 0; e < 4; e++) gl[rb][e] = R[KDA_BR_GL + 16 * (2 * w + rb) + 4 * gq + e];
+        if (c > 0) load_rev(rnxt, R - KDA_BR_FLOATS, dout, row0, len, c - 1, H, h, w, gq, r16, col);
 #pragma unroll
         for (int rb = 0; rb < 2; rb++)
 #pragma unroll
@@ -553,7 +587,7 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
         f32x4 dp[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
         for (int s = 0; s < 32; s++) {
-            const float4 f = kv[s >> 2];
+            const float4 f = rcur.kv[s >> 2];
             const float a = (s & 3) == 0 ? f.x : (s & 3) == 1 ? f.y : (s & 3) == 2 ? f.z : f.w;
             dp[s & 3] = mfma4(a, bs[s], dp[s & 3]);
         }
@@ -566,14 +600,21 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
         for (int s = 0; s < 16; s++) bd[s] = sD[d_lds(16 * gq + s, r16)];
 #pragma unroll
         for (int rb = 0; rb < 2; rb++) {
-            f32x4 acc0 = gl[rb] * dS[rb], acc1 = zero4();
+            f32x4 acc0 = rcur.gl[rb] * dS[rb], acc1 = zero4();
 #pragma unroll
             for (int s = 0; s < 16; s++) {
                 acc0 = mfma4(-wt[rb][s], bd[s], acc0);
-                acc1 = mfma4(qt[rb][s], o[s], acc1);
+                acc1 = mfma4(qt[rb][s], rcur.o[s], acc1);
             }
             dS[rb] = acc0 + acc1;
         }
+    };
+    if (nchunk > 0)
+        load_rev(rA, brec + ((int64_t)h * nslots + slot0 + nchunk - 1) * KDA_BR_FLOATS, dout, row0, len, nchunk - 1, H,
+                 h, w, gq, r16, col);
+    for (int64_t c = nchunk - 1; c >= 0; c -= 2) {
+        rev_step(rA, rB, c);
+        if (c > 0) rev_step(rB, rA, c - 1);
     }
     if (dinit != nullptr) {
 #pragma unroll
