@@ -121,3 +121,35 @@ def test_bwd_repeatable():
     a, b = run_bwd(d), run_bwd(d)
     for n in NAMES:
         assert np.array_equal(a[n], b[n]), n
+
+
+def test_bwd_long_prefill_sampled_head():
+    """The backward bench workload at full size (B=1, T=65536, H=32, lower_bound -3,
+    no initial state, the bench's seeded bf16 output gradient and fp32 final-state
+    gradient), run whole on the GPU in the bench's launch configuration; head 5 is
+    checked against the oracle run on that head alone (heads are independent)."""
+    d = ki.config_inputs(3)
+    B, T, H, N = d["B"], d["T"], d["H"], d["N"]
+    rng = np.random.default_rng(1234)
+    dout = ki.f32_to_bf16_bits(rng.standard_normal((B, T, H, 128), dtype=np.float32))
+    dfin = rng.standard_normal((N, H, 128, 128), dtype=np.float32) * np.float32(0.1)
+    t = dev_inputs(d)
+    print("kda_bwd long prefill B=%d T=%d H=%d" % (B, T, H), flush=True)
+    gr = kda.bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], to_dev_bf16(dout), t["A_log"],
+                 t["dt_bias"], d["lower_bound"], initial_state=None, dfinal_state=to_dev(dfin))
+    torch.cuda.synchronize()
+    h0 = 5
+    got = {n: gr[n][:, :, h0:h0 + 1].cpu().numpy().astype(np.float64) for n in ("dq", "dk", "dv", "dg", "dbeta")}
+    got["dA_log"] = gr["dA_log"][h0:h0 + 1].cpu().numpy().astype(np.float64)
+    got["ddt_bias"] = gr["ddt_bias"][h0:h0 + 1].cpu().numpy().astype(np.float64)
+    got["dinitial_state"] = gr["dinitial_state"][:, h0:h0 + 1].cpu().numpy().astype(np.float64)
+    del gr, t
+    d1 = dict(d)
+    for key in ("q", "k", "v", "g", "beta"):
+        d1[key] = np.ascontiguousarray(d[key][:, :, h0:h0 + 1])
+    d1["A_log"] = np.ascontiguousarray(d["A_log"][h0:h0 + 1])
+    d1["dt_bias"] = np.ascontiguousarray(d["dt_bias"][h0:h0 + 1])
+    d1["H"] = 1
+    d1["dout"] = np.ascontiguousarray(dout[:, :, h0:h0 + 1])
+    d1["dfinal"] = np.ascontiguousarray(dfin[:, h0:h0 + 1])
+    compare(d1, got, run_oracle(d1))
