@@ -70,77 +70,125 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4 &c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-/* x[s] = p[s * STRIDE] for s < 16; p is 16-byte aligned when STRIDE is 1 */
+/* x[s] = p[s * STRIDE] for s < 8; p is 16-byte aligned when STRIDE is 1 */
 template <int STRIDE>
-__device__ __forceinline__ void load16(float *x, const float *p)
+__device__ __forceinline__ void load8(float *x, const float *p)
 {
     if (STRIDE == 1) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
+        for (int i = 0; i < 2; i++) {
             const float4 f = *(const float4 *)(p + 4 * i);
             x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
         }
     } else {
 #pragma unroll
-        for (int s = 0; s < 16; s++) x[s] = p[s * STRIDE];
+        for (int s = 0; s < 8; s++) x[s] = p[s * STRIDE];
     }
 }
 
+/* one 32-wide contraction slice of wg_gemm's operands for this lane (see wg_gemm) */
+template <bool TA, bool TB, int NBW, int lda, int ldb>
+__device__ __forceinline__ void wg_load_slice(float (&a)[2][8], float (&b)[NBW][8], const float *A, const float *B,
+                                              int sl, int gq, int r16, int rb0, int cb0)
+{
+    const int kb = 32 * sl + 8 * gq;
+#pragma unroll
+    for (int rb = 0; rb < 2; rb++) {
+        const int i = 16 * (rb0 + rb) + r16;
+        if (TA) load8<lda>(a[rb], A + kb * lda + i);
+        else load8<1>(a[rb], A + i * lda + kb);
+    }
+#pragma unroll
+    for (int cb = 0; cb < NBW; cb++) {
+        const int j = 16 * (cb0 + cb) + r16;
+        if (TB) load8<1>(b[cb], B + j * ldb + kb);
+        else load8<ldb>(b[cb], B + kb * ldb + j);
+    }
+}
+
+template <int NBW>
+__device__ __forceinline__ void wg_mma_slice(f32x4 (&d)[2][NBW], const float (&a)[2][8], const float (&b)[NBW][8])
+{
+#pragma unroll
+    for (int s = 0; s < 8; s++)
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int cb = 0; cb < NBW; cb++) d[rb][cb] = mfma4(a[rb][s], b[cb][s], d[rb][cb]);
+}
+
 /* C[i][j] = (acc ? C[i][j] : 0) + alpha * sum_k a(i, k) b(k, j) for i < 64, j < N,
- * with a(i, k) = TA ? A[k][i] : A[i][k] and b(k, j) = TB ? B[j][k] : B[k][j], on fp32 MFMA (16 x 16 x 4 blocks). Wave w holds
- * row blocks 2 (w % 2) + {0, 1} and N / 32 column blocks starting at
- * (w / 2) N / 32; in each 64-wide slice of the contraction, lane group gq
- * (lanes 16 gq .. 16 gq + 15) takes contraction indices 16 gq .. 16 gq + 15, so
- * operands contiguous along it load as 16-byte pieces. Every row stride and
- * base is a multiple of 4 floats. Callers separate products that share an
- * output or read one another's output with a barrier. */
+ * with a(i, k) = TA ? A[k][i] : A[i][k] and b(k, j) = TB ? B[j][k] : B[k][j], on fp32 MFMA
+ * (16 x 16 x 4 blocks). Wave w holds row blocks 2 (w % 2) + {0, 1} and N / 32 column
+ * blocks starting at (w / 2) N / 32. The contraction runs in 32-wide slices: in slice
+ * sl, lane group gq (lanes 16 gq .. 16 gq + 15) takes indices 32 sl + 8 gq + s at step
+ * s < 8, so operands contiguous along it load as 16-byte pieces. The next slice's
+ * operands are loaded while the current one is multiplied, and scheduling barriers
+ * keep each slice's loads together ahead of the MFMAs that wait for them (left to
+ * itself the scheduler sinks loads next to their uses, and each such load then waits
+ * for every outstanding memory operation). Every row stride and base is a multiple
+ * of 4 floats. Callers separate products that share an output or read one another's
+ * output with a barrier. */
 template <bool TA, bool TB, int N, int KD>
 __device__ __forceinline__ void wg_gemm(float *C, const float *A, const float *B, float alpha, bool acc)
 {
-    static_assert(N % 32 == 0 && KD % 64 == 0, "block shape");
+    static_assert(N % 32 == 0 && KD % 32 == 0, "block shape");
     /* dense row-major operands: A is [64][KD] ([KD][64] if TA), B is [KD][N] ([N][KD] if TB), C is [64][N] */
     constexpr int lda = TA ? 64 : KD, ldb = TB ? KD : N, ldc = N;
-    constexpr int NBW = N / 32;
-    const int l = threadIdx.x & 63, w = threadIdx.x >> 6, gq = l >> 4, r16 = l & 15;
+    constexpr int NBW = N / 32, NSL = KD / 32;
+    /* the lane index is made opaque here, so the per-lane operand offsets are
+     * computed at each product instead of being hoisted out of the item loop,
+     * where they would hold hundreds of registers */
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int l = tid & 63, w = tid >> 6, gq = l >> 4, r16 = l & 15;
     const int rb0 = 2 * (w & 1), cb0 = (w >> 1) * NBW;
-    __builtin_amdgcn_sched_barrier(0); /* products are not interleaved: each holds 128 registers */
+    __builtin_amdgcn_sched_barrier(0);
     f32x4 d[2][NBW];
 #pragma unroll
     for (int rb = 0; rb < 2; rb++)
 #pragma unroll
         for (int cb = 0; cb < NBW; cb++) d[rb][cb] = zero4();
-#pragma unroll 1
-    for (int kc = 0; kc < KD; kc += 64) {
-        const int kb = kc + 16 * gq;
-        float a[2][16], b[NBW][16];
+    /* two operand sets, used for even and odd slices */
+    float a0[2][8], b0[NBW][8], a1[2][8], b1[NBW][8];
+    wg_load_slice<TA, TB, NBW, lda, ldb>(a0, b0, A, B, 0, gq, r16, rb0, cb0);
 #pragma unroll
-        for (int rb = 0; rb < 2; rb++) {
-            const int i = 16 * (rb0 + rb) + r16;
-            if (TA) load16<lda>(a[rb], A + kb * lda + i);
-            else load16<1>(a[rb], A + i * lda + kb);
+    for (int sl = 0; sl < NSL; sl++) {
+        if (sl + 1 < NSL) {
+            if ((sl & 1) == 0) wg_load_slice<TA, TB, NBW, lda, ldb>(a1, b1, A, B, sl + 1, gq, r16, rb0, cb0);
+            else wg_load_slice<TA, TB, NBW, lda, ldb>(a0, b0, A, B, sl + 1, gq, r16, rb0, cb0);
         }
-#pragma unroll
-        for (int cb = 0; cb < NBW; cb++) {
-            const int j = 16 * (cb0 + cb) + r16;
-            if (TB) load16<1>(b[cb], B + j * ldb + kb);
-            else load16<ldb>(b[cb], B + kb * ldb + j);
-        }
-#pragma unroll
-        for (int s = 0; s < 16; s++)
-#pragma unroll
-            for (int rb = 0; rb < 2; rb++)
-#pragma unroll
-                for (int cb = 0; cb < NBW; cb++) d[rb][cb] = mfma4(a[rb][s], b[cb][s], d[rb][cb]);
+        __builtin_amdgcn_sched_barrier(0);
+        if ((sl & 1) == 0) wg_mma_slice<NBW>(d, a0, b0);
+        else wg_mma_slice<NBW>(d, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    if (acc) {
+        /* all of this wave's C elements read before any is written back */
+        float cv[2][NBW][4];
 #pragma unroll
-    for (int rb = 0; rb < 2; rb++)
+        for (int rb = 0; rb < 2; rb++)
 #pragma unroll
-        for (int cb = 0; cb < NBW; cb++)
+            for (int cb = 0; cb < NBW; cb++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                float *c = C + (16 * (rb0 + rb) + 4 * gq + e) * ldc + 16 * (cb0 + cb) + r16;
-                *c = acc ? *c + alpha * d[rb][cb][e] : alpha * d[rb][cb][e];
-            }
+                for (int e = 0; e < 4; e++) cv[rb][cb][e] = C[(16 * (rb0 + rb) + 4 * gq + e) * ldc + 16 * (cb0 + cb) + r16];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int cb = 0; cb < NBW; cb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    C[(16 * (rb0 + rb) + 4 * gq + e) * ldc + 16 * (cb0 + cb) + r16] = fmaf(alpha, d[rb][cb][e], cv[rb][cb][e]);
+    } else {
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int cb = 0; cb < NBW; cb++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    C[(16 * (rb0 + rb) + 4 * gq + e) * ldc + 16 * (cb0 + cb) + r16] = alpha * d[rb][cb][e];
+    }
     __builtin_amdgcn_sched_barrier(0);
 }
 
