@@ -859,18 +859,82 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         }
         __syncthreads();
 
+        /* s8a: the pairwise sums over partners in other 16-row blocks, on fp32 MFMA.
+         * With the factor split at a block boundary (anchor row a, value G_a),
+         * e^{G_i - G_j} = e^{G_i - G_a} e^{G_a - G_j}, both factors <= 1 for j <= a < i:
+         *   row side, row block ib >= 1, a = 16 ib - 1:
+         *     SA_off[i] = e^{G_i - G_a} sum_{j <= a} dA_ij (k^_j e^{G_a - G_j}), SP_off likewise
+         *     with scale dP;
+         *   column side, block jb <= 2, a = 16 jb + 15:
+         *     CT_off[j] = e^{G_a - G_j} sum_{i > a} (dA_ij beta_i k^_i + scale dP_ij q^_i) e^{G_i - G_a}.
+         * Wave w takes channels 32 w .. 32 w + 31 (two 16-column blocks); the contraction
+         * index at step s of lane group gq is k0 + gq. Results go to scratch arrays no
+         * longer needed (D, dD, dW) as SA_off, SP_off, CT_off; rows without such
+         * partners get 0. Exponents are in log2 units and clamped at 0. */
+        {
+            float *OA = D, *OP = dD, *OC = dW;
+            int tid = t;
+            asm volatile("" : "+v"(tid));
+            const int w = tid >> 6, l = tid & 63, gq = l >> 4, r16 = l & 15;
+#pragma unroll
+            for (int cbi = 0; cbi < 2; cbi++) {
+                const int cc = 32 * w + 16 * cbi + r16;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    OA[(4 * gq + e) * KDA_DK + cc] = 0.f;
+                    OP[(4 * gq + e) * KDA_DK + cc] = 0.f;
+                    OC[(48 + 4 * gq + e) * KDA_DK + cc] = 0.f;
+                }
+                for (int ib = 1; ib < 4; ib++) {
+                    const float ga = sG[(16 * ib - 1) * LDK + cc];
+                    f32x4 sa = zero4(), sp = zero4();
+                    for (int k0 = 0; k0 < 16 * ib; k0 += 4) {
+                        const int j = k0 + gq;
+                        const float bv = sK[j * LDK + cc] * exp2_fast(fminf(ga - sG[j * LDK + cc], 0.f));
+                        sa = mfma4(sdA[(16 * ib + r16) * LDT + j], bv, sa);
+                        sp = mfma4(sdP[(16 * ib + r16) * LDT + j], bv, sp);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int i = 16 * ib + 4 * gq + e;
+                        const float f = exp2_fast(fminf(sG[i * LDK + cc] - ga, 0.f));
+                        OA[i * KDA_DK + cc] = sa[e] * f;
+                        OP[i * KDA_DK + cc] = sp[e] * f;
+                    }
+                }
+                for (int jb = 0; jb < 3; jb++) {
+                    const float ga = sG[(16 * jb + 15) * LDK + cc];
+                    f32x4 ct = zero4();
+                    for (int k0 = 16 * (jb + 1); k0 < KDA_CHUNK; k0 += 4) {
+                        const int i = k0 + gq;
+                        const float f = exp2_fast(fminf(sG[i * LDK + cc] - ga, 0.f));
+                        ct = mfma4(sdA[i * LDT + 16 * jb + r16], sBeta[i] * sK[i * LDK + cc] * f, ct);
+                        ct = mfma4(sdP[i * LDT + 16 * jb + r16], sQ[i * LDK + cc] * f, ct);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const int j = 16 * jb + 4 * gq + e;
+                        OC[j * KDA_DK + cc] = ct[e] * exp2_fast(fminf(ga - sG[j * LDK + cc], 0.f));
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
         /* s8: pairwise factors, row side: rows i of parity half, j <= i. With
          * E = e^{G_i - G_j} per channel, SA = sum_j dA_ij k^_j E and SP = sum_j scale dP_ij k^_j E
          * give every row-side term: d k^_i += beta_i SA, d q^_i += SP,
-         * dG_i += beta_i k^_i SA + q^_i SP, and the d beta partial k^_i SA */
+         * dG_i += beta_i k^_i SA + q^_i SP, and the d beta partial k^_i SA. Partners in
+         * the row's own 16-row block are summed here, the rest come from s8a. */
         for (int i = half; i < L; i += 2) {
             const int e = i * KDA_DK + c;
             const float g0 = dG[e], k0 = dkn[e], q0 = dqn[e], b0 = XU[e];
             const float gi = sG[i * LDK + c];
-            float sa = 0.f, sp = 0.f;
-            /* blocks of 8 partners with all LDS reads first; partners past i have
+            float sa = D[e], sp = dD[e];
+            /* two blocks of 8 partners with all LDS reads first; partners past i have
              * dA = dP = 0 there and a clamped (finite) factor, so they add exactly 0 */
-            for (int j0 = 0; j0 <= i; j0 += 8) {
+#pragma unroll
+            for (int j0 = (i & ~15); j0 < (i & ~15) + 16; j0 += 8) {
                 float xg[8], xk[8], xa[8], xp[8];
 #pragma unroll
                 for (int u = 0; u < 8; u++) {
@@ -895,15 +959,17 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         __syncthreads();
 
         /* s9: pairwise factors, column side: rows j of parity half, i >= j:
-         * CT = sum_i (dA_ij beta_i k^_i + scale dP_ij q^_i) E; d k^_j += CT, dG_j -= k^_j CT */
+         * CT = sum_i (dA_ij beta_i k^_i + scale dP_ij q^_i) E; d k^_j += CT, dG_j -= k^_j CT.
+         * Rows i in the row's own 16-row block are summed here, the rest come from s8a. */
         for (int jj = half; jj < L; jj += 2) {
             const int e = jj * KDA_DK + c;
             const float g0 = dG[e], k0 = dkn[e];
             const float gj = sG[jj * LDK + c], knj = sK[jj * LDK + c];
-            float ct = 0.f;
-            /* blocks of 8 rows from the one holding jj, LDS reads first; rows before jj
-             * or past the chunk have dA = dP = 0 there and add exactly 0 */
-            for (int i0 = jj & ~7; i0 < L; i0 += 8) {
+            float ct = dW[e];
+            /* two blocks of 8 rows, LDS reads first; rows before jj or past the chunk
+             * have dA = dP = 0 there and add exactly 0 */
+#pragma unroll
+            for (int i0 = (jj & ~15); i0 < (jj & ~15) + 16; i0 += 8) {
                 float xg[8], xk[8], xq[8], xb[8], xa[8], xp[8];
 #pragma unroll
                 for (int u = 0; u < 8; u++) {
