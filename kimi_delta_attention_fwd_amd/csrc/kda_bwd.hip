@@ -285,23 +285,51 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
     }
     __syncthreads();
 
-    /* 3. A (j < i) and P (j <= i) over the 2080 lower-triangle pairs */
-    for (int e = t; e < KDA_CHUNK * (KDA_CHUNK + 1) / 2; e += NT) {
-        int i = (int)((sqrtf(8.f * (float)e + 1.f) - 1.f) * 0.5f);
-        while (i * (i + 1) / 2 > e) i--;
-        while ((i + 1) * (i + 2) / 2 <= e) i++;
-        const int j = e - i * (i + 1) / 2;
+    /* 3. A (j < i) and P (j <= i). Pairs inside the four diagonal 16 x 16 blocks
+     *    (136 each) element by element; the six blocks below them on fp32 MFMA with
+     *    the decay split at the end of the block before row i's (anchor a, G_a):
+     *      A_ij = beta_i sum_c (k^_ic e^{G_ic - G_ac}) (k^_jc e^{G_ac - G_jc}),
+     *      P_ij = scale sum_c (q^_ic e^{G_ic - G_ac}) (k^_jc e^{G_ac - G_jc}),
+     *    both factors <= 1 for j <= a < i. Rows past the chunk have k^ = q^ = 0. */
+    for (int e = t; e < 4 * 136; e += NT) {
+        const int bd = e / 136, r = e - bd * 136;
+        int ii = (int)((sqrtf(8.f * (float)r + 1.f) - 1.f) * 0.5f);
+        while (ii * (ii + 1) / 2 > r) ii--;
+        while ((ii + 1) * (ii + 2) / 2 <= r) ii++;
+        const int i = 16 * bd + ii, j = 16 * bd + r - ii * (ii + 1) / 2;
         float a = 0.f, p = 0.f;
-        if (i < L) {
-            for (int c = 0; c < KDA_DK; c++) {
-                const float E = exp2_fast((sG[i * LDK + c] - sG[j * LDK + c]) * LOG2E_F);
-                const float kj = sK[j * LDK + c] * E;
-                a = fmaf(sK[i * LDK + c], kj, a);
-                p = fmaf(sQ[i * LDK + c], kj, p);
-            }
+        for (int c = 0; c < KDA_DK; c++) {
+            const float E = exp2_fast((sG[i * LDK + c] - sG[j * LDK + c]) * LOG2E_F);
+            const float kj = sK[j * LDK + c] * E;
+            a = fmaf(sK[i * LDK + c], kj, a);
+            p = fmaf(sQ[i * LDK + c], kj, p);
         }
         sA[i * LDT + j] = j < i ? sB[i] * a : 0.f;
         sP[i * LDT + j] = scale * p;
+    }
+    {
+        /* block (ib, jb), jb < ib: list index w and w + 4 per wave */
+        const int w = t >> 6, l = t & 63, gq = l >> 4, r16 = l & 15;
+        for (int bi = w; bi < 6; bi += 4) {
+            const int ib = bi == 0 ? 1 : bi < 3 ? 2 : 3;
+            const int jb = bi == 0 ? 0 : bi < 3 ? bi - 1 : bi - 3;
+            const int ia = 16 * ib - 1, i = 16 * ib + r16, j = 16 * jb + r16;
+            f32x4 accA = zero4(), accP = zero4();
+            for (int c0 = 0; c0 < KDA_DK; c0 += 4) {
+                const int c = c0 + gq;
+                const float ga = sG[ia * LDK + c];
+                const float fi = exp2_fast(fminf(sG[i * LDK + c] - ga, 0.f) * LOG2E_F);
+                const float bj = sK[j * LDK + c] * exp2_fast(fminf(ga - sG[j * LDK + c], 0.f) * LOG2E_F);
+                accA = mfma4(sK[i * LDK + c] * fi, bj, accA);
+                accP = mfma4(sQ[i * LDK + c] * fi, bj, accP);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int ro = 16 * ib + 4 * gq + e;
+                sA[ro * LDT + j] = sB[ro] * accA[e];
+                sP[ro * LDT + j] = scale * accP[e];
+            }
+        }
     }
     __syncthreads();
 
