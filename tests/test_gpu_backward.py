@@ -123,22 +123,27 @@ def test_bwd_repeatable():
         assert np.array_equal(a[n], b[n]), n
 
 
-def test_bwd_long_prefill_sampled_head():
-    """The backward bench workload at full size (B=1, T=65536, H=32, lower_bound -3,
-    no initial state, the bench's seeded bf16 output gradient and fp32 final-state
-    gradient), run whole on the GPU in the bench's launch configuration; head 5 is
-    checked against the oracle run on that head alone (heads are independent)."""
-    d = ki.config_inputs(3)
+@pytest.mark.parametrize("cfg,h0", [(3, 5), (2, 17)])
+def test_bwd_full_size_sampled_head(cfg, h0):
+    """Backward workloads at full size, run whole on the GPU in the launch
+    configuration of `bench.py --backward --config cfg` (the bench's seeded bf16
+    output gradient and fp32 final-state gradient): the long prefill (B=1,
+    T=65536, H=32, lower_bound -3, no initial state) and the varlen batch (16
+    packed sequences, 66,399 tokens, H=32, bf16 initial state). Head h0 is checked
+    against the oracle run on that head alone (heads are independent)."""
+    d = ki.config_inputs(cfg)
     B, T, H, N = d["B"], d["T"], d["H"], d["N"]
     rng = np.random.default_rng(1234)
     dout = ki.f32_to_bf16_bits(rng.standard_normal((B, T, H, 128), dtype=np.float32))
     dfin = rng.standard_normal((N, H, 128, 128), dtype=np.float32) * np.float32(0.1)
+    if not d["final"]:
+        dfin = None
     t = dev_inputs(d)
-    print("kda_bwd long prefill B=%d T=%d H=%d" % (B, T, H), flush=True)
+    print("kda_bwd %s B=%d T=%d H=%d N=%d" % (d["name"], B, T, H, N), flush=True)
     gr = kda.bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], to_dev_bf16(dout), t["A_log"],
-                 t["dt_bias"], d["lower_bound"], initial_state=None, dfinal_state=to_dev(dfin))
+                 t["dt_bias"], d["lower_bound"], initial_state=t["initial_state"],
+                 dfinal_state=None if dfin is None else to_dev(dfin), cu_seqlens=t["cu_seqlens"])
     torch.cuda.synchronize()
-    h0 = 5
     got = {n: gr[n][:, :, h0:h0 + 1].cpu().numpy().astype(np.float64) for n in ("dq", "dk", "dv", "dg", "dbeta")}
     got["dA_log"] = gr["dA_log"][h0:h0 + 1].cpu().numpy().astype(np.float64)
     got["ddt_bias"] = gr["ddt_bias"][h0:h0 + 1].cpu().numpy().astype(np.float64)
@@ -150,6 +155,8 @@ def test_bwd_long_prefill_sampled_head():
     d1["A_log"] = np.ascontiguousarray(d["A_log"][h0:h0 + 1])
     d1["dt_bias"] = np.ascontiguousarray(d["dt_bias"][h0:h0 + 1])
     d1["H"] = 1
+    if d["initial_state"] is not None:
+        d1["initial_state"] = np.ascontiguousarray(d["initial_state"][:, h0:h0 + 1])
     d1["dout"] = np.ascontiguousarray(dout[:, :, h0:h0 + 1])
-    d1["dfinal"] = np.ascontiguousarray(dfin[:, h0:h0 + 1])
+    d1["dfinal"] = None if dfin is None else np.ascontiguousarray(dfin[:, h0:h0 + 1])
     compare(d1, got, run_oracle(d1))
