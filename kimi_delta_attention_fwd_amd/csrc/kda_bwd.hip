@@ -9,9 +9,11 @@
  * arithmetic is fp32: the matrix products of the scan and of the gradient
  * kernel on fp32 MFMA (v_mfma_f32_16x16x4f32), the rest on the vector ALUs:
  *
- *   kda_bwd_chunk_kernel  one workgroup per (chunk, head): q^, k^, log a, G, A, P,
- *                         T = (I + A)^-1 (forward substitution), W, U, Q', K~,
- *                         e^{G_L}, stored as fp32 per-chunk areas.
+ *   kda_bwd_chunk_kernel  one workgroup per (chunk, head): q^, k^, log a, G, A, P
+ *                         (16 x 16 blocks below the diagonal on MFMA with the decay
+ *                         split at a block boundary, diagonal blocks per element),
+ *                         T = (I + A)^-1 (forward substitution by 16-row blocks),
+ *                         W, U, Q' (MFMA), K~, e^{G_L}, stored as fp32 per-chunk areas.
  *   kda_bwd_scan_kernel   one workgroup per (sequence, head, 16 value columns),
  *                         fp32 MFMA; value columns are independent in both directions:
  *                         forward  S <- diag(e^{G_L}) S + K~^T (U - W S), storing S
@@ -24,8 +26,10 @@
  *                         dP = dout U^T - dQ' W^T, dU = P^T dout + dD (dD = K~ dS,
  *                         D = U - W S), then through W = T X_W, U = T X_U,
  *                         dA = -T^T dT T^T, the pairwise decay factors
- *                         e^{G_i - G_j} (<= 1, formed per element), the in-chunk
- *                         cumsum, the gate and the L2 norms.
+ *                         e^{G_i - G_j} (<= 1; partners in other 16-row blocks on
+ *                         MFMA with the factor split at a block boundary, own-block
+ *                         partners per element), the in-chunk cumsum, the gate and
+ *                         the L2 norms.
  *   kda_bwd_reduce_kernel sums the per-chunk gate partials of each head into
  *                         d A_log and d dt_bias (fixed order: deterministic).
  */
