@@ -404,6 +404,13 @@ def run_backward(args):
     kda.profile_enable(False)
     prof = kda.profile_read()
     kern = {name: ms / n for name, (ms, n) in prof.items()}
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     units = ki.token_heads(d)
     grad_ms = kern["kda_bwd_grad"]
     achieved = units * BWD_GRAD_FLOPS_PER_TH / (grad_ms * 1e-3) / 1e12

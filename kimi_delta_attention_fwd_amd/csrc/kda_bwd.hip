@@ -554,8 +554,12 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
                     float *__restrict__ dinit)
 {
     __shared__ float sS[s_lds(127, 15) + 1], sD[d_lds(63, 15) + 1];
-    const int tile = blockIdx.x & 7;
-    const int64_t chain = blockIdx.x >> 3;
+    /* XCD-aware: consecutive workgroups go to the 8 XCDs in turn, so the 8 value
+     * tiles of chain c are workgroups 64 (c / 8) + 8 tile + c % 8, all on XCD c % 8,
+     * and read each chunk's operands through one L2 */
+    const int64_t bq = blockIdx.x >> 3;
+    const int tile = (int)(bq & 7);
+    const int64_t chain = (bq >> 3) * 8 + (blockIdx.x & 7);
     const int64_t seq = chain / H;
     const int h = (int)(chain - seq * H);
     if (seq >= nseq) return;
@@ -1172,7 +1176,7 @@ extern "C" hipError_t kda_launch_bwd(int stage, const void *q, const void *k, co
                            (int)H, nslots, brec);
         break;
     case 1:
-        hipLaunchKernelGGL(kda_bwd_scan_kernel, dim3((unsigned)(nseq * H * 8)), dim3(NT), 0, st, brec, cu,
+        hipLaunchKernelGGL(kda_bwd_scan_kernel, dim3((unsigned)((nseq * H + 7) / 8 * 64)), dim3(NT), 0, st, brec, cu,
                            chunk_off, nseq, T, (int)H, nslots, init, init_fp32, dfinal, (const uint16_t *)dout,
                            ckpt, dse, dinit);
         break;
