@@ -38,7 +38,8 @@
 
 namespace {
 
-constexpr int NT = 256;   /* threads of every backward workgroup */
+constexpr int NT = 256;   /* threads of the chunk and scan workgroups */
+constexpr int NTG = 512;  /* threads of a gradient workgroup (eight waves) */
 constexpr int LDK = 129;  /* padded LDS row stride of [64][128] arrays */
 constexpr int LDT = 65;   /* padded LDS row stride of [64][64] arrays  */
 
@@ -123,8 +124,8 @@ __device__ __forceinline__ void wg_mma_slice(f32x4 (&d)[2][NBW], const float (&a
 
 /* C[i][j] = (acc ? C[i][j] : 0) + alpha * sum_k a(i, k) b(k, j) for i < 64, j < N,
  * with a(i, k) = TA ? A[k][i] : A[i][k] and b(k, j) = TB ? B[j][k] : B[k][j], on fp32 MFMA
- * (16 x 16 x 4 blocks). Wave w holds row blocks 2 (w % 2) + {0, 1} and N / 32 column
- * blocks starting at (w / 2) N / 32. The contraction runs in 32-wide slices: in slice
+ * (16 x 16 x 4 blocks), by the eight waves of a gradient workgroup. Wave w holds row
+ * blocks 2 (w % 2) + {0, 1} and N / 64 column blocks starting at (w / 2) N / 64. The contraction runs in 32-wide slices: in slice
  * sl, lane group gq (lanes 16 gq .. 16 gq + 15) takes indices 32 sl + 8 gq + s at step
  * s < 8, so operands contiguous along it load as 16-byte pieces. The next slice's
  * operands are loaded while the current one is multiplied, and scheduling barriers
@@ -136,10 +137,10 @@ __device__ __forceinline__ void wg_mma_slice(f32x4 (&d)[2][NBW], const float (&a
 template <bool TA, bool TB, int N, int KD>
 __device__ __forceinline__ void wg_gemm(float *C, const float *A, const float *B, float alpha, bool acc)
 {
-    static_assert(N % 32 == 0 && KD % 32 == 0, "block shape");
+    static_assert(N % 64 == 0 && KD % 32 == 0, "block shape");
     /* dense row-major operands: A is [64][KD] ([KD][64] if TA), B is [KD][N] ([N][KD] if TB), C is [64][N] */
     constexpr int lda = TA ? 64 : KD, ldb = TB ? KD : N, ldc = N;
-    constexpr int NBW = N / 32, NSL = KD / 32;
+    constexpr int NBW = N / 64, NSL = KD / 32;
     /* the lane index is made opaque here, so the per-lane operand offsets are
      * computed at each product instead of being hoisted out of the item loop,
      * where they would hold hundreds of registers */
@@ -713,7 +714,7 @@ kda_bwd_scan_kernel(const float *__restrict__ brec, const int32_t *__restrict__ 
 /* gradients of one (chunk, head) per loop trip; grid <= KDA_BWD_GRAD_WGS,     */
 /* each workgroup with its own KDA_BWD_SCR_FLOATS of scratch                   */
 /* ------------------------------------------------------------------------- */
-extern "C" __global__ void __launch_bounds__(NT)
+extern "C" __global__ void __launch_bounds__(NTG)
 kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__ g,
                     const uint16_t *__restrict__ dout, const float *__restrict__ A_log,
                     const float *__restrict__ dt_bias, float scale, float lower_bound,
@@ -725,11 +726,13 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
 {
     __shared__ float sG[KDA_CHUNK * LDK], sK[KDA_CHUNK * LDK], sQ[KDA_CHUNK * LDK];
     __shared__ float sdA[KDA_CHUNK * LDT], sdP[KDA_CHUNK * LDT];
-    __shared__ float sBeta[KDA_CHUNK], sGL[KDA_DK], sGL2[KDA_DK], sRed[KDA_DK], sX[2 * KDA_DK];
+    __shared__ float sBeta[KDA_CHUNK], sGL[KDA_DK], sRed[KDA_DK];
+    __shared__ float sQx[3][KDA_DK], sTot[4][KDA_DK], sX[3][2][KDA_DK]; /* row-quarter exchanges */
 
     float *const scr0 = scratch + (size_t)blockIdx.x * KDA_BWD_SCR_FLOATS;
 
-    const int t = threadIdx.x, c = t & 127, half = t >> 7;
+    /* thread t: channel c = t % 128 and row quarter qtr = t / 128 in the per-element phases */
+    const int t = threadIdx.x, c = t & 127, qtr = t >> 7;
     const int64_t nitems = (int64_t)H * nslots;
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
         const int h = (int)(item / nslots);
@@ -755,11 +758,11 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         /* s0: dout, X_W, X_U, D <- U; LDS copies of G (in log2 units), k^ and q^. Eight
          * elements per pass with all their loads issued before any store (the scratch
          * stores could otherwise alias the record loads for the compiler) */
-        for (int e0 = t; e0 < KDA_CHUNK * KDA_DK; e0 += 8 * NT) {
+        for (int e0 = t; e0 < KDA_CHUNK * KDA_DK; e0 += 8 * NTG) {
             float xb[8], xo[8], xv[8], xg[8], xk[8], xu[8], xq[8];
 #pragma unroll
             for (int u = 0; u < 8; u++) {
-                const int e = e0 + u * NT, i = e >> 7, cc = e & 127;
+                const int e = e0 + u * NTG, i = e >> 7, cc = e & 127;
                 const bool ok = i < L;
                 /* loads are unconditional (rows clamped into the chunk) and selected after */
                 const int64_t row = ((t0 + (ok ? i : L - 1)) * H + h) * KDA_DV + cc;
@@ -774,7 +777,7 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
             }
 #pragma unroll
             for (int u = 0; u < 8; u++) {
-                const int e = e0 + u * NT, i = e >> 7, cc = e & 127;
+                const int e = e0 + u * NTG, i = e >> 7, cc = e & 127;
                 DO[e] = xo[u];
                 XU[e] = xb[u] * xv[u];
                 XW[e] = xb[u] * xk[u] * exp2_fast(xg[u] * LOG2E_F);
@@ -803,14 +806,14 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         /* s3: Q' = scale q^ e^G - P W: dP -= dQ' W^T, dW -= P^T dQ'; dU += dD */
         wg_gemm<false, true, KDA_CHUNK, KDA_DK>(dP, dQp, R + KDA_BR_W, -1.f, true);
         wg_gemm<true, false, KDA_DK, KDA_CHUNK>(dW, R + KDA_BR_P, dQp, -1.f, true);
-        for (int e = t; e < KDA_CHUNK * KDA_DV; e += NT) dU[e] += dD[e];
+        for (int e = t; e < KDA_CHUNK * KDA_DV; e += NTG) dU[e] += dD[e];
         __syncthreads();
 
         /* s4: dT = dW X_W^T (+ dU X_U^T below), dX_W = T^T dW, dX_U = T^T dU; masked dP to LDS */
         wg_gemm<false, true, KDA_CHUNK, KDA_DK>(dT, dW, XW, 1.f, false);
         wg_gemm<true, false, KDA_DK, KDA_CHUNK>(dXW, R + KDA_BR_T, dW, 1.f, false);
         wg_gemm<true, false, KDA_DV, KDA_CHUNK>(dXU, R + KDA_BR_T, dU, 1.f, false);
-        for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NT) {
+        for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NTG) {
             const int i = e >> 6, jj = e & 63;
             sdP[i * LDT + jj] = jj <= i ? scale * dP[e] : 0.f; /* scale folded in */
         }
@@ -825,14 +828,14 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         /* s6: dA = -X1 T^T (into dT, which is no longer needed), kept on the strict lower triangle */
         wg_gemm<false, true, KDA_CHUNK, KDA_CHUNK>(dT, X1, R + KDA_BR_T, -1.f, false);
         /* s6b: d G_L from the carried decay: e^{G_L} sum_j dS[r][j] S[r][j]; thread t takes
-         * row t / 2, columns 64 (t % 2) .. + 63 as 16-byte pieces */
+         * row t / 4, columns 32 (t % 4) .. + 31 as 16-byte pieces */
         {
-            const int r = t >> 1, hf = t & 1;
-            const float4 *a4 = (const float4 *)(dS + r * KDA_DV + 64 * hf);
-            const float4 *b4 = (const float4 *)(S0 + r * KDA_DV + 64 * hf);
+            const int r = t >> 2, hf = t & 3;
+            const float4 *a4 = (const float4 *)(dS + r * KDA_DV + 32 * hf);
+            const float4 *b4 = (const float4 *)(S0 + r * KDA_DV + 32 * hf);
             float s = 0.f;
 #pragma unroll
-            for (int jj = 0; jj < 16; jj++) {
+            for (int jj = 0; jj < 8; jj++) {
                 const float4 x = a4[jj], y = b4[jj];
                 s = fmaf(x.x, y.x, s);
                 s = fmaf(x.y, y.y, s);
@@ -840,27 +843,28 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
                 s = fmaf(x.w, y.w, s);
             }
             s += __shfl_xor(s, 1);
+            s += __shfl_xor(s, 2);
             if (hf == 0) sGL[r] = R[KDA_BR_GL + r] * s;
         }
         __syncthreads();
-        for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NT) {
+        for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NTG) {
             const int i = e >> 6, jj = e & 63;
             sdA[i * LDT + jj] = jj < i ? dT[e] : 0.f;
         }
         __syncthreads();
 
-        /* s7: per-element terms (Q', K~, X_W, X_U); thread (c, half) takes rows of parity
-         * half, four rows per pass with all their loads issued first */
+        /* s7: per-element terms (Q', K~, X_W, X_U); thread (c, qtr) takes rows i with
+         * i % 4 = qtr, four rows per pass with all their loads issued first */
         {
             const float gl = sG[(L - 1) * LDK + c];
             float glacc = 0.f;
-            for (int i0 = half; i0 < L; i0 += 8) {
+            for (int i0 = qtr; i0 < L; i0 += 16) {
                 float xdq[4], xkt[4], xdkt[4], xdxw[4], xdxu[4], xv[4];
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
                     /* unconditional loads from a row clamped into the chunk (rows past it
                      * are not used) */
-                    const int i = i0 + 2 * u, ic = i < L ? i : L - 1, e = ic * KDA_DK + c;
+                    const int i = i0 + 4 * u, ic = i < L ? i : L - 1, e = ic * KDA_DK + c;
                     xdq[u] = dQp[e];
                     xkt[u] = R[KDA_BR_KT + e];
                     xdkt[u] = dKt[e];
@@ -870,7 +874,7 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
                 }
 #pragma unroll
                 for (int u = 0; u < 4; u++) {
-                    const int i = i0 + 2 * u, e = i * KDA_DK + c;
+                    const int i = i0 + 4 * u, e = i * KDA_DK + c;
                     if (i < L) {
                         const float gam = exp2_fast(sG[i * LDK + c]), kn = sK[i * LDK + c], qn = sQ[i * LDK + c];
                         const float b = sBeta[i];
@@ -889,9 +893,9 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
                     }
                 }
             }
-            if (half == 1) sGL2[c] = glacc;
+            if (qtr > 0) sQx[qtr - 1][c] = glacc;
             __syncthreads();
-            if (half == 0) sGL[c] += glacc + sGL2[c];
+            if (qtr == 0) sGL[c] += glacc + (sQx[0][c] + sQx[1][c]) + sQx[2][c];
         }
         __syncthreads();
 
@@ -903,7 +907,7 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
          *     with scale dP;
          *   column side, block jb <= 2, a = 16 jb + 15:
          *     CT_off[j] = e^{G_a - G_j} sum_{i > a} (dA_ij beta_i k^_i + scale dP_ij q^_i) e^{G_i - G_a}.
-         * Wave w takes channels 32 w .. 32 w + 31 (two 16-column blocks); the contraction
+         * Wave w takes channels 16 w .. 16 w + 15 (one 16-column block); the contraction
          * index at step s of lane group gq is k0 + gq. Results go to scratch arrays no
          * longer needed (D, dD, dW) as SA_off, SP_off, CT_off; rows without such
          * partners get 0. Exponents are in log2 units and clamped at 0. */
@@ -912,9 +916,8 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
             int tid = t;
             asm volatile("" : "+v"(tid));
             const int w = tid >> 6, l = tid & 63, gq = l >> 4, r16 = l & 15;
-#pragma unroll
-            for (int cbi = 0; cbi < 2; cbi++) {
-                const int cc = 32 * w + 16 * cbi + r16;
+            {
+                const int cc = 16 * w + r16;
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     OA[(4 * gq + e) * KDA_DK + cc] = 0.f;
@@ -957,12 +960,12 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         }
         __syncthreads();
 
-        /* s8: pairwise factors, row side: rows i of parity half, j <= i. With
+        /* s8: pairwise factors, row side: rows i with i % 4 = qtr, j <= i. With
          * E = e^{G_i - G_j} per channel, SA = sum_j dA_ij k^_j E and SP = sum_j scale dP_ij k^_j E
          * give every row-side term: d k^_i += beta_i SA, d q^_i += SP,
          * dG_i += beta_i k^_i SA + q^_i SP, and the d beta partial k^_i SA. Partners in
          * the row's own 16-row block are summed here, the rest come from s8a. */
-        for (int i = half; i < L; i += 2) {
+        for (int i = qtr; i < L; i += 4) {
             const int e = i * KDA_DK + c;
             const float g0 = dG[e], k0 = dkn[e], q0 = dqn[e], b0 = XU[e];
             const float gi = sG[i * LDK + c];
@@ -994,10 +997,10 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         }
         __syncthreads();
 
-        /* s9: pairwise factors, column side: rows j of parity half, i >= j:
+        /* s9: pairwise factors, column side: rows j with j % 4 = qtr, i >= j:
          * CT = sum_i (dA_ij beta_i k^_i + scale dP_ij q^_i) E; d k^_j += CT, dG_j -= k^_j CT.
          * Rows i in the row's own 16-row block are summed here, the rest come from s8a. */
-        for (int jj = half; jj < L; jj += 2) {
+        for (int jj = qtr; jj < L; jj += 4) {
             const int e = jj * KDA_DK + c;
             const float g0 = dG[e], k0 = dkn[e];
             const float gj = sG[jj * LDK + c], knj = sK[jj * LDK + c];
@@ -1029,29 +1032,30 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         __syncthreads();
 
         /* s10: d log a = reverse cumsum of dG (G_L's gradient on the last row), then the
-         * gate; thread (c, half) takes rows 32 half .. 32 half + 31, and the lower half
-         * starts from the upper half's total */
+         * gate; thread (c, qtr) takes rows 16 qtr .. 16 qtr + 15, starting from the
+         * totals of the quarters below it in the chunk (higher rows) */
         {
-            const int r0 = 32 * half, n = L - r0; /* rows of this half: u < n */
-            float xg[32], tot = 0.f;
+            const int r0 = 16 * qtr, n = L - r0; /* rows of this quarter: u < n */
+            float xg[16], tot = 0.f;
 #pragma unroll
-            for (int u = 0; u < 32; u++) {
+            for (int u = 0; u < 16; u++) {
                 const float x = dG[(r0 + u) * KDA_DK + c]; /* row < 64: always inside the scratch tile */
                 xg[u] = u < n ? x : 0.f;
                 tot += xg[u];
             }
-            if (half == 1) sGL2[c] = tot;
+            sTot[qtr][c] = tot;
             __syncthreads();
-            float run = sGL[c] + (half == 0 ? sGL2[c] : 0.f), pdt = 0.f, pa = 0.f;
+            float run = sGL[c], pdt = 0.f, pa = 0.f;
+            for (int q = 3; q > qtr; q--) run += sTot[q][c];
             const float bias = dt_bias[h * KDA_DK + c];
-            float xx[32]; /* gate inputs, loaded unconditionally from rows clamped into the chunk */
+            float xx[16]; /* gate inputs, loaded unconditionally from rows clamped into the chunk */
 #pragma unroll
-            for (int u = 0; u < 32; u++) {
+            for (int u = 0; u < 16; u++) {
                 const int ic = r0 + u < L ? r0 + u : L - 1;
                 xx[u] = bf2f(g[((t0 + ic) * H + h) * KDA_DK + c]);
             }
 #pragma unroll
-            for (int u = 31; u >= 0; u--) {
+            for (int u = 15; u >= 0; u--) {
                 if (u < n) {
                     const int i = r0 + u;
                     run += xg[u];
@@ -1064,14 +1068,14 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
                     pa = fmaf(dla, free_la, pa);
                 }
             }
-            if (half == 1) {
-                sX[c] = pdt;
-                sX[KDA_DK + c] = pa;
+            if (qtr > 0) {
+                sX[qtr - 1][0][c] = pdt;
+                sX[qtr - 1][1][c] = pa;
             }
             __syncthreads();
-            if (half == 0) {
-                part[item * KDA_BWD_PART_FLOATS + c] = pdt + sX[c];
-                sRed[c] = pa + sX[KDA_DK + c];
+            if (qtr == 0) {
+                part[item * KDA_BWD_PART_FLOATS + c] = pdt + (sX[0][0][c] + sX[1][0][c]) + sX[2][0][c];
+                sRed[c] = pa + (sX[0][1][c] + sX[1][1][c]) + sX[2][1][c];
             }
         }
         __syncthreads();
@@ -1081,16 +1085,16 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
             part[item * KDA_BWD_PART_FLOATS + KDA_DK] = s;
         }
 
-        /* s11: through the L2 norms; thread t: row t / 4, channels 16 m + 4 (t % 4) + [0, 4)
-         * for m < 8 (16-byte pieces of the scratch rows) */
+        /* s11: through the L2 norms; thread t: row t / 8, channels 32 m + 4 (t % 8) + [0, 4)
+         * for m < 4 (16-byte pieces of the scratch rows) */
         {
-            const int i = t >> 2, q4 = t & 3;
-            float xq[8][4], xk[8][4];
+            const int i = t >> 3, q8 = t & 7;
+            float xq[4][4], xk[4][4];
             float sq = 0.f, sk = 0.f, sb = 0.f;
             if (i < L) {
 #pragma unroll
-                for (int m = 0; m < 8; m++) {
-                    const int e = i * KDA_DK + 16 * m + 4 * q4;
+                for (int m = 0; m < 4; m++) {
+                    const int e = i * KDA_DK + 32 * m + 4 * q8;
                     const float4 fq = *(const float4 *)(dqn + e), fk = *(const float4 *)(dkn + e);
                     const float4 fb = *(const float4 *)(XU + e);
                     xq[m][0] = fq.x; xq[m][1] = fq.y; xq[m][2] = fq.z; xq[m][3] = fq.w;
@@ -1098,33 +1102,34 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
                     sb += (fb.x + fb.y) + (fb.z + fb.w);
                 }
 #pragma unroll
-                for (int m = 0; m < 8; m++)
+                for (int m = 0; m < 4; m++)
 #pragma unroll
                     for (int u = 0; u < 4; u++) {
-                        const int cc = 16 * m + 4 * q4 + u;
+                        const int cc = 32 * m + 4 * q8 + u;
                         sq = fmaf(sQ[i * LDK + cc], xq[m][u], sq);
                         sk = fmaf(sK[i * LDK + cc], xk[m][u], sk);
                     }
             }
-            /* xor butterflies: every lane of a quad adds the same pairs (deterministic) */
-            sq += __shfl_xor(sq, 1);
-            sq += __shfl_xor(sq, 2);
-            sk += __shfl_xor(sk, 1);
-            sk += __shfl_xor(sk, 2);
-            sb += __shfl_xor(sb, 1);
-            sb += __shfl_xor(sb, 2);
+            /* xor butterflies over the row's 8 lanes: every lane adds the same pairs
+             * (deterministic) */
+#pragma unroll
+            for (int o = 1; o < 8; o <<= 1) {
+                sq += __shfl_xor(sq, o);
+                sk += __shfl_xor(sk, o);
+                sb += __shfl_xor(sb, o);
+            }
             if (i < L) {
                 const float inq = 1.f / R[KDA_BR_NQ + i], ink = 1.f / R[KDA_BR_NK + i];
                 const int64_t row = ((t0 + i) * H + h) * KDA_DK;
 #pragma unroll
-                for (int m = 0; m < 8; m++)
+                for (int m = 0; m < 4; m++)
 #pragma unroll
                     for (int u = 0; u < 4; u++) {
-                        const int cc = 16 * m + 4 * q4 + u;
+                        const int cc = 32 * m + 4 * q8 + u;
                         dq[row + cc] = (xq[m][u] - sQ[i * LDK + cc] * sq) * inq;
                         dk[row + cc] = (xk[m][u] - sK[i * LDK + cc] * sk) * ink;
                     }
-                if (q4 == 0) dbeta[(t0 + i) * H + h] = sb;
+                if (q8 == 0) dbeta[(t0 + i) * H + h] = sb;
             }
         }
         __syncthreads();
@@ -1181,7 +1186,7 @@ extern "C" hipError_t kda_launch_bwd(int stage, const void *q, const void *k, co
                            ckpt, dse, dinit);
         break;
     case 2:
-        hipLaunchKernelGGL(kda_bwd_grad_kernel, dim3((unsigned)kda_bwd_grad_wgs(items)), dim3(NT), 0, st,
+        hipLaunchKernelGGL(kda_bwd_grad_kernel, dim3((unsigned)kda_bwd_grad_wgs(items)), dim3(NTG), 0, st,
                            (const uint16_t *)v, (const uint16_t *)g, (const uint16_t *)dout, A_log, dt_bias, scale,
                            lower_bound, cu, chunk_off, nseq, T, (int)H, nslots, brec, ckpt, dse, part, scratch,
                            dq, dk, dv, dg, dbeta);
