@@ -202,7 +202,7 @@ __device__ __forceinline__ void wg_gemm(float *C, const float *A, const float *B
 /* ------------------------------------------------------------------------- */
 /* chunk quantities, one workgroup per (chunk slot, head), grid H * nslots     */
 /* ------------------------------------------------------------------------- */
-extern "C" __global__ void __launch_bounds__(NT)
+extern "C" __global__ void __launch_bounds__(NTG)
 kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                      const uint16_t *__restrict__ v, const uint16_t *__restrict__ g,
                      const uint16_t *__restrict__ beta, const float *__restrict__ A_log,
@@ -223,34 +223,55 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
     float *R = brec + item * KDA_BR_FLOATS;
     const int t = threadIdx.x;
 
-    /* 1. norms and gate: thread t covers row t / 4, channels 32 (t % 4) + [0, 32) */
+    /* 1. norms and gate: thread t covers row t / 8, channels 16 (t % 8) + [0, 16), read
+     *    as 16-byte pieces */
     {
-        const int i = t >> 2, c0 = (t & 3) * 32;
+        const int i = t >> 3, c0 = (t & 7) * 16;
         const float rate = expf(A_log[h]);
         if (i < L) {
             const int64_t base = ((t0 + i) * H + h) * KDA_DK + c0;
-            float qx[32], kx[32];
+            uint4 uq[2], uk[2], ug[2];
+#pragma unroll
+            for (int p = 0; p < 2; p++) {
+                uq[p] = *(const uint4 *)(q + base + 8 * p);
+                uk[p] = *(const uint4 *)(k + base + 8 * p);
+                ug[p] = *(const uint4 *)(g + base + 8 * p);
+            }
+            float qx[16], kx[16], gx[16];
+#pragma unroll
+            for (int p = 0; p < 2; p++)
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const uint32_t wq = u == 0 ? uq[p].x : u == 1 ? uq[p].y : u == 2 ? uq[p].z : uq[p].w;
+                    const uint32_t wk = u == 0 ? uk[p].x : u == 1 ? uk[p].y : u == 2 ? uk[p].z : uk[p].w;
+                    const uint32_t wg = u == 0 ? ug[p].x : u == 1 ? ug[p].y : u == 2 ? ug[p].z : ug[p].w;
+                    qx[8 * p + 2 * u] = bf2f((uint16_t)(wq & 0xffff));
+                    qx[8 * p + 2 * u + 1] = bf2f((uint16_t)(wq >> 16));
+                    kx[8 * p + 2 * u] = bf2f((uint16_t)(wk & 0xffff));
+                    kx[8 * p + 2 * u + 1] = bf2f((uint16_t)(wk >> 16));
+                    gx[8 * p + 2 * u] = bf2f((uint16_t)(wg & 0xffff));
+                    gx[8 * p + 2 * u + 1] = bf2f((uint16_t)(wg >> 16));
+                }
             float sq = 0.f, sk = 0.f;
 #pragma unroll
-            for (int c = 0; c < 32; c++) {
-                qx[c] = bf2f(q[base + c]);
-                kx[c] = bf2f(k[base + c]);
+            for (int c = 0; c < 16; c++) {
                 sq = fmaf(qx[c], qx[c], sq);
                 sk = fmaf(kx[c], kx[c], sk);
             }
-            sq += __shfl_xor(sq, 1);
-            sq += __shfl_xor(sq, 2);
-            sk += __shfl_xor(sk, 1);
-            sk += __shfl_xor(sk, 2);
+#pragma unroll
+            for (int o = 1; o < 8; o <<= 1) {
+                sq += __shfl_xor(sq, o);
+                sk += __shfl_xor(sk, o);
+            }
             const float nq = sqrtf(sq + 1e-6f), nk = sqrtf(sk + 1e-6f);
 #pragma unroll
-            for (int c = 0; c < 32; c++) {
+            for (int c = 0; c < 16; c++) {
                 sQ[i * LDK + c0 + c] = qx[c] / nq;
                 sK[i * LDK + c0 + c] = kx[c] / nk;
-                const float x = bf2f(g[base + c]) + dt_bias[h * KDA_DK + c0 + c];
+                const float x = gx[c] + dt_bias[h * KDA_DK + c0 + c];
                 sG[i * LDK + c0 + c] = fmaxf(-rate * softplus_f(x), lower_bound);
             }
-            if ((t & 3) == 0) {
+            if ((t & 7) == 0) {
                 const float b = bf2f(beta[(t0 + i) * H + h]);
                 sB[i] = b;
                 R[KDA_BR_BETA + i] = b;
@@ -259,12 +280,12 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
             }
         } else {
 #pragma unroll
-            for (int c = 0; c < 32; c++) {
+            for (int c = 0; c < 16; c++) {
                 sQ[i * LDK + c0 + c] = 0.f;
                 sK[i * LDK + c0 + c] = 0.f;
                 sG[i * LDK + c0 + c] = 0.f;
             }
-            if ((t & 3) == 0) {
+            if ((t & 7) == 0) {
                 sB[i] = 0.f;
                 R[KDA_BR_BETA + i] = 0.f;
                 R[KDA_BR_NQ + i] = 1.f;
@@ -272,7 +293,7 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
             }
         }
     }
-    for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NT) {
+    for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NTG) {
         const int i = e >> 6, j = e & 63;
         sA[i * LDT + j] = 0.f;
         sP[i * LDT + j] = 0.f;
@@ -296,7 +317,7 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
      *      A_ij = beta_i sum_c (k^_ic e^{G_ic - G_ac}) (k^_jc e^{G_ac - G_jc}),
      *      P_ij = scale sum_c (q^_ic e^{G_ic - G_ac}) (k^_jc e^{G_ac - G_jc}),
      *    both factors <= 1 for j <= a < i. Rows past the chunk have k^ = q^ = 0. */
-    for (int e = t; e < 4 * 136; e += NT) {
+    for (int e = t; e < 4 * 136; e += NTG) {
         const int bd = e / 136, r = e - bd * 136;
         int ii = (int)((sqrtf(8.f * (float)r + 1.f) - 1.f) * 0.5f);
         while (ii * (ii + 1) / 2 > r) ii--;
@@ -313,9 +334,9 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
         sP[i * LDT + j] = scale * p;
     }
     {
-        /* block (ib, jb), jb < ib: list index w and w + 4 per wave */
+        /* block (ib, jb), jb < ib: list index w, one per wave (waves 6 and 7 idle) */
         const int w = t >> 6, l = t & 63, gq = l >> 4, r16 = l & 15;
-        for (int bi = w; bi < 6; bi += 4) {
+        for (int bi = w; bi < 6; bi += 8) {
             const int ib = bi == 0 ? 1 : bi < 3 ? 2 : 3;
             const int jb = bi == 0 ? 0 : bi < 3 ? bi - 1 : bi - 3;
             const int ia = 16 * ib - 1, i = 16 * ib + r16, j = 16 * jb + r16;
@@ -345,17 +366,19 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
      *    taking block (b + d, b) */
     {
         const int w = t >> 6, l = t & 63, gq = l >> 4, r16 = l & 15;
-        float tc[16];
+        if (w < 4) { /* waves 4-7 have no diagonal block */
+            float tc[16];
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            float s = r == r16 ? 1.f : 0.f;
+            for (int r = 0; r < 16; r++) {
+                float s = r == r16 ? 1.f : 0.f;
 #pragma unroll
-            for (int m = 0; m < r; m++) s = fmaf(-sA[(16 * w + r) * LDT + 16 * w + m], tc[m], s);
-            tc[r] = s;
-        }
-        if (gq == 0) {
+                for (int m = 0; m < r; m++) s = fmaf(-sA[(16 * w + r) * LDT + 16 * w + m], tc[m], s);
+                tc[r] = s;
+            }
+            if (gq == 0) {
 #pragma unroll
-            for (int r = 0; r < 16; r++) sT[(16 * w + r) * LDT + 16 * w + r16] = tc[r];
+                for (int r = 0; r < 16; r++) sT[(16 * w + r) * LDT + 16 * w + r16] = tc[r];
+            }
         }
         __syncthreads();
         for (int d = 1; d < 4; d++) {
@@ -384,12 +407,12 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
     }
 
     /* 5. store T, P, q^, k^, G */
-    for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NT) {
+    for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NTG) {
         const int i = e >> 6, j = e & 63;
         R[KDA_BR_T + e] = sT[i * LDT + j];
         R[KDA_BR_P + e] = sP[i * LDT + j];
     }
-    for (int e = t; e < KDA_CHUNK * KDA_DK; e += NT) {
+    for (int e = t; e < KDA_CHUNK * KDA_DK; e += NTG) {
         const int i = e >> 7, c = e & 127;
         R[KDA_BR_QN + e] = sQ[i * LDK + c];
         R[KDA_BR_KN + e] = sK[i * LDK + c];
@@ -397,18 +420,18 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
     }
 
     /* 6. W = T X_W (X_W = beta k^ e^G), U = T X_U (X_U = beta v) and
-     *    Q' = scale q^ e^G - P W on fp32 MFMA: wave w takes columns 32 w .. 32 w + 31
-     *    (two 16-column blocks) of all 64 rows; the contraction index of the first two
+     *    Q' = scale q^ e^G - P W on fp32 MFMA: wave w takes columns 16 w .. 16 w + 15
+     *    (one 16-column block) of all 64 rows; the contraction index of the first two
      *    products is 16 kb + 4 s + gq at step s, and W's accumulators serve as the B
      *    operand of P W (contraction index 16 kb + 4 gq + s). Rows m >= L contribute
      *    nothing (beta_m = 0 there, and v is not read). Then K~ and e^{G_L}. */
     {
         const int w = t >> 6, l = t & 63, gq = l >> 4, r16 = l & 15;
-        f32x4 wacc[4][2], uacc[4][2];
+        f32x4 wacc[4][1], uacc[4][1];
 #pragma unroll
         for (int rb = 0; rb < 4; rb++)
 #pragma unroll
-            for (int cbi = 0; cbi < 2; cbi++) {
+            for (int cbi = 0; cbi < 1; cbi++) {
                 wacc[rb][cbi] = zero4();
                 uacc[rb][cbi] = zero4();
             }
@@ -421,8 +444,8 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
 #pragma unroll
                 for (int rb = 0; rb < 4; rb++) ta[rb] = sT[(16 * rb + r16) * LDT + m];
 #pragma unroll
-                for (int cbi = 0; cbi < 2; cbi++) {
-                    const int c = 32 * w + 16 * cbi + r16;
+                for (int cbi = 0; cbi < 1; cbi++) {
+                    const int c = 16 * (w + cbi) + r16;
                     const float xw = sB[m] * sK[m * LDK + c] * expf(sG[m * LDK + c]);
                     /* unconditional load from a row inside the chunk, then a select:
                      * a load under a branch would wait for every outstanding load */
@@ -436,14 +459,14 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
                 }
             }
         }
-        f32x4 qacc[4][2];
+        f32x4 qacc[4][1];
 #pragma unroll
         for (int rb = 0; rb < 4; rb++)
 #pragma unroll
-            for (int cbi = 0; cbi < 2; cbi++)
+            for (int cbi = 0; cbi < 1; cbi++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const int row = 16 * rb + 4 * gq + e, c = 32 * w + 16 * cbi + r16;
+                    const int row = 16 * rb + 4 * gq + e, c = 16 * (w + cbi) + r16;
                     R[KDA_BR_W + row * KDA_DK + c] = wacc[rb][cbi][e];
                     R[KDA_BR_U + row * KDA_DV + c] = uacc[rb][cbi][e];
                     qacc[rb][cbi][e] = scale * sQ[row * LDK + c] * expf(sG[row * LDK + c]);
@@ -457,19 +480,19 @@ kda_bwd_chunk_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict_
                 for (int ib = 0; ib < 4; ib++) {
                     const float pa = -sP[(16 * ib + r16) * LDT + m];
 #pragma unroll
-                    for (int cbi = 0; cbi < 2; cbi++) qacc[ib][cbi] = mfma4(pa, wacc[kb][cbi][s4], qacc[ib][cbi]);
+                    for (int cbi = 0; cbi < 1; cbi++) qacc[ib][cbi] = mfma4(pa, wacc[kb][cbi][s4], qacc[ib][cbi]);
                 }
             }
         }
 #pragma unroll
         for (int rb = 0; rb < 4; rb++)
 #pragma unroll
-            for (int cbi = 0; cbi < 2; cbi++)
+            for (int cbi = 0; cbi < 1; cbi++)
 #pragma unroll
                 for (int e = 0; e < 4; e++)
-                    R[KDA_BR_QP + (16 * rb + 4 * gq + e) * KDA_DK + 32 * w + 16 * cbi + r16] = qacc[rb][cbi][e];
+                    R[KDA_BR_QP + (16 * rb + 4 * gq + e) * KDA_DK + 16 * (w + cbi) + r16] = qacc[rb][cbi][e];
     }
-    for (int e = t; e < KDA_CHUNK * KDA_DK; e += NT) {
+    for (int e = t; e < KDA_CHUNK * KDA_DK; e += NTG) {
         const int i = e >> 7, c = e & 127;
         R[KDA_BR_KT + e] = sK[i * LDK + c] * expf(sG[(L - 1) * LDK + c] - sG[i * LDK + c]);
     }
@@ -1175,7 +1198,7 @@ extern "C" hipError_t kda_launch_bwd(int stage, const void *q, const void *k, co
     float *scratch = (float *)((unsigned char *)part + kda_bwd_part_bytes(items));
     switch (stage) {
     case 0:
-        hipLaunchKernelGGL(kda_bwd_chunk_kernel, dim3((unsigned)items), dim3(NT), 0, st, (const uint16_t *)q,
+        hipLaunchKernelGGL(kda_bwd_chunk_kernel, dim3((unsigned)items), dim3(NTG), 0, st, (const uint16_t *)q,
                            (const uint16_t *)k, (const uint16_t *)v, (const uint16_t *)g,
                            (const uint16_t *)beta, A_log, dt_bias, scale, lower_bound, cu, chunk_off, nseq, T,
                            (int)H, nslots, brec);
