@@ -61,7 +61,9 @@ typedef enum {
                                 B != 1 with cu_seqlens, or sizes past the limits
                                 below (KDA_MAX_HEADS, 32-bit grids and offsets)     */
     KDA_ERR_STATE_DTYPE = 4, /* state_dtype inconsistent with the state pointers   */
-    KDA_ERR_ARG = 5,         /* scale or lower_bound non-finite, or lower_bound > 0 */
+    KDA_ERR_ARG = 5,         /* scale or lower_bound non-finite, lower_bound > 0,
+                                or a tensor that must be 16-byte aligned is not
+                                (see "Alignment" below)                            */
     KDA_ERR_WORKSPACE = 6,   /* workspace NULL, not 256-byte aligned, or smaller
                                 than kda_fwd_workspace_size                        */
     KDA_ERR_ALIAS = 7,       /* out overlaps an input, or the states overlap only
@@ -81,6 +83,12 @@ typedef enum {
  * offsets); for kda_fwd, (chunk slots) * H and 8 * N * H at most INT32_MAX, and for
  * kda_decode N * H at most INT32_MAX (launch grids). */
 #define KDA_MAX_HEADS 65536
+
+/* Alignment (checked, KDA_ERR_ARG): q, k, v, g, out, dt_bias and the state tensors
+ * (initial_state, final_state, the decode state, dfinal_state, dinitial_state) and
+ * the fp32 gradients of kda_bwd must be 16-byte aligned: the kernels move them in
+ * 16-byte pieces. beta, A_log, cu_seqlens and dout need only their element
+ * alignment. Tensors allocated by torch are 256-byte aligned. */
 
 /* Most negative lower_bound of the fast form of kda_fwd. Inside one 16-token
  * sub-chunk the fast form anchors the decay factors at the middle token, so the

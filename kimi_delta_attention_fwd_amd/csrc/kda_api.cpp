@@ -101,7 +101,8 @@ extern "C" const char *kda_status_string(int status)
     case KDA_ERR_STATE_DTYPE:
         return "KDA_ERR_STATE_DTYPE: state_dtype must be NONE exactly when no state is given, else BF16 or FP32";
     case KDA_ERR_ARG:
-        return "KDA_ERR_ARG: scale and lower_bound must be finite with lower_bound <= 0";
+        return "KDA_ERR_ARG: scale and lower_bound must be finite with lower_bound <= 0, and the tensors kda.h "
+               "lists under Alignment 16-byte aligned";
     case KDA_ERR_WORKSPACE:
         return "KDA_ERR_WORKSPACE: workspace is NULL, not 256-byte aligned, or smaller than kda_fwd_workspace_size";
     case KDA_ERR_ALIAS:
@@ -110,6 +111,9 @@ extern "C" const char *kda_status_string(int status)
     default: return "unknown kda status";
     }
 }
+
+/* 16-byte alignment of the tensors the kernels move in 16-byte pieces (NULL passes) */
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 /* the size limits of kda.h (KDA_MAX_HEADS, 32-bit grids and offsets) */
 static bool fwd_sizes_ok(int64_t B, int64_t T, int64_t H, int64_t num_seqs)
@@ -183,6 +187,9 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
         return KDA_ERR_STATE_DTYPE;
     }
     if (!std::isfinite(scale) || !std::isfinite(lower_bound) || lower_bound > 0.f) return KDA_ERR_ARG;
+    for (const void *p : {q, k, v, g, (const void *)out, (const void *)dt_bias, initial_state,
+                          (const void *)final_state})
+        if (!aligned16(p)) return KDA_ERR_ARG;
     const int64_t nseq_arg = cu_seqlens ? num_seqs : 0;
     const size_t need = kda_fwd_workspace_size(B, T, H, nseq_arg);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return KDA_ERR_WORKSPACE;
@@ -246,6 +253,8 @@ extern "C" int kda_decode(const void *q, const void *k, const void *v, const voi
     if (!q || !k || !v || !g || !beta || !out || !A_log || !dt_bias || !state) return KDA_ERR_NULL;
     if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP32) return KDA_ERR_STATE_DTYPE;
     if (!std::isfinite(scale) || !std::isfinite(lower_bound) || lower_bound > 0.f) return KDA_ERR_ARG;
+    for (const void *p : {q, k, v, g, (const void *)out, (const void *)dt_bias, (const void *)state})
+        if (!aligned16(p)) return KDA_ERR_ARG;
     const size_t vec = (size_t)N * H * KDA_DK * 2;
     const size_t sbytes = (size_t)N * H * KDA_DK * KDA_DV * (state_dtype == KDA_STATE_FP32 ? 4 : 2);
     const Range r_out = rng(out, vec), r_state = rng(state, sbytes);
@@ -297,6 +306,10 @@ extern "C" int kda_bwd(const void *q, const void *k, const void *v, const void *
         return KDA_ERR_STATE_DTYPE;
     }
     if (!std::isfinite(scale) || !std::isfinite(lower_bound) || lower_bound > 0.f) return KDA_ERR_ARG;
+    for (const void *p : {q, k, v, g, (const void *)dt_bias, initial_state, (const void *)dfinal_state,
+                          (const void *)dq, (const void *)dk, (const void *)dv, (const void *)dg,
+                          (const void *)dbeta, (const void *)ddt_bias, (const void *)dinitial_state})
+        if (!aligned16(p)) return KDA_ERR_ARG;
     const int64_t nseq_arg = cu_seqlens ? num_seqs : 0;
     const size_t need = kda_bwd_workspace_size(B, T, H, nseq_arg);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return KDA_ERR_WORKSPACE;

@@ -123,6 +123,18 @@ def test_rejects_args(fb):
     assert fb.call(lib, scale=float("inf")) == 5
 
 
+def test_rejects_misaligned(fb):
+    """Tensors moved in 16-byte pieces must be 16-byte aligned (KDA_ERR_ARG)."""
+    lib = kda.load_library()
+    for name in ["q", "k", "v", "g", "out", "dt_bias"]:
+        assert fb.call(lib, **{"p_" + name: fb.addr[name] + 2}) == 5, name
+    assert fb.call(lib, sd=2, init=fb.addr["init"] + 8) == 5
+    assert fb.call(lib, sd=2, fin=fb.addr["fin"] + 4) == 5
+    # element alignment is enough for beta and A_log
+    assert fb.call(lib, p_beta=fb.addr["beta"] + 2, wsb=0) == 6
+    assert fb.call(lib, p_A_log=fb.addr["A_log"] + 4, wsb=0) == 6
+
+
 def test_rejects_workspace(fb):
     lib = kda.load_library()
     assert fb.call(lib, p_ws=None) == 6
@@ -170,6 +182,9 @@ def test_decode_rejects_bad_arguments():
     assert _decode_call(lib, {"lb": 0.25}) == 5
     assert _decode_call(lib, {"lb": float("-inf")}) == 5
     assert _decode_call(lib, {"scale": float("nan")}) == 5
+    base0, step0 = 1 << 40, 1 << 32
+    assert _decode_call(lib, {"p_q": base0 + 2}) == 5                      # q not 16-byte aligned
+    assert _decode_call(lib, {"p_state": base0 + 8 * step0 + 4}) == 5      # state not 16-byte aligned
     base, step = 1 << 40, 1 << 32
     assert _decode_call(lib, {"p_out": base + 2 * step + 16}) == 7         # out overlaps v
     assert _decode_call(lib, {"p_state": base + 0 * step + 256}) == 7      # state overlaps q
