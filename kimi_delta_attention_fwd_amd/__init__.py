@@ -43,6 +43,10 @@ def load_library():
     global _lib
     if _lib is not None:
         return _lib
+    # torch ships its own HIP runtime; it must be the one in the process before
+    # libkda binds to a HIP runtime, or libkda would load a second copy and its
+    # launches on torch's memory and streams fail (KDA_ERR_HIP)
+    import torch  # noqa: F401
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError("libkda.so is not built: run `python -c \"import __graft_entry__ as e; e.build()\"` "
                            "or `python kimi_delta_attention_fwd_amd/build.py`")

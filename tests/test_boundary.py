@@ -189,3 +189,15 @@ def test_decode_rejects_bad_arguments():
     assert _decode_call(lib, {"p_out": base + 2 * step + 16}) == 7         # out overlaps v
     assert _decode_call(lib, {"p_state": base + 0 * step + 256}) == 7      # state overlaps q
     assert _decode_call(lib, {"p_out": base + 8 * step + 512}) == 7        # out inside the state
+
+
+def test_load_library_brings_torch_first():
+    """torch ships its own HIP runtime: load_library() imports torch before binding
+    libkda, so a program that loads the library before importing torch still runs
+    libkda on torch's runtime (a second runtime would make every launch fail)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r); import kimi_delta_attention_fwd_amd as kda; "
+            "assert 'torch' not in sys.modules; kda.load_library(); assert 'torch' in sys.modules" % ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]

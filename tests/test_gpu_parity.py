@@ -7,6 +7,7 @@ absolute error <= 5e-2 for ``out`` and, where returned, ``final_state``; exact
 multiple of 64 with an fp32 state, repeated calls).
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -465,3 +466,33 @@ def test_errors_raise():
     o2 = torch.empty_like(q2)
     with pytest.raises(ValueError, match="KDA_ERR_SHAPE"):
         kda.fwd(q2, q2, q2, q2, b2, d["scale"], o2, t["A_log"], t["dt_bias"], -5.0, cu_seqlens=cu)
+
+
+def test_library_loaded_before_torch():
+    """A fresh process that loads libkda before importing torch runs kda.fwd
+    correctly (regression: libkda used to bind the system HIP runtime next to
+    torch's own, and every launch failed with KDA_ERR_HIP)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = """
+import sys
+sys.path.insert(0, %r)
+import kimi_delta_attention_fwd_amd as kda
+kda.load_library()
+import numpy as np, torch
+import kda_inputs as ki, oracle
+d = ki.make_inputs(1, 100, 2, seed=3, state="fp32", initial=True, sigma=0.02)
+bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+out = torch.empty((1, 100, 2, 128), dtype=torch.bfloat16, device="cuda:0")
+kda.fwd(bf(d["q"]), bf(d["k"]), bf(d["v"]), bf(d["g"]), bf(d["beta"]), d["scale"], out,
+        torch.from_numpy(d["A_log"]).to("cuda:0"), torch.from_numpy(d["dt_bias"]).to("cuda:0"), d["lower_bound"],
+        initial_state=torch.from_numpy(d["initial_state"]).to("cuda:0"))
+torch.cuda.synchronize()
+ro, _ = oracle.fwd_inputs(d)
+e = oracle.rel_l2(out.float().cpu().numpy(), ro)
+assert e <= 1e-2, e
+print("ok", e)
+""" % root
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout[-1000:] + r.stderr[-2000:]
