@@ -38,7 +38,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "kimi_delta_attention_fwd_amd", "csrc")
 KERNEL_SOURCES = {"kda_prep": ("kda_prep.hip", "kda_device.h", "kda_internal.h", "../../include/kda.h"),
                   "kda_scan": ("kda_scan.hip", "kda_device.h", "kda_internal.h"),
-                  "kda_decode": ("kda_decode.hip", "kda_device.h", "kda_internal.h")}
+                  "kda_decode": ("kda_decode.hip", "kda_device.h", "kda_internal.h"),
+                  "kda_bwd_grad": ("kda_bwd.hip", "kda_device.h", "kda_internal.h")}
 # algorithmic MFMA flops per token-head with 16x16 blocks and 64-token chunks:
 # state-side 6*K*V + intra-chunk 2*C*(3K + 2V)
 FLOPS_PER_TH = 6 * 128 * 128 + 2 * 64 * (3 * 128 + 2 * 128)
@@ -422,7 +423,8 @@ def run_backward(args):
         "config": {"workload": "%s backward: B=%d T=%d H=%d, bf16 inputs, fp32 gradients" % (d["name"], B, T, H),
                    "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None, "kernel": "kda_bwd_grad",
+                     "frac": achieved / PEAK_FP32_TFLOPS,
+                     "traffic": measured_traffic("kda_bwd_grad", d["name"] + "_backward"), "kernel": "kda_bwd_grad",
                      "kernel_ms": grad_ms, "alg_flops_per_launch": units * BWD_GRAD_FLOPS_PER_TH},
         "kernels_ms": kern,
     }
