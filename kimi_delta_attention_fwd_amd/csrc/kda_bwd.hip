@@ -75,101 +75,109 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4 &c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-/* x[s] = p[s * STRIDE] for s < 8; p is 16-byte aligned when STRIDE is 1 */
-template <int STRIDE>
-__device__ __forceinline__ void load8(float *x, const float *p)
+/* LDS staging of one 32-wide contraction slice for wg_gemm: A^T [32][WS_LSA] and
+ * B [32][WS_LSB] (rows = contraction index); two such buffers */
+constexpr int WS_LSA = 68, WS_LSB = 132;
+constexpr int WS_STAGE = 32 * WS_LSA + 32 * WS_LSB;
+
+/* one operand slice of wg_gemm (contraction indices 32 sl .. 32 sl + 31) into this
+ * thread's registers: 16 bytes of A and N / 64 times 16 bytes of B */
+template <bool TA, bool TB, int N, int lda, int ldb>
+__device__ __forceinline__ void wg_slice_load(float4 &ra, float4 (&rbq)[N / 64], const float *A, const float *B,
+                                              int sl, int tid)
 {
-    if (STRIDE == 1) {
+    const int kb = 32 * sl;
+    if (TA) ra = *(const float4 *)(A + (kb + (tid >> 4)) * lda + 4 * (tid & 15));
+    else ra = *(const float4 *)(A + (tid >> 3) * lda + kb + 4 * (tid & 7));
 #pragma unroll
-        for (int i = 0; i < 2; i++) {
-            const float4 f = *(const float4 *)(p + 4 * i);
-            x[4 * i] = f.x; x[4 * i + 1] = f.y; x[4 * i + 2] = f.z; x[4 * i + 3] = f.w;
-        }
+    for (int p = 0; p < N / 64; p++) {
+        const int idx = tid + 512 * p;
+        if (TB) rbq[p] = *(const float4 *)(B + (idx >> 3) * ldb + kb + 4 * (idx & 7));
+        else rbq[p] = *(const float4 *)(B + (kb + idx / (N / 4)) * ldb + 4 * (idx % (N / 4)));
+    }
+}
+
+/* the registers of wg_slice_load into one LDS staging buffer (A^T and B rows by
+ * contraction index) */
+template <bool TA, bool TB, int N>
+__device__ __forceinline__ void wg_slice_store(float *sa, const float4 &ra, const float4 (&rbq)[N / 64], int tid)
+{
+    float *sb = sa + 32 * WS_LSA;
+    if (TA) {
+        *(float4 *)(sa + (tid >> 4) * WS_LSA + 4 * (tid & 15)) = ra;
     } else {
-#pragma unroll
-        for (int s = 0; s < 8; s++) x[s] = p[s * STRIDE];
-    }
-}
-
-/* one 32-wide contraction slice of wg_gemm's operands for this lane (see wg_gemm) */
-template <bool TA, bool TB, int NBW, int lda, int ldb>
-__device__ __forceinline__ void wg_load_slice(float (&a)[2][8], float (&b)[NBW][8], const float *A, const float *B,
-                                              int sl, int gq, int r16, int rb0, int cb0)
-{
-    const int kb = 32 * sl + 8 * gq;
-#pragma unroll
-    for (int rb = 0; rb < 2; rb++) {
-        const int i = 16 * (rb0 + rb) + r16;
-        if (TA) load8<lda>(a[rb], A + kb * lda + i);
-        else load8<1>(a[rb], A + i * lda + kb);
+        const int i = tid >> 3, c = 4 * (tid & 7);
+        sa[c * WS_LSA + i] = ra.x; sa[(c + 1) * WS_LSA + i] = ra.y;
+        sa[(c + 2) * WS_LSA + i] = ra.z; sa[(c + 3) * WS_LSA + i] = ra.w;
     }
 #pragma unroll
-    for (int cb = 0; cb < NBW; cb++) {
-        const int j = 16 * (cb0 + cb) + r16;
-        if (TB) load8<1>(b[cb], B + j * ldb + kb);
-        else load8<ldb>(b[cb], B + kb * ldb + j);
+    for (int p = 0; p < N / 64; p++) {
+        const int idx = tid + 512 * p;
+        if (TB) {
+            const int j = idx >> 3, c = 4 * (idx & 7);
+            sb[c * WS_LSB + j] = rbq[p].x; sb[(c + 1) * WS_LSB + j] = rbq[p].y;
+            sb[(c + 2) * WS_LSB + j] = rbq[p].z; sb[(c + 3) * WS_LSB + j] = rbq[p].w;
+        } else {
+            *(float4 *)(sb + (idx / (N / 4)) * WS_LSB + 4 * (idx % (N / 4))) = rbq[p];
+        }
     }
-}
-
-template <int NBW>
-__device__ __forceinline__ void wg_mma_slice(f32x4 (&d)[2][NBW], const float (&a)[2][8], const float (&b)[NBW][8])
-{
-#pragma unroll
-    for (int s = 0; s < 8; s++)
-#pragma unroll
-        for (int rb = 0; rb < 2; rb++)
-#pragma unroll
-            for (int cb = 0; cb < NBW; cb++) d[rb][cb] = mfma4(a[rb][s], b[cb][s], d[rb][cb]);
 }
 
 /* C[i][j] = (acc ? C[i][j] : 0) + alpha * sum_k a(i, k) b(k, j) for i < 64, j < N,
- * with a(i, k) = TA ? A[k][i] : A[i][k] and b(k, j) = TB ? B[j][k] : B[k][j], on fp32 MFMA
- * (16 x 16 x 4 blocks), by the eight waves of a gradient workgroup. Wave w holds row
- * blocks 2 (w % 2) + {0, 1} and N / 64 column blocks starting at (w / 2) N / 64. The contraction runs in 32-wide slices: in slice
- * sl, lane group gq (lanes 16 gq .. 16 gq + 15) takes indices 32 sl + 8 gq + s at step
- * s < 8, so operands contiguous along it load as 16-byte pieces. The next slice's
- * operands are loaded while the current one is multiplied, and scheduling barriers
- * keep each slice's loads together ahead of the MFMAs that wait for them (left to
- * itself the scheduler sinks loads next to their uses, and each such load then waits
- * for every outstanding memory operation). Every row stride and base is a multiple
- * of 4 floats. Callers separate products that share an output or read one another's
- * output with a barrier. */
+ * with a(i, k) = TA ? A[k][i] : A[i][k] and b(k, j) = TB ? B[j][k] : B[k][j], dense
+ * row-major operands (A is [64][KD], [KD][64] if TA; B is [KD][N], [N][KD] if TB;
+ * C is [64][N]), on fp32 MFMA (16 x 16 x 4 blocks) by the eight waves of a
+ * gradient workgroup. Wave w holds row blocks 2 (w % 2) + {0, 1} and N / 64 column
+ * blocks starting at (w / 2) N / 64. The contraction runs in 32-wide slices: each
+ * operand slice is read from global memory once per workgroup, 16 bytes per thread
+ * (coalesced), into an LDS buffer from which the waves read their fragments (lane
+ * group gq takes contraction indices 8 gq .. 8 gq + 7 of the slice); the next slice
+ * is loaded into registers while the current one is multiplied, then written to the
+ * other buffer (one barrier per slice). Every row stride and base is a multiple of
+ * 4 floats. stage: 2 * WS_STAGE floats of LDS, 16-byte aligned. Every thread of the
+ * workgroup calls it (it holds barriers); callers separate products that share an
+ * output or read one another's output with a barrier. */
 template <bool TA, bool TB, int N, int KD>
-__device__ __forceinline__ void wg_gemm(float *C, const float *A, const float *B, float alpha, bool acc)
+__device__ __forceinline__ void wg_gemm(float *C, const float *A, const float *B, float alpha, bool acc,
+                                          float *stage)
 {
     static_assert(N % 64 == 0 && KD % 32 == 0, "block shape");
-    /* dense row-major operands: A is [64][KD] ([KD][64] if TA), B is [KD][N] ([N][KD] if TB), C is [64][N] */
     constexpr int lda = TA ? 64 : KD, ldb = TB ? KD : N, ldc = N;
-    constexpr int NBW = N / 64, NSL = KD / 32;
-    /* the lane index is made opaque here, so the per-lane operand offsets are
-     * computed at each product instead of being hoisted out of the item loop,
-     * where they would hold hundreds of registers */
+    constexpr int NBW = N / 64, NSL = KD / 32, NBQ = N / 64; /* B float4 pieces per thread */
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int l = tid & 63, w = tid >> 6, gq = l >> 4, r16 = l & 15;
     const int rb0 = 2 * (w & 1), cb0 = (w >> 1) * NBW;
-    __builtin_amdgcn_sched_barrier(0);
+    float4 ra, rbq[NBQ];
     f32x4 d[2][NBW];
 #pragma unroll
     for (int rb = 0; rb < 2; rb++)
 #pragma unroll
         for (int cb = 0; cb < NBW; cb++) d[rb][cb] = zero4();
-    /* two operand sets, used for even and odd slices */
-    float a0[2][8], b0[NBW][8], a1[2][8], b1[NBW][8];
-    wg_load_slice<TA, TB, NBW, lda, ldb>(a0, b0, A, B, 0, gq, r16, rb0, cb0);
+    wg_slice_load<TA, TB, N, lda, ldb>(ra, rbq, A, B, 0, tid);
+    wg_slice_store<TA, TB, N>(stage, ra, rbq, tid);
+    __syncthreads();
 #pragma unroll
     for (int sl = 0; sl < NSL; sl++) {
-        if (sl + 1 < NSL) {
-            if ((sl & 1) == 0) wg_load_slice<TA, TB, NBW, lda, ldb>(a1, b1, A, B, sl + 1, gq, r16, rb0, cb0);
-            else wg_load_slice<TA, TB, NBW, lda, ldb>(a0, b0, A, B, sl + 1, gq, r16, rb0, cb0);
+        if (sl + 1 < NSL) wg_slice_load<TA, TB, N, lda, ldb>(ra, rbq, A, B, sl + 1, tid);
+        const float *sa = stage + (sl & 1) * WS_STAGE, *sb = sa + 32 * WS_LSA;
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            const int k = 8 * gq + s;
+            float a[2], b[NBW];
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++) a[rb] = sa[k * WS_LSA + 16 * (rb0 + rb) + r16];
+#pragma unroll
+            for (int cb = 0; cb < NBW; cb++) b[cb] = sb[k * WS_LSB + 16 * (cb0 + cb) + r16];
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+                for (int cb = 0; cb < NBW; cb++) d[rb][cb] = mfma4(a[rb], b[cb], d[rb][cb]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if ((sl & 1) == 0) wg_mma_slice<NBW>(d, a0, b0);
-        else wg_mma_slice<NBW>(d, a1, b1);
-        __builtin_amdgcn_sched_barrier(0);
+        if (sl + 1 < NSL) wg_slice_store<TA, TB, N>(stage + ((sl + 1) & 1) * WS_STAGE, ra, rbq, tid);
+        __syncthreads();
     }
     if (acc) {
-        /* all of this wave's C elements read before any is written back */
         float cv[2][NBW][4];
 #pragma unroll
         for (int rb = 0; rb < 2; rb++)
@@ -177,7 +185,6 @@ __device__ __forceinline__ void wg_gemm(float *C, const float *A, const float *B
             for (int cb = 0; cb < NBW; cb++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) cv[rb][cb][e] = C[(16 * (rb0 + rb) + 4 * gq + e) * ldc + 16 * (cb0 + cb) + r16];
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int rb = 0; rb < 2; rb++)
 #pragma unroll
@@ -194,7 +201,6 @@ __device__ __forceinline__ void wg_gemm(float *C, const float *A, const float *B
                 for (int e = 0; e < 4; e++)
                     C[(16 * (rb0 + rb) + 4 * gq + e) * ldc + 16 * (cb0 + cb) + r16] = alpha * d[rb][cb][e];
     }
-    __builtin_amdgcn_sched_barrier(0);
 }
 
 } // namespace
@@ -747,7 +753,12 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
                     float *__restrict__ scratch, float *__restrict__ dq, float *__restrict__ dk,
                     float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta)
 {
-    __shared__ float sG[KDA_CHUNK * LDK], sK[KDA_CHUNK * LDK], sQ[KDA_CHUNK * LDK];
+    /* G, k^, q^ for the per-element phases; during the matrix products the same
+     * LDS holds the products' operand slices */
+    __shared__ __attribute__((aligned(16))) float sGKQ[3 * KDA_CHUNK * LDK];
+    float *const sG = sGKQ, *const sK = sGKQ + KDA_CHUNK * LDK, *const sQ = sGKQ + 2 * KDA_CHUNK * LDK;
+    float *const stage = sGKQ;
+    static_assert(2 * WS_STAGE <= 3 * KDA_CHUNK * LDK, "staging fits");
     __shared__ float sdA[KDA_CHUNK * LDT], sdP[KDA_CHUNK * LDT];
     __shared__ float sBeta[KDA_CHUNK], sGL[KDA_DK], sRed[KDA_DK];
     __shared__ float sQx[3][KDA_DK], sTot[4][KDA_DK], sX[3][2][KDA_DK]; /* row-quarter exchanges */
@@ -778,11 +789,11 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         float *dP = scr + 14 * 8192, *dT = dP + 4096, *X1 = dP + 2 * 4096;
         const float rate = expf(A_log[h]);
 
-        /* s0: dout, X_W, X_U, D <- U; LDS copies of G (in log2 units), k^ and q^. Eight
-         * elements per pass with all their loads issued before any store (the scratch
-         * stores could otherwise alias the record loads for the compiler) */
+        /* s0: dout, X_W, X_U, D <- U. Eight elements per pass with all their loads
+         * issued before any store (the scratch stores could otherwise alias the record
+         * loads for the compiler) */
         for (int e0 = t; e0 < KDA_CHUNK * KDA_DK; e0 += 8 * NTG) {
-            float xb[8], xo[8], xv[8], xg[8], xk[8], xu[8], xq[8];
+            float xb[8], xo[8], xv[8], xg[8], xk[8], xu[8];
 #pragma unroll
             for (int u = 0; u < 8; u++) {
                 const int e = e0 + u * NTG, i = e >> 7, cc = e & 127;
@@ -796,60 +807,56 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
                 xg[u] = R[KDA_BR_G + e];
                 xk[u] = R[KDA_BR_KN + e];
                 xu[u] = R[KDA_BR_U + e];
-                xq[u] = R[KDA_BR_QN + e];
             }
 #pragma unroll
             for (int u = 0; u < 8; u++) {
-                const int e = e0 + u * NTG, i = e >> 7, cc = e & 127;
+                const int e = e0 + u * NTG;
                 DO[e] = xo[u];
                 XU[e] = xb[u] * xv[u];
                 XW[e] = xb[u] * xk[u] * exp2_fast(xg[u] * LOG2E_F);
                 D[e] = xu[u];
-                sG[i * LDK + cc] = xg[u] * LOG2E_F;
-                sK[i * LDK + cc] = xk[u];
-                sQ[i * LDK + cc] = xq[u];
             }
         }
         if (t < KDA_CHUNK) sBeta[t] = R[KDA_BR_BETA + t];
         __syncthreads();
 
         /* s1: D = U - W S, dD = K~ dS, dQ' = dout S^T */
-        wg_gemm<false, false, KDA_DV, KDA_DK>(D, R + KDA_BR_W, S0, -1.f, true);
-        wg_gemm<false, false, KDA_DV, KDA_DK>(dD, R + KDA_BR_KT, dS, 1.f, false);
-        wg_gemm<false, true, KDA_DK, KDA_DV>(dQp, DO, S0, 1.f, false);
+        wg_gemm<false, false, KDA_DV, KDA_DK>(D, R + KDA_BR_W, S0, -1.f, true, stage);
+        wg_gemm<false, false, KDA_DV, KDA_DK>(dD, R + KDA_BR_KT, dS, 1.f, false, stage);
+        wg_gemm<false, true, KDA_DK, KDA_DV>(dQp, DO, S0, 1.f, false, stage);
         __syncthreads();
 
         /* s2: dW = -dD S^T, dK~ = D dS^T, dP = dout U^T, dU = P^T dout */
-        wg_gemm<false, true, KDA_DK, KDA_DV>(dW, dD, S0, -1.f, false);
-        wg_gemm<false, true, KDA_DK, KDA_DV>(dKt, D, dS, 1.f, false);
-        wg_gemm<false, true, KDA_CHUNK, KDA_DV>(dP, DO, R + KDA_BR_U, 1.f, false);
-        wg_gemm<true, false, KDA_DV, KDA_CHUNK>(dU, R + KDA_BR_P, DO, 1.f, false);
+        wg_gemm<false, true, KDA_DK, KDA_DV>(dW, dD, S0, -1.f, false, stage);
+        wg_gemm<false, true, KDA_DK, KDA_DV>(dKt, D, dS, 1.f, false, stage);
+        wg_gemm<false, true, KDA_CHUNK, KDA_DV>(dP, DO, R + KDA_BR_U, 1.f, false, stage);
+        wg_gemm<true, false, KDA_DV, KDA_CHUNK>(dU, R + KDA_BR_P, DO, 1.f, false, stage);
         __syncthreads();
 
         /* s3: Q' = scale q^ e^G - P W: dP -= dQ' W^T, dW -= P^T dQ'; dU += dD */
-        wg_gemm<false, true, KDA_CHUNK, KDA_DK>(dP, dQp, R + KDA_BR_W, -1.f, true);
-        wg_gemm<true, false, KDA_DK, KDA_CHUNK>(dW, R + KDA_BR_P, dQp, -1.f, true);
+        wg_gemm<false, true, KDA_CHUNK, KDA_DK>(dP, dQp, R + KDA_BR_W, -1.f, true, stage);
+        wg_gemm<true, false, KDA_DK, KDA_CHUNK>(dW, R + KDA_BR_P, dQp, -1.f, true, stage);
         for (int e = t; e < KDA_CHUNK * KDA_DV; e += NTG) dU[e] += dD[e];
         __syncthreads();
 
         /* s4: dT = dW X_W^T (+ dU X_U^T below), dX_W = T^T dW, dX_U = T^T dU; masked dP to LDS */
-        wg_gemm<false, true, KDA_CHUNK, KDA_DK>(dT, dW, XW, 1.f, false);
-        wg_gemm<true, false, KDA_DK, KDA_CHUNK>(dXW, R + KDA_BR_T, dW, 1.f, false);
-        wg_gemm<true, false, KDA_DV, KDA_CHUNK>(dXU, R + KDA_BR_T, dU, 1.f, false);
+        wg_gemm<false, true, KDA_CHUNK, KDA_DK>(dT, dW, XW, 1.f, false, stage);
+        wg_gemm<true, false, KDA_DK, KDA_CHUNK>(dXW, R + KDA_BR_T, dW, 1.f, false, stage);
+        wg_gemm<true, false, KDA_DV, KDA_CHUNK>(dXU, R + KDA_BR_T, dU, 1.f, false, stage);
         for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NTG) {
             const int i = e >> 6, jj = e & 63;
             sdP[i * LDT + jj] = jj <= i ? scale * dP[e] : 0.f; /* scale folded in */
         }
         __syncthreads();
-        wg_gemm<false, true, KDA_CHUNK, KDA_DV>(dT, dU, XU, 1.f, true);
+        wg_gemm<false, true, KDA_CHUNK, KDA_DV>(dT, dU, XU, 1.f, true, stage);
         __syncthreads();
 
         /* s5: X1 = T^T dT */
-        wg_gemm<true, false, KDA_CHUNK, KDA_CHUNK>(X1, R + KDA_BR_T, dT, 1.f, false);
+        wg_gemm<true, false, KDA_CHUNK, KDA_CHUNK>(X1, R + KDA_BR_T, dT, 1.f, false, stage);
         __syncthreads();
 
         /* s6: dA = -X1 T^T (into dT, which is no longer needed), kept on the strict lower triangle */
-        wg_gemm<false, true, KDA_CHUNK, KDA_CHUNK>(dT, X1, R + KDA_BR_T, -1.f, false);
+        wg_gemm<false, true, KDA_CHUNK, KDA_CHUNK>(dT, X1, R + KDA_BR_T, -1.f, false, stage);
         /* s6b: d G_L from the carried decay: e^{G_L} sum_j dS[r][j] S[r][j]; thread t takes
          * row t / 4, columns 32 (t % 4) .. + 31 as 16-byte pieces */
         {
@@ -873,6 +880,25 @@ kda_bwd_grad_kernel(const uint16_t *__restrict__ v, const uint16_t *__restrict__
         for (int e = t; e < KDA_CHUNK * KDA_CHUNK; e += NTG) {
             const int i = e >> 6, jj = e & 63;
             sdA[i * LDT + jj] = jj < i ? dT[e] : 0.f;
+        }
+        /* s6c: the products are done with the staging LDS: G (in log2 units), k^ and
+         * q^ go there for the per-element phases, eight elements per pass */
+        for (int e0 = t; e0 < KDA_CHUNK * KDA_DK; e0 += 8 * NTG) {
+            float xg[8], xk[8], xq[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int e = e0 + u * NTG;
+                xg[u] = R[KDA_BR_G + e];
+                xk[u] = R[KDA_BR_KN + e];
+                xq[u] = R[KDA_BR_QN + e];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                const int e = e0 + u * NTG, i = e >> 7, cc = e & 127;
+                sG[i * LDK + cc] = xg[u] * LOG2E_F;
+                sK[i * LDK + cc] = xk[u];
+                sQ[i * LDK + cc] = xq[u];
+            }
         }
         __syncthreads();
 
