@@ -113,11 +113,24 @@ _ws_cache = {}
 
 
 def _workspace(nbytes, device):
+    """Workspace for a call on the current stream of ``device``.
+
+    One cached buffer per (device, stream): calls on one stream run in order and
+    may share it, calls on different streams may overlap and must not (the
+    caching allocator also ties a buffer to the stream it was allocated on, so a
+    buffer outgrown on one stream is only recycled after that stream's work).
+    During graph capture the buffer is allocated per call from the graph's
+    memory pool, which keeps it reserved for every replay.
+    """
     import torch
-    key = (str(device), )
+    stream = torch.cuda.current_stream(device)
+    n = max(nbytes, 256)
+    if torch.cuda.is_current_stream_capturing():
+        return torch.empty(n, dtype=torch.uint8, device=device)
+    key = (str(device), stream.cuda_stream)
     buf = _ws_cache.get(key)
-    if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if buf is None or buf.numel() < n:
+        buf = torch.empty(n, dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
 
