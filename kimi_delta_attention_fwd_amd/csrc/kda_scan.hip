@@ -25,7 +25,7 @@
  *                  accumulators.
  * wave 1 (output): out = Q' S + P U from the bf16 copy of the chunk's entering
  *                  state that wave 0 leaves in a two-slot LDS ring.
- * wave 2 (L2 warm): touches its eighth of the record four chunks ahead with
+ * wave 2 (L2 warm): touches its eighth of the record three chunks ahead with
  *                  LDS-DMA loads into a scratch LDS buffer, so that the eight
  *                  workgroups of a chain find their records in L2.
  * The three waves meet at one barrier per chunk. Waves 0 and 1 double-buffer
@@ -167,7 +167,10 @@ __device__ __forceinline__ void warm_l2(const unsigned char *p, uint32_t lds_add
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(lds_addr) : "memory", "m0");
 }
 
-#define KDA_WARM_AHEAD 4
+/* chunks between the one a workgroup computes and the one its warming wave
+   touches (long prefill scan: 2 or 3 -> 1.021 ms, 4 -> 1.038, 6 -> 1.106,
+   8 -> 1.150) */
+#define KDA_WARM_AHEAD 3
 
 /* the scan body; SEG instantiates the segment-parallel rescan (one workgroup per
    (chain, segment, tile)), which the plain kernel compiles without */
