@@ -235,10 +235,13 @@ def chunk_twin(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound,
                 la = gate_log_alpha(gf[c0:c1, h], dtb[h], alog[h], lower_bound)
                 G = np.cumsum(la, axis=0)
                 Kc, Qc, Vc, bc = kf[c0:c1, h], qf[c0:c1, h], vf[c0:c1, h], bf[c0:c1, h]
-                E = np.exp(G[:, None, :] - G[None, :, :])      # [L, L, K], valid for j <= r
-                tril = np.tril(np.ones((L, L)), -1)
-                A = bc[:, None] * np.einsum("rc,jc,rjc->rj", Kc, Kc, np.where(tril[:, :, None] > 0, E, 0.0))
-                Pm = np.einsum("rc,jc,rjc->rj", Qc, Kc, np.where((tril + np.eye(L))[:, :, None] > 0, E, 0.0))
+                # pairwise decay e^{G_r - G_j} for j <= r only (the exponent is <= 0
+                # there); pairs j > r get exponent -inf, i.e. factor 0
+                causal = np.tril(np.ones((L, L), dtype=bool))
+                E = np.exp(np.where(causal[:, :, None], G[:, None, :] - G[None, :, :], -np.inf))  # [L, L, K]
+                strict = np.tril(np.ones((L, L), dtype=bool), -1)
+                A = bc[:, None] * np.einsum("rc,jc,rjc->rj", Kc, Kc, np.where(strict[:, :, None], E, 0.0))
+                Pm = np.einsum("rc,jc,rjc->rj", Qc, Kc, E)
                 Tm = np.linalg.inv(np.eye(L) + A)
                 W = Tm @ (bc[:, None] * Kc * np.exp(G))
                 U = Tm @ (bc[:, None] * Vc)
@@ -257,8 +260,14 @@ def chunk_twin(q, k, v, g, beta, scale, A_log, dt_bias, lower_bound,
     return res
 
 
+# ---------------------------------------------------------------------------
+# acceptance arithmetic (the tolerance bar: relative L2 and largest absolute
+# error per tensor, plus a per-row relative error that no single wrong row of
+# a large tensor can pass)
+# ---------------------------------------------------------------------------
+
 def rel_l2(x, ref):
-    """||x - ref||_2 / ||ref||_2 over the whole tensor, in fp64."""
+    """||x - ref||_2 / ||ref||_2 over the whole tensor, in fp64 (||x||_2 if ref is 0)."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     den = np.linalg.norm(ref.ravel())
@@ -269,4 +278,32 @@ def rel_l2(x, ref):
 
 
 def max_abs(x, ref):
+    """max |x - ref| over the whole tensor, in fp64 (0 for empty tensors)."""
     return float(np.max(np.abs(np.asarray(x, dtype=np.float64) - np.asarray(ref, dtype=np.float64)))) if np.size(ref) else 0.0
+
+
+def row_rel_l2(x, ref, row_ndim=1, floor=0.25):
+    """Largest relative L2 error over rows, and the row where it occurs.
+
+    A row is a slice over the trailing ``row_ndim`` axes (the 128 values of one
+    token and head for ``out``; the K x V block of one sequence and head for a
+    state). Row r's error is ||x_r - ref_r||_2 / max(||ref_r||_2, floor * R),
+    where R is the root mean square of the reference row norms, so rows whose
+    reference is near zero are measured against a fraction of a typical row.
+    Returns (error, flat row index); (0.0, -1) for empty tensors.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0, -1
+    n = int(np.prod(ref.shape[ref.ndim - row_ndim:]))
+    d = (x - ref).reshape(-1, n)
+    r = ref.reshape(-1, n)
+    dn = np.sqrt(np.sum(d * d, axis=1))
+    rn = np.sqrt(np.sum(r * r, axis=1))
+    rms = np.sqrt(np.mean(rn * rn))
+    den = np.maximum(rn, floor * rms)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        e = np.where(den > 0, dn / np.where(den > 0, den, 1.0), np.where(dn > 0, np.inf, 0.0))
+    i = int(np.argmax(e))
+    return float(e[i]), i

@@ -1,10 +1,19 @@
 """GPU parity of libkda (through its C ABI) against the fp64 oracle.
 
 Bar (fixed before measuring): per tensor, relative L2 error <= 1e-2 and max
-absolute error <= 5e-2 for ``out`` and, where returned, ``final_state``; exact
-(bitwise) equality where the chunking makes two computations identical
-(varlen vs separate calls, batch vs separate calls, chained calls split at a
-multiple of 64 with an fp32 state, repeated calls).
+absolute error <= 5e-2 for ``out`` and, where returned, ``final_state``; per
+row (the 128 outputs of one token and head, or the 128 x 128 final state of one
+sequence and head), relative L2 error <= 5e-2 against the row's reference norm,
+floored at a quarter of the root-mean-square row norm; exact (bitwise) equality
+where the chunking makes two computations identical (varlen vs separate calls,
+batch vs separate calls, chained calls split at a multiple of 64 with an fp32
+state, repeated calls).
+
+The per-row bound: an element of ``out`` is a sum of bf16-rounded products
+(relative rounding 2^-9 per operand), so a correct row carries a relative error
+of a few 1e-3, as the whole tensor does; 5e-2 leaves an order of magnitude for
+cancellation and accumulation over chunks, while a wrong, stale or unwritten row
+(relative error about 1) fails it however large the tensor is.
 """
 import math
 import os
@@ -21,6 +30,7 @@ pytestmark = pytest.mark.gpu
 
 REL_TOL = 1e-2
 ABS_TOL = 5e-2
+ROW_TOL = 5e-2
 
 
 def _gpu():
@@ -30,34 +40,35 @@ def _gpu():
     return gpu_util
 
 
-def check(name, got, ref):
+def check(name, got, ref, row_ndim=1):
+    """The tensor bar and the per-row bound; rows span the trailing row_ndim axes."""
     rel = oracle.rel_l2(got, ref)
     mab = oracle.max_abs(got, ref)
-    print("%-28s rel_l2=%.3e max_abs=%.3e" % (name, rel, mab), flush=True)
+    row, at = oracle.row_rel_l2(got, ref, row_ndim=row_ndim)
+    print("%-28s rel_l2=%.3e max_abs=%.3e row_max=%.3e (row %d)" % (name, rel, mab, row, at), flush=True)
     assert np.all(np.isfinite(got)), name + ": non-finite values"
     assert rel <= REL_TOL and mab <= ABS_TOL, (name, rel, mab)
+    assert row <= ROW_TOL, (name, "row", at, row)
+
+
+def check_state(name, got, ref):
+    """check() with one row per (sequence, head) state block."""
+    check(name, got, ref, row_ndim=2)
 
 
 # ---------------------------------------------------------------- workloads
 # full-size workloads run on the GPU exactly as the bench launches them; the
-# oracle recomputes a sample of heads (chains are independent per head)
-SAMPLE_HEADS = {0: None, 1: None, 2: [0, 13, 31], 3: [0, 9, 31], 4: [0, 33, 63]}
-
-
+# oracle recomputes every head, token and state
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_workload_parity(cfg):
     gu = _gpu()
     print("workload %d" % cfg, flush=True)
     d = ki.config_inputs(cfg)
     o, f = gu.run_gpu(d)
-    heads = SAMPLE_HEADS[cfg]
-    ds = d if heads is None else gu.subset_heads(d, heads)
-    ro, rf = oracle.fwd_inputs(ds, want_final=d["final"])
-    og = o if heads is None else o[:, :, heads]
-    check("cfg%d out" % cfg, og, ro)
+    ro, rf = oracle.fwd_inputs(d, want_final=d["final"])
+    check("cfg%d out" % cfg, o, ro)
     if d["final"]:
-        fg = f if heads is None else f[:, heads]
-        check("cfg%d final_state" % cfg, fg, rf)
+        check_state("cfg%d final_state" % cfg, f, rf)
 
 
 # ---------------------------------------------------------------- edge cases
@@ -68,7 +79,7 @@ def test_ragged_lengths(T):
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("T=%d out" % T, o, ro)
-    check("T=%d final" % T, f, rf)
+    check_state("T=%d final" % T, f, rf)
 
 
 @pytest.mark.parametrize("state", ["bf16", "fp32"])
@@ -79,7 +90,7 @@ def test_varlen_with_empty_and_single(state):
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("varlen %s out" % state, o, ro)
-    check("varlen %s final" % state, f, rf)
+    check_state("varlen %s final" % state, f, rf)
     # empty sequences pass the state through (bf16 -> fp32 -> bf16 is exact)
     init = d["initial_state"]
     init64 = ki.bf16_bits_to_f64(init) if state == "bf16" else init.astype(np.float64)
@@ -92,7 +103,7 @@ def test_no_state_and_final_only():
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("final-only out", o, ro)
-    check("final-only final", f, rf)
+    check_state("final-only final", f, rf)
     d2 = ki.make_inputs(1, 300, 2, seed=6)
     o2, f2 = gu.run_gpu(d2)
     assert f2 is None and np.array_equal(o2, o)
@@ -107,7 +118,7 @@ def test_lower_bound_range(lb):
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("lb=%g out" % lb, o, ro)
-    check("lb=%g final" % lb, f, rf)
+    check_state("lb=%g final" % lb, f, rf)
 
 
 def test_maximum_sizes():
@@ -119,13 +130,13 @@ def test_maximum_sizes():
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("T=2^20+3 out", o, ro)
-    check("T=2^20+3 final", f, rf)
+    check_state("T=2^20+3 final", f, rf)
     del d, o, ro
     d = ki.make_inputs(1, 300, 256, seed=29, state="bf16", initial=True, sigma=0.05)
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("H=256 out", o, ro)
-    check("H=256 final", f, rf)
+    check_state("H=256 final", f, rf)
 
 
 def test_unnormalised_inputs():
@@ -139,7 +150,7 @@ def test_unnormalised_inputs():
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("unnormalised out", o, ro)
-    check("unnormalised final", f, rf)
+    check_state("unnormalised final", f, rf)
 
 
 # ---------------------------------------------------------------- exact invariants
@@ -174,7 +185,7 @@ def test_many_chain_scan(state):
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("many-chain %s out" % state, o, ro)
-    check("many-chain %s final" % state, f, rf)
+    check_state("many-chain %s final" % state, f, rf)
     cu = d["cu_seqlens"]
     for n in range(len(lens)):
         a, b = int(cu[n]), int(cu[n + 1])
@@ -200,7 +211,7 @@ def test_many_sequences_chunk_table():
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("3000 seqs out", o, ro)
-    check("3000 seqs final", f, rf)
+    check_state("3000 seqs final", f, rf)
 
 
 def test_many_chain_fixed_batch():
@@ -211,7 +222,7 @@ def test_many_chain_fixed_batch():
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("fixed-batch out", o, ro)
-    check("fixed-batch final", f, rf)
+    check_state("fixed-batch final", f, rf)
     for b in (0, 17, 63):
         e = dict(d)
         for key in ("q", "k", "v", "g", "beta"):
@@ -238,7 +249,7 @@ def test_segmented_scan(B, T, H, state):
     ro, rf = oracle.fwd_inputs(d, want_final=d["final"])
     check("segmented B=%d T=%d H=%d out" % (B, T, H), o, ro)
     if d["final"]:
-        check("segmented B=%d T=%d H=%d final" % (B, T, H), f, rf)
+        check_state("segmented B=%d T=%d H=%d final" % (B, T, H), f, rf)
     # the same batch as packed sequences (cu_seqlens): the plain scan
     e = dict(d)
     for key in ("q", "k", "v", "g", "beta"):
@@ -261,7 +272,7 @@ def test_segmented_scan_packed(lens, H, state):
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("segmented packed %s out" % lens, o, ro)
-    check("segmented packed %s final" % lens, f, rf)
+    check_state("segmented packed %s final" % lens, f, rf)
     n, t = len(lens), sum(lens)
     e = ki.make_inputs(1, t + 5, H, seed=27, lengths=lens + [1] * 5, state=state, initial=True, sigma=0.05)
     for key in ("q", "k", "v", "g", "beta"):
@@ -314,7 +325,7 @@ def test_segmented_long_memory(packed):
     o, f = gu.run_gpu(d)
     ro, rf = oracle.fwd_inputs(d, want_final=True)
     check("long-memory %s out" % ("packed" if packed else "batch"), o, ro)
-    check("long-memory %s final" % ("packed" if packed else "batch"), f, rf)
+    check_state("long-memory %s final" % ("packed" if packed else "batch"), f, rf)
     # the plain scan: the same sequences plus 5 one-token sequences (more than 10 chains)
     ls = lens if packed else [8192]
     n, t = len(ls), sum(ls)
@@ -372,7 +383,7 @@ def test_state_chaining(split):
         assert np.array_equal(oc, o) and np.array_equal(f2, f)
     else:
         check("chain out", oc, o)
-        check("chain final", f2, f)
+        check_state("chain final", f2, f)
 
 
 def test_in_place_state():

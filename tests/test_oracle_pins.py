@@ -318,3 +318,71 @@ def test_bf16_inputs_match_f64_path():
                         d["A_log"], d["dt_bias"], d["lower_bound"],
                         initial_state=w(d["initial_state"]))
     assert np.array_equal(o, o2) and np.array_equal(f, f2)
+
+
+# ---------------------------------------------------------------------------
+# Acceptance arithmetic. The tolerance bar (relative L2 and largest absolute
+# error per tensor) and the per-row bound are themselves pinned on vectors whose
+# results are worked out by hand, so a missing abs(), a norm taken over the
+# candidate instead of the reference, or a row slice along the wrong axis fails.
+# ---------------------------------------------------------------------------
+def test_rel_l2_hand_values():
+    ref = np.array([3.0, 4.0])                      # ||ref|| = 5
+    assert oracle.rel_l2(np.array([3.0, 4.0]), ref) == 0.0
+    assert oracle.rel_l2(np.array([3.0, 5.0]), ref) == pytest.approx(1.0 / 5.0, rel=1e-15)
+    assert oracle.rel_l2(np.array([3.0, 3.0]), ref) == pytest.approx(1.0 / 5.0, rel=1e-15)  # sign of the deviation
+    # normalised by the reference, not the candidate: x = 2 ref gives ||ref|| / ||ref|| = 1
+    assert oracle.rel_l2(2.0 * ref, ref) == pytest.approx(1.0, rel=1e-15)
+    assert oracle.rel_l2(0.5 * ref, ref) == pytest.approx(0.5, rel=1e-15)
+    # a zero reference falls back to ||x||
+    assert oracle.rel_l2(np.array([0.0, 2.0]), np.zeros(2)) == pytest.approx(2.0, rel=1e-15)
+    assert oracle.rel_l2(np.zeros(3), np.zeros(3)) == 0.0
+    # whole-tensor norms: [[1, 0], [0, 1]] against [[1, 1], [1, 1]] -> sqrt(2) / 2
+    assert oracle.rel_l2(np.eye(2), np.ones((2, 2))) == pytest.approx(math.sqrt(2.0) / 2.0, rel=1e-15)
+
+
+def test_max_abs_hand_values():
+    ref = np.array([1.0, -2.0, 0.5])
+    assert oracle.max_abs(ref, ref) == 0.0
+    assert oracle.max_abs(np.array([1.0, -2.5, 0.5]), ref) == pytest.approx(0.5)    # negative deviation
+    assert oracle.max_abs(np.array([1.25, -2.0, 0.0]), ref) == pytest.approx(0.5)   # largest of 0.25 and 0.5
+    assert oracle.max_abs(np.array([[0.0, 3.0]]), np.array([[0.0, -1.0]])) == pytest.approx(4.0)
+    assert oracle.max_abs(np.zeros(0), np.zeros(0)) == 0.0
+
+
+def test_row_rel_l2_hand_values():
+    ref = np.array([[3.0, 4.0], [0.0, 5.0], [5.0, 0.0]])    # every row norm 5, rms 5
+    e, i = oracle.row_rel_l2(ref, ref)
+    assert e == 0.0
+    x = ref.copy()
+    x[1, 1] = 4.0                                            # row 1 off by 1 -> 1 / 5
+    e, i = oracle.row_rel_l2(x, ref)
+    assert i == 1 and e == pytest.approx(0.2, rel=1e-15)
+    # the whole-tensor error of the same deviation is diluted: 1 / sqrt(75)
+    assert oracle.rel_l2(x, ref) == pytest.approx(1.0 / math.sqrt(75.0), rel=1e-15)
+    # one zero row among unit rows: measured against floor * rms
+    ref2 = np.array([[1.0, 0.0], [0.0, 1.0], [0.0, 0.0], [1.0, 0.0]])   # rms of norms = sqrt(3/4)
+    x2 = ref2.copy()
+    x2[2] = [0.1, 0.0]
+    e, i = oracle.row_rel_l2(x2, ref2, floor=0.25)
+    assert i == 2 and e == pytest.approx(0.1 / (0.25 * math.sqrt(0.75)), rel=1e-12)
+    # rows over two trailing axes (a state block per sequence and head)
+    refs = np.ones((2, 3, 2, 2))
+    xs = refs.copy()
+    xs[1, 2, 0, 1] = 3.0                                    # block (1, 2): ||d|| = 2, ||ref|| = 2
+    e, i = oracle.row_rel_l2(xs, refs, row_ndim=2)
+    assert i == 1 * 3 + 2 and e == pytest.approx(1.0, rel=1e-15)
+    assert oracle.row_rel_l2(np.zeros((0, 4)), np.zeros((0, 4))) == (0.0, -1)
+
+
+def test_chunk_twin_no_overflow_at_strong_decay():
+    """The twin forms the pairwise decay only for j <= r, where the exponent is <= 0,
+    so a very negative lower_bound raises no floating-point overflow."""
+    rng = np.random.default_rng(31)
+    d = rand_inputs(rng, 1, 96, 1, K=16, V=8, lb=-200.0)
+    d["A_log"] = np.array([math.log(16.0)])
+    with np.errstate(over="raise", invalid="raise"):
+        ot, ft = oracle.chunk_twin(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], d["A_log"],
+                                   d["dt_bias"], d["lower_bound"], initial_state=d["initial_state"])
+    o, f = run(d)
+    assert oracle.rel_l2(ot, o) < 1e-12 and oracle.rel_l2(ft, f) < 1e-12
