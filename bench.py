@@ -6,11 +6,15 @@ one batch of seeded synthetic inputs already resident in HBM. The default
 workload is the long prefill: B = 1, T = 65536, H = 32, K = V = 128, bf16
 activations, lower_bound = -3, fp32 final state, no initial state.
 
-Prints one JSON line with the throughput (token*heads/s), the roofline of the
-dominant kernel (its algorithmic HBM bytes per launch over its mean duration,
-timed live with hipEvents on the launch stream), the roofline of the whole step,
-and the fp64 oracle timed on this host's cores on a bounded prefix of the same
-workload; the oracle's output on that prefix is also compared with the GPU's.
+Prints one JSON line with the throughput (token*heads/s) of K uninstrumented
+steps, the HBM roofline of the step (its algorithmic bytes, 1,282 per token-head
+plus the state tensors, over the step's mean duration between hipEvents on the
+launch stream; the counter-measured HBM bytes of all its kernels beside them),
+per-kernel figures from a second, instrumented pass, and the fp64 oracle timed on
+this host's cores on the same workload; the oracle's output is also compared
+with the GPU's. Workloads small enough for the 256 MB Infinity Cache to keep
+between steps are timed one step at a time after a 512 MiB write (--warm skips
+that).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 0..4]
 """
@@ -53,6 +57,25 @@ FLOPS_PER_TH = 6 * 128 * 128 + 2 * 64 * (3 * 128 + 2 * 128)
 PEAK_FP32_TFLOPS = 157.3
 BWD_GRAD_FLOPS_PER_TH = (2 * (5 * 64 * 128 * 128 + 8 * 64 * 64 * 128 + 64 ** 3 + 64 ** 3 // 2)
                          + 17 * (64 * 65 // 2) * 128) / 64.0
+
+
+# Infinity Cache (MALL) of the MI355X
+MALL_BYTES = 256 << 20
+# the long-prefill scan's kernel time in the committed kernel-stats profile; the
+# bench flags a run where it is more than 3 % slower (its warming loop's place
+# relative to instruction-fetch blocks moved it by up to 6 %)
+SCAN_REF_MS = {"long_prefill": 1.021}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def state_bytes(d):
@@ -106,6 +129,8 @@ def main():
                     help="keep only the first N heads of the workload (one GPU's share when heads are sharded)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run 3 device copies of this many MiB (counter calibration)")
+    ap.add_argument("--warm", action="store_true",
+                    help="never flush the Infinity Cache between steps (small workloads are flushed by default)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -161,25 +186,58 @@ def main():
         kda.fwd(q, k, v, g, beta, d["scale"], out, A_log, dt_bias, d["lower_bound"],
                 initial_state=init, final_state=fin, cu_seqlens=cu, workspace=ws)
 
+    th = ki.token_heads(d)
+    path_bytes = th * (PREP_BYTES_PER_TH + SCAN_BYTES_PER_TH) + state_bytes(d)
+    # The 256 MB Infinity Cache (MALL) keeps a small workload's inputs between
+    # steps. Working sets below twice its size are timed one step at a time with
+    # a 512 MiB write between steps (outside the timed events), unless --warm.
+    flush = (not args.warm) and (path_bytes + ws.numel() < 2 * MALL_BYTES)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    kda.profile_enable(True)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
+    if not flush:
+        # the timed region: K uninstrumented steps, synchronised on both sides
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record()
+        for _ in range(args.steps):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        event_ms = ev0.elapsed_time(ev1) / args.steps
+        ms_per_step = wall / args.steps * 1e3
+        ws_bytes = path_bytes + ws.numel()
+        mall = ("cold: the step moves %.2f GB, more than twice the 256 MB Infinity Cache" % (ws_bytes / 1e9)
+                if ws_bytes >= 2 * MALL_BYTES else
+                "warm: the step's %.0f MB may stay in the 256 MB Infinity Cache between steps" % (ws_bytes / 1e6))
+    else:
+        sink = torch.empty(MALL_BYTES * 2, dtype=torch.uint8, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in evs:
+            sink.fill_(1)
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        event_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+        ms_per_step = event_ms
+        mall = "flushed: a 512 MiB write before each step, steps timed one by one with events"
+        del sink
+    value = th / (ms_per_step * 1e-3)
+
+    # per-kernel times: a second pass of K steps with the library's own events
+    # around each kernel (not part of the timed region above)
+    kda.profile_enable(True)
     for _ in range(args.steps):
         step()
-    ev1.record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
     kda.profile_enable(False)
     prof = kda.profile_read()
-    wall = t1 - t0
-    ms_per_step = wall / args.steps * 1e3
-    th = ki.token_heads(d)
-    value = th * args.steps / wall
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -189,17 +247,27 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # per-kernel live timing (hipEvents on the launch stream)
     kernels = {name: tot / cnt for name, (tot, cnt) in prof.items()}
     alg_bytes = {"kda_prep": th * PREP_BYTES_PER_TH,
                  "kda_scan": th * SCAN_BYTES_PER_TH + state_bytes(d),
                  "kda_chunk_map": 0}
+    per_kernel = {}
+    for name, ms in kernels.items():
+        per_kernel[name] = {"ms": ms, "alg_bytes": alg_bytes.get(name, 0),
+                            "frac_hbm": alg_bytes.get(name, 0) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                            "traffic": measured_traffic(name, d["name"])}
     dom = max(kernels, key=kernels.get)
-    dom_ms = kernels[dom]
-    achieved = alg_bytes.get(dom, 0) / (dom_ms * 1e-3) / 1e9
-    path_bytes = th * (PREP_BYTES_PER_TH + SCAN_BYTES_PER_TH) + state_bytes(d)
-    path_gbs = path_bytes / (ms_per_step * 1e-3) / 1e9
-    path_tflops = th * FLOPS_PER_TH / (ms_per_step * 1e-3) / 1e12
+    # counter-measured HBM bytes of the whole step: every kernel of the call must
+    # have a figure for the current sources (the chunk map moves a few KB)
+    traffic = 0.0
+    for name in kernels:
+        t = per_kernel[name]["traffic"]
+        if t is None and name != "kda_chunk_map":
+            traffic = None
+            break
+        traffic += t or 0.0
+    achieved = path_bytes / (event_ms * 1e-3) / 1e9
+    path_tflops = th * FLOPS_PER_TH / (event_ms * 1e-3) / 1e12
 
     res = {
         "metric": METRIC,
@@ -218,15 +286,28 @@ def main():
             d["name"], B, T, H, d["lower_bound"], d["state_dtype"],
             " varlen N=%d" % d["N"] if cu is not None else ""),
             "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU"},
+        # the unit of the roofline is one whole kda_fwd call (all of its kernels):
+        # the algorithmic bytes of the step (1,282 B per token-head plus the state
+        # tensors) over the step's mean duration between hipEvents on the launch
+        # stream in the timed region
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(dom, d["name"]), "kernel": dom,
-                     "kernel_ms": dom_ms, "alg_bytes_per_launch": alg_bytes.get(dom, 0)},
-        "kernels_ms": kernels,
-        "path_roofline": {"bound": "hbm", "alg_bytes_per_step": path_bytes, "achieved_GBs": path_gbs,
-                          "frac_hbm": path_gbs / PEAK_HBM_GBS, "achieved_TFLOPs": path_tflops,
-                          "frac_mfma": path_tflops / PEAK_BF16_TFLOPS},
-        "event_ms_per_step": ev0.elapsed_time(ev1) / args.steps,
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "traffic_ratio": None if traffic is None else traffic / path_bytes,
+                     "kernel": "kda_fwd step (%s)" % ", ".join(sorted(kernels)),
+                     "launch_ms": event_ms, "alg_bytes_per_launch": path_bytes,
+                     "mfma_frac": path_tflops / PEAK_BF16_TFLOPS},
+        "kernels": per_kernel,
+        "dominant_kernel": dom,
+        "mall": mall,
+        "event_ms_per_step": event_ms,
     }
+    ref = SCAN_REF_MS.get(d["name"])
+    if ref is not None and "kda_scan" in kernels:
+        res["scan_placement_check"] = {"ref_ms": ref, "ms": kernels["kda_scan"],
+                                       "ok": kernels["kda_scan"] <= 1.03 * ref}
+        if kernels["kda_scan"] > 1.03 * ref:
+            print("[bench] warning: kda_scan took %.3f ms, more than 3%% over its reference %.3f ms (instruction "
+                  "placement of its warming loop?)" % (kernels["kda_scan"], ref), file=sys.stderr, flush=True)
 
     if not args.no_cpu:
         import oracle
@@ -248,7 +329,7 @@ def main():
         sample_th = ki.token_heads(sub)
         got = out[:, :sub["T"]].float().cpu().numpy()
         res["cpu_baseline"] = {"value": reps * sample_th / tc, "unit": "token*heads/s", "cores": threads,
-                               "kind": "oracle",
+                               "kind": "oracle", "cpu": cpu_model(),
                                "sample": "fp64 per-token recurrence on %s (%d tokens x %d heads = %d token-heads), "
                                          "%d passes in %.1f s" % (
                                              "the whole workload" if sub["T"] == T else
@@ -331,7 +412,7 @@ def run_decode(args):
             tc += time.perf_counter() - tc0
             reps += 1
         res["cpu_baseline"] = {"value": reps * units / tc, "unit": "token*heads/s", "cores": oracle.max_threads(),
-                               "kind": "oracle", "sample": "fp64 recurrence on the whole workload (%d "
+                               "kind": "oracle", "cpu": cpu_model(), "sample": "fp64 recurrence on the whole workload (%d "
                                "token-heads), %d passes in %.1f s" % (units, reps, tc)}
         # parity of one step from the initial state
         state.copy_(state0)
@@ -443,6 +524,7 @@ def run_backward(args):
                 tc += time.perf_counter() - tc0
                 reps += 1
         res["cpu_baseline"] = {"value": reps * ts * H / tc, "unit": "token*heads/s", "cores": 1, "kind": "oracle",
+                               "cpu": cpu_model(),
                                "sample": "fp64 per-token reverse pass on the first %d tokens of sequence 0, all %d "
                                "heads, %d passes in %.1f s" % (ts, H, reps, tc)}
     print(json.dumps(res), flush=True)

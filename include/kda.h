@@ -135,8 +135,14 @@ KDA_API int kda_fwd(const void *q, const void *k, const void *v, const void *g,
 
 /*
  * kda_fwd_workspace_size -- bytes of workspace kda_fwd needs (host only).
+ *  In the pages' call ("Core Kernel API / flash_kda.fwd", ccm-staging page) the
+ *  caller hands in every result buffer (out, final_state); libkda keeps that
+ *  convention for the scratch its chunked kernels pass between them, which is
+ *  one more caller-owned buffer whose size this call reports (chunk table,
+ *  per-chunk records, segment maps of the segment-parallel scan).
  *  num_seqs = 0 means no cu_seqlens (N = B); otherwise B must be 1 and T is the
- *  packed token count. Returns 0 for invalid sizes.
+ *  packed token count. Returns 0 for invalid sizes (those kda_fwd rejects with
+ *  KDA_ERR_SHAPE).
  */
 KDA_API size_t kda_fwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t num_seqs);
 
@@ -206,7 +212,12 @@ KDA_API int kda_bwd(const void *q, const void *k, const void *v, const void *g,
  * as for kda_fwd_workspace_size, 0 for invalid sizes. */
 KDA_API size_t kda_bwd_workspace_size(int64_t B, int64_t T, int64_t H, int64_t num_seqs);
 
-/* Static, NUL-terminated description of a kda_status code (host only). */
+/* kda_status_string -- static, NUL-terminated description of a kda_status code
+ * (host only; "unknown kda status" for other values). The pages' debugging
+ * advice ("Accuracy Verification and Debugging", trend.ondo.sh page) is to log
+ * whether the fast kernel was selected or why a call was rejected; these
+ * strings state the reason for each rejection, and the Python binding raises
+ * them as its error messages. */
 KDA_API const char *kda_status_string(int status);
 
 /*

@@ -17,7 +17,8 @@ import ctypes
 import os
 
 __all__ = ["fwd", "decode", "bwd", "workspace_size", "bwd_workspace_size", "status_string", "library_path", "load_library",
-           "profile_enable", "profile_read", "KDA_LOWER_BOUND_NARROW", "KDA_MAX_HEADS", "KdaError"]
+           "profile_enable", "profile_read", "release_workspaces", "KDA_LOWER_BOUND_NARROW", "KDA_MAX_HEADS",
+           "KdaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -110,29 +111,48 @@ def profile_read(cap: int = 8):
 
 
 _ws_cache = {}
+# backward workspaces larger than this are allocated per call and not kept
+# (the long prefill's is 13.5 GB)
+BWD_CACHE_MAX_BYTES = 1 << 30
 
 
-def _workspace(nbytes, device):
+def _workspace(nbytes, device, kind="fwd"):
     """Workspace for a call on the current stream of ``device``.
 
-    One cached buffer per (device, stream): calls on one stream run in order and
-    may share it, calls on different streams may overlap and must not (the
-    caching allocator also ties a buffer to the stream it was allocated on, so a
-    buffer outgrown on one stream is only recycled after that stream's work).
+    One cached buffer per (kind, device, stream), kind "fwd" or "bwd": calls on
+    one stream run in order and may share it, calls on different streams may
+    overlap and must not (the caching allocator also ties a buffer to the stream
+    it was allocated on, so a buffer outgrown on one stream is only recycled after
+    that stream's work). Forward and backward keep separate buffers, and a
+    backward workspace above BWD_CACHE_MAX_BYTES is not cached at all, so one
+    large backward call does not pin its workspace for the later forward calls.
     During graph capture the buffer is allocated per call from the graph's
     memory pool, which keeps it reserved for every replay.
+    ``release_workspaces`` drops the cached buffers.
     """
     import torch
     stream = torch.cuda.current_stream(device)
     n = max(nbytes, 256)
     if torch.cuda.is_current_stream_capturing():
         return torch.empty(n, dtype=torch.uint8, device=device)
-    key = (str(device), stream.cuda_stream)
+    if kind == "bwd" and n > BWD_CACHE_MAX_BYTES:
+        return torch.empty(n, dtype=torch.uint8, device=device)
+    key = (kind, str(device), stream.cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < n:
+        _ws_cache.pop(key, None)
         buf = torch.empty(n, dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf
+
+
+def release_workspaces() -> int:
+    """Drop every cached workspace buffer (their memory returns to torch's
+    caching allocator once the streams that used them are done with it).
+    Returns the number of bytes released."""
+    n = sum(int(b.numel()) for b in _ws_cache.values())
+    _ws_cache.clear()
+    return n
 
 
 def _ptr(t):
@@ -356,7 +376,7 @@ def bwd(q, k, v, g, beta, scale, dout, A_log, dt_bias, lower_bound, initial_stat
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
     need = lib.kda_bwd_workspace_size(B, T, H, num_seqs)
-    ws = _workspace(need, dev) if workspace is None else workspace
+    ws = _workspace(need, dev, "bwd") if workspace is None else workspace
     stream = torch.cuda.current_stream(dev).cuda_stream
     rc = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(dout),
                      _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state), sd,

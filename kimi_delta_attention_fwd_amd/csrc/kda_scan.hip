@@ -178,7 +178,7 @@ template <bool SEG>
 __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
                                           const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H,
                                           int64_t nslots, uint16_t *__restrict__ out,
-                                          const void *__restrict__ init_state, void *__restrict__ final_state,
+                                          const void *init_state, void *final_state,
                                           int state_fp32, const int32_t *__restrict__ long_list, int64_t nseg,
                                           int64_t segc, const float *__restrict__ seg_init)
 {
@@ -340,8 +340,8 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
 extern "C" __global__ void __launch_bounds__(192)
 kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
                 const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
-                uint16_t *__restrict__ out, const void *__restrict__ init_state,
-                void *__restrict__ final_state, int state_fp32, const int32_t *__restrict__ long_list)
+                uint16_t *__restrict__ out, const void *init_state,
+                void *final_state, int state_fp32, const int32_t *__restrict__ long_list)
 {
     scan_body<false>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state, state_fp32, long_list,
                      1, 0, nullptr);
@@ -351,7 +351,7 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
 extern "C" __global__ void __launch_bounds__(192)
 kda_scan_seg_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
                     const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
-                    uint16_t *__restrict__ out, void *__restrict__ final_state, int state_fp32, int64_t nseg,
+                    uint16_t *__restrict__ out, void *final_state, int state_fp32, int64_t nseg,
                     int64_t segc, const float *__restrict__ seg_init)
 {
     scan_body<true>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, nullptr, final_state, state_fp32, nullptr,

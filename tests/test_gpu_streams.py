@@ -206,3 +206,31 @@ def test_bwd_graph_replays():
         torch.cuda.synchronize()
         for n in NAMES:
             assert torch.equal(got[n], eager[n]), (rep, n)
+
+
+def test_workspace_cache_release():
+    """The binding caches one forward and one backward workspace per (device,
+    stream); a backward workspace above BWD_CACHE_MAX_BYTES is not kept, and
+    release_workspaces() drops every cached buffer. Results do not depend on it."""
+    gu = _gu()
+    kda.release_workspaces()
+    d = ki.make_inputs(1, 200, 2, seed=41, state="fp32", initial=True, sigma=0.05)
+    o1, f1 = gu.run_gpu(d)
+    keys = list(kda._ws_cache)
+    assert len(keys) == 1 and keys[0][0] == "fwd"
+    n = kda.release_workspaces()
+    assert n >= kda.workspace_size(1, 200, 2) and not kda._ws_cache
+    o2, f2 = gu.run_gpu(d)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+    old = kda.BWD_CACHE_MAX_BYTES
+    try:
+        kda.BWD_CACHE_MAX_BYTES = 0  # every backward workspace counts as large
+        t = gu.dev_inputs(d)
+        dout = torch.ones((1, 200, 2, 128), dtype=torch.bfloat16, device=gu.DEV)
+        kda.bwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], dout, t["A_log"], t["dt_bias"],
+                d["lower_bound"], initial_state=t["initial_state"])
+        torch.cuda.synchronize()
+        assert all(key[0] == "fwd" for key in kda._ws_cache)
+    finally:
+        kda.BWD_CACHE_MAX_BYTES = old
+    kda.release_workspaces()
