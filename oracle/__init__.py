@@ -282,14 +282,16 @@ def max_abs(x, ref):
     return float(np.max(np.abs(np.asarray(x, dtype=np.float64) - np.asarray(ref, dtype=np.float64)))) if np.size(ref) else 0.0
 
 
-def row_rel_l2(x, ref, row_ndim=1, floor=0.25):
+def row_rel_l2(x, ref, row_ndim=1, floor=1.0):
     """Largest relative L2 error over rows, and the row where it occurs.
 
     A row is a slice over the trailing ``row_ndim`` axes (the 128 values of one
     token and head for ``out``; the K x V block of one sequence and head for a
     state). Row r's error is ||x_r - ref_r||_2 / max(||ref_r||_2, floor * R),
-    where R is the root mean square of the reference row norms, so rows whose
-    reference is near zero are measured against a fraction of a typical row.
+    where R is the root mean square of the reference row norms: a row is
+    measured against its own norm, or against a typical row where cancellation
+    has made its own norm small (the rounding error of a row follows the size of
+    the operands that formed it, not the size of the result).
     Returns (error, flat row index); (0.0, -1) for empty tensors.
     """
     x = np.asarray(x, dtype=np.float64)
