@@ -68,7 +68,9 @@ typedef enum {
                                 than kda_fwd_workspace_size                        */
     KDA_ERR_ALIAS = 7,       /* out overlaps an input, or the states overlap only
                                 partially                                          */
-    KDA_ERR_HIP = 8          /* a HIP launch/runtime error after validation         */
+    KDA_ERR_HIP = 8,         /* a HIP launch/runtime error after validation         */
+    KDA_ERR_SCRATCH = 9      /* kda_fwd_noalloc: the call needs more workspace than
+                                KDA_NOALLOC_SCRATCH_BYTES                           */
 } kda_status;
 
 /* dtype of initial_state / final_state (one dtype for both). */
@@ -132,6 +134,36 @@ KDA_API int kda_fwd(const void *q, const void *k, const void *v, const void *g,
             void *final_state, int state_dtype, const int32_t *cu_seqlens,
             int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
             int64_t V, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kda_fwd_noalloc -- kda_fwd without a workspace argument, for callers that
+ * cannot allocate device memory at call time: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The workspace kda_fwd
+ * would take from the caller comes from a scratch array built into the library
+ * (a file-scope device array of KDA_NOALLOC_SCRATCH_BYTES, one per GPU the
+ * library runs on, held until the process ends); nothing is allocated or freed
+ * by the call. The kernels, their results and every argument rule are those of
+ * kda_fwd, and the output is the same bit for bit.
+ *
+ *  Arguments as for kda_fwd, without workspace / workspace_bytes.
+ *  Errors as for kda_fwd, plus KDA_ERR_SCRATCH (checked before any HIP call)
+ *  when kda_fwd_workspace_size(B, T, H, num_seqs) > KDA_NOALLOC_SCRATCH_BYTES,
+ *  and KDA_ERR_HIP if the scratch's device address cannot be obtained.
+ *  The first call on a GPU looks up that GPU's scratch address (the device of
+ *  `stream`, or the current device for the NULL stream).
+ *  Every call on one GPU uses that GPU's one scratch array: calls that may
+ *  overlap in time on one GPU (other streams, other host threads) race and
+ *  must be serialised by the caller; calls in order on one stream are safe.
+ *  The scratch needs no clearing between calls: every call writes each part
+ *  it reads before reading it.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+KDA_API int kda_fwd_noalloc(const void *q, const void *k, const void *v, const void *g,
+            const void *beta, float scale, void *out, const float *A_log,
+            const float *dt_bias, float lower_bound, const void *initial_state,
+            void *final_state, int state_dtype, const int32_t *cu_seqlens,
+            int64_t num_seqs, int64_t B, int64_t T, int64_t H, int64_t K,
+            int64_t V, void *stream);
 
 /*
  * kda_fwd_workspace_size -- bytes of workspace kda_fwd needs (host only).

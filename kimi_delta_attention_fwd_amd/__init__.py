@@ -16,7 +16,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "decode", "bwd", "workspace_size", "bwd_workspace_size", "status_string", "library_path", "load_library",
+__all__ = ["fwd", "fwd_noalloc", "decode", "bwd", "workspace_size", "bwd_workspace_size", "status_string", "library_path", "load_library",
            "profile_enable", "profile_read", "release_workspaces", "KDA_LOWER_BOUND_NARROW", "KDA_MAX_HEADS",
            "KdaError"]
 
@@ -27,8 +27,10 @@ _lib = None
 KDA_STATE_NONE, KDA_STATE_BF16, KDA_STATE_FP32 = 0, 1, 2
 KDA_LOWER_BOUND_NARROW = -10.0  # below it kda_fwd takes its wide-range chunk preparation
 KDA_MAX_HEADS = 65536  # H limit of kda_fwd and kda_decode (KDA_ERR_SHAPE above it)
-EXPORTED = ("kda_fwd", "kda_decode", "kda_fwd_workspace_size", "kda_status_string",
+EXPORTED = ("kda_fwd", "kda_fwd_noalloc", "kda_decode", "kda_fwd_workspace_size", "kda_status_string",
             "kda_profile_enable", "kda_profile_read", "kda_bwd", "kda_bwd_workspace_size")
+KDA_ERR_HIP = 8
+KDA_NOALLOC_SCRATCH_BYTES = 256 << 20  # built-in scratch of kda_fwd_noalloc, per GPU
 
 
 class KdaError(RuntimeError):
@@ -56,6 +58,9 @@ def load_library():
     lib.kda_fwd.restype = ctypes.c_int
     lib.kda_fwd.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_float, P, P,
                             ctypes.c_int, P, I64, I64, I64, I64, I64, I64, P, ctypes.c_size_t, P]
+    lib.kda_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_fwd_noalloc.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_float, P, P,
+                                    ctypes.c_int, P, I64, I64, I64, I64, I64, I64, P]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, P, P, ctypes.c_float, P, ctypes.c_int,
                                I64, I64, I64, I64, P]
@@ -159,21 +164,10 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
-        initial_state=None, final_state=None, cu_seqlens=None, workspace=None):
-    """Chunked KDA forward on the current torch (ROCm) stream; fills ``out``.
-
-    q, k, g: bf16 [B, T, H, 128]; v, out: bf16 [B, T, H, 128]; beta: bf16
-    [B, T, H]; A_log: fp32 [H]; dt_bias: fp32 [H, 128]; lower_bound: finite,
-    <= 0; initial_state / final_state: None or
-    [N, H, 128, 128] of one dtype (bf16 or fp32), final_state may be the same
-    tensor as initial_state; cu_seqlens: None or int32 [N + 1] on the device
-    (B must be 1). ``workspace`` (optional) is a uint8 device tensor of at least
-    ``workspace_size`` bytes; by default a cached buffer is used.
-    Raises ValueError for invalid arguments and KdaError for HIP failures.
-    """
+def _fwd_args(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state, cu_seqlens, workspace):
+    """Check dtypes, devices, contiguity and shapes on the host; returns
+    (state_dtype, num_seqs, B, T, H, K, V)."""
     import torch
-    lib = load_library()
     bf16 = torch.bfloat16
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), ("out", out)):
         if t.dtype != bf16:
@@ -226,6 +220,35 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
         for s in states:
             if tuple(s.shape) != (N, H, K, V):
                 raise ValueError("states must be [N, H, K, V] = %s" % ((N, H, K, V),))
+    return sd, num_seqs, B, T, H, K, V
+
+
+def _check(lib, rc):
+    if rc == 0:
+        return
+    msg = lib.kda_status_string(rc).decode()
+    if rc == KDA_ERR_HIP:
+        raise KdaError(msg)
+    raise ValueError(msg)
+
+
+def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+        initial_state=None, final_state=None, cu_seqlens=None, workspace=None):
+    """Chunked KDA forward on the current torch (ROCm) stream; fills ``out``.
+
+    q, k, g: bf16 [B, T, H, 128]; v, out: bf16 [B, T, H, 128]; beta: bf16
+    [B, T, H]; A_log: fp32 [H]; dt_bias: fp32 [H, 128]; lower_bound: finite,
+    <= 0; initial_state / final_state: None or
+    [N, H, 128, 128] of one dtype (bf16 or fp32), final_state may be the same
+    tensor as initial_state; cu_seqlens: None or int32 [N + 1] on the device
+    (B must be 1). ``workspace`` (optional) is a uint8 device tensor of at least
+    ``workspace_size`` bytes; by default a cached buffer is used.
+    Raises ValueError for invalid arguments and KdaError for HIP failures.
+    """
+    import torch
+    lib = load_library()
+    sd, num_seqs, B, T, H, K, V = _fwd_args(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state,
+                                            cu_seqlens, workspace)
     need = lib.kda_fwd_workspace_size(B, T, H, num_seqs)
     if workspace is None:
         ws = _workspace(need, q.device)
@@ -236,12 +259,30 @@ def fwd(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
                      _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
                      _ptr(final_state), sd, _ptr(cu_seqlens), num_seqs, B, T, H, K, V,
                      _ptr(ws), ws.numel(), ctypes.c_void_p(stream))
-    if rc == 0:
-        return out
-    msg = lib.kda_status_string(rc).decode()
-    if rc == 8:
-        raise KdaError(msg)
-    raise ValueError(msg)
+    _check(lib, rc)
+    return out
+
+
+def fwd_noalloc(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound,
+                initial_state=None, final_state=None, cu_seqlens=None):
+    """``fwd`` through kda_fwd_noalloc: the workspace is the library's built-in
+    scratch array of the GPU (KDA_NOALLOC_SCRATCH_BYTES), so the call allocates
+    nothing, neither in libkda nor here. Same arguments and results as ``fwd``;
+    sizes whose workspace exceeds the scratch raise ValueError
+    (KDA_ERR_SCRATCH). Calls that may overlap in time on one GPU share the
+    scratch and must be serialised by the caller.
+    """
+    import torch
+    lib = load_library()
+    sd, num_seqs, B, T, H, K, V = _fwd_args(q, k, v, g, beta, out, A_log, dt_bias, initial_state, final_state,
+                                            cu_seqlens, None)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = lib.kda_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(out),
+                             _ptr(A_log), _ptr(dt_bias), float(lower_bound), _ptr(initial_state),
+                             _ptr(final_state), sd, _ptr(cu_seqlens), num_seqs, B, T, H, K, V,
+                             ctypes.c_void_p(stream))
+    _check(lib, rc)
+    return out
 
 
 def decode(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, state):

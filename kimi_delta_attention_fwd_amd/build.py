@@ -21,6 +21,7 @@ KERNEL_UNITS = [
     ("kda_scan.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),  # accumulators in VGPRs: no AGPR copies in the chunk loop
     ("kda_decode.hip", []),
     ("kda_bwd.hip", []),
+    ("kda_noalloc.hip", []),
 ]
 
 

@@ -108,6 +108,9 @@ extern "C" const char *kda_status_string(int status)
     case KDA_ERR_ALIAS:
         return "KDA_ERR_ALIAS: out/final_state/state/workspace overlap an input or each other, or the states overlap partially";
     case KDA_ERR_HIP: return "KDA_ERR_HIP: a HIP launch or runtime error occurred";
+    case KDA_ERR_SCRATCH:
+        return "KDA_ERR_SCRATCH: kda_fwd_noalloc needs more workspace than its built-in scratch "
+               "(KDA_NOALLOC_SCRATCH_BYTES, 256 MiB) for these sizes; call kda_fwd with a caller workspace";
     default: return "unknown kda status";
     }
 }
@@ -166,12 +169,17 @@ extern "C" int kda_profile_read(const char **names, float *total_ms, int *counts
     return nk;
 }
 
-extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
-                       float scale, void *out, const float *A_log, const float *dt_bias,
-                       float lower_bound, const void *initial_state, void *final_state,
-                       int state_dtype, const int32_t *cu_seqlens, int64_t num_seqs, int64_t B,
-                       int64_t T, int64_t H, int64_t K, int64_t V, void *workspace,
-                       size_t workspace_bytes, void *stream)
+extern "C" hipError_t kda_noalloc_scratch(void *stream, void **ptr);
+
+/* kda_fwd and kda_fwd_noalloc: validation, then the launches. With noalloc the
+   workspace is the library's scratch array of the stream's GPU, looked up after
+   every argument check has passed (workspace / workspace_bytes are ignored). */
+static int fwd_run(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                   float scale, void *out, const float *A_log, const float *dt_bias,
+                   float lower_bound, const void *initial_state, void *final_state,
+                   int state_dtype, const int32_t *cu_seqlens, int64_t num_seqs, int64_t B,
+                   int64_t T, int64_t H, int64_t K, int64_t V, void *workspace,
+                   size_t workspace_bytes, void *stream, bool noalloc)
 {
     /* ---- validation (host only, nothing enqueued yet) ---- */
     if (K != KDA_DK || V != KDA_DV) return KDA_ERR_HEAD_DIM;
@@ -192,7 +200,13 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
         if (!aligned16(p)) return KDA_ERR_ARG;
     const int64_t nseq_arg = cu_seqlens ? num_seqs : 0;
     const size_t need = kda_fwd_workspace_size(B, T, H, nseq_arg);
-    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) return KDA_ERR_WORKSPACE;
+    if (noalloc) {
+        if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+        workspace = nullptr;
+        workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+    } else if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0) {
+        return KDA_ERR_WORKSPACE;
+    }
 
     const int64_t N = cu_seqlens ? num_seqs : B;
     const size_t act = (size_t)B * T * H * KDA_DK * 2;
@@ -204,7 +218,11 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
                             rng(cu_seqlens, cu_seqlens ? (size_t)(num_seqs + 1) * 4 : 0),
                             rng(initial_state, initial_state ? sbytes : 0)};
     const Range r_fin = rng(final_state, final_state ? sbytes : 0);
-    const Range r_ws = rng(workspace, need);
+    if (noalloc) {
+        /* the scratch array is the library's own: no caller tensor can overlap it */
+        if (kda_noalloc_scratch(stream, &workspace) != hipSuccess) return KDA_ERR_HIP;
+    }
+    const Range r_ws = noalloc ? Range{0, 0} : rng(workspace, need);
     for (const Range &in : inputs) {
         if (overlap(r_out, in)) return KDA_ERR_ALIAS;
         if (overlap(r_ws, in)) return KDA_ERR_ALIAS;
@@ -240,6 +258,27 @@ extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *
             return KDA_ERR_HIP;
     }
     return KDA_OK;
+}
+
+extern "C" int kda_fwd(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                       float scale, void *out, const float *A_log, const float *dt_bias,
+                       float lower_bound, const void *initial_state, void *final_state,
+                       int state_dtype, const int32_t *cu_seqlens, int64_t num_seqs, int64_t B,
+                       int64_t T, int64_t H, int64_t K, int64_t V, void *workspace,
+                       size_t workspace_bytes, void *stream)
+{
+    return fwd_run(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, final_state,
+                   state_dtype, cu_seqlens, num_seqs, B, T, H, K, V, workspace, workspace_bytes, stream, false);
+}
+
+extern "C" int kda_fwd_noalloc(const void *q, const void *k, const void *v, const void *g, const void *beta,
+                               float scale, void *out, const float *A_log, const float *dt_bias,
+                               float lower_bound, const void *initial_state, void *final_state,
+                               int state_dtype, const int32_t *cu_seqlens, int64_t num_seqs, int64_t B,
+                               int64_t T, int64_t H, int64_t K, int64_t V, void *stream)
+{
+    return fwd_run(q, k, v, g, beta, scale, out, A_log, dt_bias, lower_bound, initial_state, final_state,
+                   state_dtype, cu_seqlens, num_seqs, B, T, H, K, V, nullptr, 0, stream, true);
 }
 
 extern "C" int kda_decode(const void *q, const void *k, const void *v, const void *g, const void *beta,

@@ -28,7 +28,7 @@ def test_exports_match_header():
 def test_status_strings():
     for code, tag in enumerate(["KDA_OK", "KDA_ERR_NULL", "KDA_ERR_HEAD_DIM", "KDA_ERR_SHAPE",
                                 "KDA_ERR_STATE_DTYPE", "KDA_ERR_ARG", "KDA_ERR_WORKSPACE",
-                                "KDA_ERR_ALIAS", "KDA_ERR_HIP"]):
+                                "KDA_ERR_ALIAS", "KDA_ERR_HIP", "KDA_ERR_SCRATCH"]):
         assert kda.status_string(code).startswith(tag)
     assert "unknown" in kda.status_string(99)
 
@@ -201,3 +201,29 @@ def test_load_library_brings_torch_first():
             "assert 'torch' not in sys.modules; kda.load_library(); assert 'torch' in sys.modules" % ROOT)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    """kda_fwd_noalloc validates like kda_fwd and rejects sizes whose workspace
+    exceeds its built-in scratch (KDA_ERR_SCRATCH) before it touches HIP."""
+    lib = kda.load_library()
+    assert kda.KDA_NOALLOC_SCRATCH_BYTES == 256 << 20
+    fbuf = FakeBufs()
+    a = {n: ctypes.c_void_p(v) for n, v in fbuf.addr.items()}
+
+    def call(B, T, H, K=128, lb=-5.0, q=a["q"]):
+        return lib.kda_fwd_noalloc(q, a["k"], a["v"], a["g"], a["beta"], 0.088, a["out"], a["A_log"],
+                                   a["dt_bias"], lb, None, None, 0, None, 0, B, T, H, K, 128, None)
+    # 1024 chunks x 32 heads x 72 KB records: far beyond 256 MiB
+    assert kda.workspace_size(1, 65536, 32) > kda.KDA_NOALLOC_SCRATCH_BYTES
+    assert call(1, 65536, 32) == 9
+    # 11 heads (more than 10 chains: no segment-parallel area): 338 chunks per head
+    # are 3,718 records of 72,192 bytes and fit, 339 do not
+    assert kda.workspace_size(1, 338 * 64, 11) <= kda.KDA_NOALLOC_SCRATCH_BYTES
+    assert kda.workspace_size(1, 339 * 64, 11) > kda.KDA_NOALLOC_SCRATCH_BYTES
+    assert call(1, 339 * 64, 11) == 9
+    # kda_fwd's own checks come first
+    assert call(1, 64, 2, K=64) == 2
+    assert call(1, 64, 2, lb=1.0) == 5
+    assert call(1, 64, 2, q=None) == 1
+    assert call(0, 64, 2) == 3
