@@ -56,7 +56,8 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_NULL = 1,        /* a required pointer is NULL                         */
-    KDA_ERR_HEAD_DIM = 2,    /* K != 128 or V != 128                               */
+    KDA_ERR_HEAD_DIM = 2,    /* head dims other than K = V = 128 (kda_fwd and
+                                kda_fwd_noalloc: other than K = V = 128 or 64)      */
     KDA_ERR_SHAPE = 3,       /* B, T, H <= 0, num_seqs <= 0 with cu_seqlens,
                                 B != 1 with cu_seqlens, or sizes past the limits
                                 below (KDA_MAX_HEADS, 32-bit grids and offsets)     */
@@ -120,7 +121,10 @@ typedef enum {
  *  cu_seqlens       : NULL, or int32 [num_seqs + 1] on the device (B must be 1).
  *  num_seqs         : number of packed sequences when cu_seqlens != NULL, else
  *                     ignored (N = B).
- *  B, T, H, K, V    : sizes; K and V must be 128. T counts packed tokens when
+ *  B, T, H, K, V    : sizes; K = V = 128 (the pages' head dims, "Kernel API and
+ *                     Constraints") or K = V = 64, where every 128 in the layouts
+ *                     above reads 64 (q, k, g, v, out rows of 64, dt_bias [H, 64],
+ *                     states [N, H, 64, 64]). T counts packed tokens when
  *                     cu_seqlens is given.
  *  workspace        : device scratch of at least kda_fwd_workspace_size(...)
  *                     bytes, 256-byte aligned; contents on entry are ignored and

@@ -96,16 +96,18 @@ def _unit_rows_bf16(rng, shape):
 def make_inputs(B: int, T: int, H: int, seed: int = 0, *, lengths=None,
                 lower_bound: float = -5.0, state: str | None = None,
                 initial: bool = False, sigma: float = 0.02,
-                dt_sigma: float = 0.0, rng: np.random.Generator | None = None):
+                dt_sigma: float = 0.0, rng: np.random.Generator | None = None,
+                head_dim: int = HEAD_DIM):
     """Draw one batch of inputs.
 
     ``lengths`` (optional) packs sequences of these lengths into B = 1 with
-    ``cu_seqlens``; then T must equal their sum. Returns a dict of numpy arrays
-    (bf16 tensors as uint16 bit patterns) plus scalar arguments.
+    ``cu_seqlens``; then T must equal their sum. ``head_dim`` sets K = V (128
+    for every benchmark workload). Returns a dict of numpy arrays (bf16 tensors
+    as uint16 bit patterns) plus scalar arguments.
     """
     if rng is None:
         rng = np.random.default_rng(seed)
-    K = V = HEAD_DIM
+    K = V = int(head_dim)
     cu = None
     if lengths is not None:
         lengths = np.asarray(lengths, dtype=np.int64)
@@ -133,7 +135,7 @@ def make_inputs(B: int, T: int, H: int, seed: int = 0, *, lengths=None,
     return dict(q=q, k=k, v=v, g=g, beta=beta, A_log=A_log, dt_bias=dt_bias,
                 scale=float(K) ** -0.5, lower_bound=float(lower_bound),
                 initial_state=init, state_dtype=state, final=state is not None,
-                cu_seqlens=cu, B=B, T=T, H=H, N=N)
+                cu_seqlens=cu, B=B, T=T, H=H, N=N, K=K, V=V)
 
 
 def config_inputs(i: int, seed: int = 0) -> dict:

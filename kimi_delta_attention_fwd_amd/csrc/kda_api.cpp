@@ -24,11 +24,11 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
                                       const void *beta, const float *A_log, const float *dt_bias,
                                       float scale, float lower_bound, const int32_t *cu,
                                       const int32_t *chunk_off, int64_t nseq, int64_t T, int64_t H,
-                                      int64_t nslots, void *records, hipStream_t st);
+                                      int64_t nslots, int64_t K, int64_t V, void *records, hipStream_t st);
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
-                                      int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
-                                      const void *init_state, void *final_state, int state_fp32, int64_t segc,
-                                      void *seg_area, hipStream_t st);
+                                      int64_t nseq, int64_t T, int64_t H, int64_t nslots, int64_t K, int64_t V,
+                                      void *out, const void *init_state, void *final_state, int state_fp32,
+                                      int64_t segc, void *seg_area, hipStream_t st);
 extern "C" hipError_t kda_launch_bwd(int stage, const void *q, const void *k, const void *v, const void *g,
                                      const void *beta, const void *dout, const float *A_log,
                                      const float *dt_bias, float scale, float lower_bound,
@@ -95,7 +95,8 @@ extern "C" const char *kda_status_string(int status)
     switch (status) {
     case KDA_OK: return "KDA_OK: success";
     case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
-    case KDA_ERR_HEAD_DIM: return "KDA_ERR_HEAD_DIM: K and V must both be 128";
+    case KDA_ERR_HEAD_DIM:
+        return "KDA_ERR_HEAD_DIM: K and V must both be 128 (kda_fwd and kda_fwd_noalloc also take K = V = 64)";
     case KDA_ERR_SHAPE:
         return "KDA_ERR_SHAPE: B, T, H must be positive and within the size limits (KDA_MAX_HEADS, 32-bit grids); with cu_seqlens B must be 1 and num_seqs positive";
     case KDA_ERR_STATE_DTYPE:
@@ -113,6 +114,12 @@ extern "C" const char *kda_status_string(int status)
                "(KDA_NOALLOC_SCRATCH_BYTES, 256 MiB) for these sizes; call kda_fwd with a caller workspace";
     default: return "unknown kda status";
     }
+}
+
+/* head dims of kda_fwd: K = V = 128 (the pages' dims) or K = V = 64 */
+static bool fwd_head_dims_ok(int64_t K, int64_t V)
+{
+    return (K == KDA_DK && V == KDA_DV) || (K == 64 && V == 64);
 }
 
 /* 16-byte alignment of the tensors the kernels move in 16-byte pieces (NULL passes) */
@@ -182,7 +189,7 @@ static int fwd_run(const void *q, const void *k, const void *v, const void *g, c
                    size_t workspace_bytes, void *stream, bool noalloc)
 {
     /* ---- validation (host only, nothing enqueued yet) ---- */
-    if (K != KDA_DK || V != KDA_DV) return KDA_ERR_HEAD_DIM;
+    if (!fwd_head_dims_ok(K, V)) return KDA_ERR_HEAD_DIM;
     if (B <= 0 || T <= 0 || H <= 0) return KDA_ERR_SHAPE;
     if (cu_seqlens && (B != 1 || num_seqs <= 0)) return KDA_ERR_SHAPE;
     if (!fwd_sizes_ok(B, T, H, cu_seqlens ? num_seqs : 0)) return KDA_ERR_SHAPE;
@@ -209,12 +216,12 @@ static int fwd_run(const void *q, const void *k, const void *v, const void *g, c
     }
 
     const int64_t N = cu_seqlens ? num_seqs : B;
-    const size_t act = (size_t)B * T * H * KDA_DK * 2;
-    const size_t sbytes = (size_t)N * H * KDA_DK * KDA_DV * (state_dtype == KDA_STATE_FP32 ? 4 : 2);
-    const Range r_out = rng(out, act);
-    const Range inputs[] = {rng(q, act), rng(k, act), rng(v, act), rng(g, act),
+    const size_t act = (size_t)B * T * H * K * 2, actv = (size_t)B * T * H * V * 2;
+    const size_t sbytes = (size_t)N * H * K * V * (state_dtype == KDA_STATE_FP32 ? 4 : 2);
+    const Range r_out = rng(out, actv);
+    const Range inputs[] = {rng(q, act), rng(k, act), rng(v, actv), rng(g, act),
                             rng(beta, (size_t)B * T * H * 2), rng(A_log, (size_t)H * 4),
-                            rng(dt_bias, (size_t)H * KDA_DK * 4),
+                            rng(dt_bias, (size_t)H * K * 4),
                             rng(cu_seqlens, cu_seqlens ? (size_t)(num_seqs + 1) * 4 : 0),
                             rng(initial_state, initial_state ? sbytes : 0)};
     const Range r_fin = rng(final_state, final_state ? sbytes : 0);
@@ -246,14 +253,16 @@ static int fwd_run(const void *q, const void *k, const void *v, const void *g, c
     {
         ProfScope ps("kda_prep", st);
         if (kda_launch_prep(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound, cu_seqlens, chunk_off,
-                            N, T, H, nslots, records, st) != hipSuccess)
+                            N, T, H, nslots, K, V, records, st) != hipSuccess)
             return KDA_ERR_HIP;
     }
     {
+        /* the segment-parallel scan (few long chains) exists for K = V = 128 only */
+        const int64_t segc = (K == KDA_DK && V == KDA_DV) ? kda_seg_len(B, T, H, nseq_arg) : 0;
         ProfScope ps("kda_scan", st);
-        if (kda_launch_scan(records, cu_seqlens, chunk_off, N, T, H, nslots, out,
+        if (kda_launch_scan(records, cu_seqlens, chunk_off, N, T, H, nslots, K, V, out,
                             state_dtype == KDA_STATE_NONE ? nullptr : initial_state, final_state,
-                            state_dtype == KDA_STATE_FP32 ? 1 : 0, kda_seg_len(B, T, H, nseq_arg),
+                            state_dtype == KDA_STATE_FP32 ? 1 : 0, segc,
                             (unsigned char *)records + (size_t)nslots * (size_t)H * KDA_REC_BYTES, st) != hipSuccess)
             return KDA_ERR_HIP;
     }

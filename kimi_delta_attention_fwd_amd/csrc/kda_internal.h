@@ -45,6 +45,27 @@
 #define KDA_REC_U 55808      /* U    : [8 value tiles][64 lanes][4 token tiles][4] bf16              */
 #define KDA_REC_BYTES 72192
 
+/* The same layout for any head dims DK = 32 NKB key channels and DV = 16 NVT
+ * value columns (K, V in {64, 128}): NKB key blocks of 32 channels, NVT value
+ * tiles of 16 columns; W and Q' hold 4 NKB fragments (index mt * NKB + kb),
+ * K~^T 4 NKB (index ct * 2 + jb over the 2 NKB key tiles ct), P 6, e^{G_L} DK
+ * floats, U NVT x 64 lanes x 16 bf16. RecLayout<4, 8> is the layout above. */
+template <int NKB, int NVT> struct RecLayout {
+    static constexpr int NFR = 4 * NKB;
+    static constexpr int W = 0, Q = NFR * 1024, KT = 2 * NFR * 1024, P = 3 * NFR * 1024;
+    static constexpr int GL = P + 6 * 1024, U = GL + 128 * NKB, BYTES = U + NVT * 2048;
+};
+static_assert(RecLayout<4, 8>::Q == KDA_REC_Q && RecLayout<4, 8>::KT == KDA_REC_KT &&
+                  RecLayout<4, 8>::P == KDA_REC_P && RecLayout<4, 8>::GL == KDA_REC_GL &&
+                  RecLayout<4, 8>::U == KDA_REC_U && RecLayout<4, 8>::BYTES == KDA_REC_BYTES,
+              "record layout");
+
+/* record bytes for head dims K, V in {64, 128} (at most KDA_REC_BYTES) */
+static inline size_t kda_rec_bytes(int64_t K, int64_t V)
+{
+    return (size_t)(3 * 4 * (K / 32) * 1024 + 6 * 1024 + 4 * K + (V / 16) * 2048);
+}
+
 /* fragment index of P(mt, jb); only jb <= mt / 2 exists */
 #define KDA_PIDX(mt, jb) ((mt) < 2 ? (mt) : 2 + 2 * ((mt) - 2) + (jb))
 

@@ -78,25 +78,26 @@ kda_chunk_map_kernel(const int32_t *__restrict__ cu, int64_t nseq, int32_t *__re
  */
 #define KDA_TS 68 /* row stride (floats) of the fp32 64x64 tiles: 16-byte rows, rows spread over the banks */
 
-struct PrepShared {
+/* DK = 32 NKB key channels, DV = 32 NVB value columns */
+template <int NKB, int NVB> struct PrepShared {
     float beta[KDA_CHUNK];
     union {
         struct { /* phases A-D */
-            float tot[4][KDA_DK]; /* in-sub-chunk inclusive cumsum at token 15 (log2)  */
-            float mid[4][KDA_DK]; /* ... at token 7 (the anchor m_w)                    */
-            float fq[4][KDA_DK];  /* 2^{Gm_w}                                           */
-            float fk[4][KDA_DK];  /* 2^{G_L - Gm_w}                                     */
-            float fm[4][KDA_DK];  /* 2^{m_w}                                            */
-            float fy[6][KDA_DK];  /* 2^{B_i - Gm_b}, pair (i, b) -> i (i - 1) / 2 + b     */
-            bf16x8 yd[4][4][64];  /* diagonal key side k^ 2^{m_w - c}, per sub-chunk    */
+            float tot[4][32 * NKB]; /* in-sub-chunk inclusive cumsum at token 15 (log2)  */
+            float mid[4][32 * NKB]; /* ... at token 7 (the anchor m_w)                    */
+            float fq[4][32 * NKB];  /* 2^{Gm_w}                                           */
+            float fk[4][32 * NKB];  /* 2^{G_L - Gm_w}                                     */
+            float fm[4][32 * NKB];  /* 2^{m_w}                                            */
+            float fy[6][32 * NKB];  /* 2^{B_i - Gm_b}, pair (i, b) -> i (i - 1) / 2 + b     */
+            bf16x8 yd[4][NKB][64];  /* diagonal key side k^ 2^{m_w - c}, per sub-chunk    */
         } p1;
         struct { /* phases E-F */
             float t[KDA_CHUNK][KDA_TS]; /* T = (I + A)^-1, blocks on or below the diagonal */
             bf16x8 tbt[6][64];          /* (T diag(beta))^T fragments, index kda_tbt_idx  */
         } p2;
     } u;
-    bf16x8 rt[8][2][64];      /* R^T fragments (key tile, token block)                 */
-    bf16x8 vt[8][2][64];      /* V^T fragments (value tile, token block)               */
+    bf16x8 rt[2 * NKB][2][64];  /* R^T fragments (key tile, token block)                 */
+    bf16x8 vt[2 * NVB][2][64];  /* V^T fragments (value tile, token block)               */
     float a[KDA_CHUNK][KDA_TS]; /* A (strictly lower; beta_r on row r)                 */
 };
 
@@ -135,7 +136,7 @@ __device__ __forceinline__ void store_transposed(const bf16x8 &fr, const bf16x8 
      values from the lanes of the same channel group).
    (c = in-sub-chunk inclusive cumsum, tot_w = its value at the sub-chunk's last
    row, B_w = G before sub-chunk w, all log2.) */
-template <bool WIDE>
+template <bool WIDE, int NKB, int NVB>
 __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gt,
                                           const uint16_t *beta, const float *__restrict__ A_log,
                                           const float *__restrict__ dt_bias, float scale, float lower_bound,
@@ -143,13 +144,15 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
                                           int64_t nseq, int64_t T, int H, int64_t nslots,
                                           unsigned char *__restrict__ rec_base)
 {
-    __shared__ PrepShared sh;
+    constexpr int DK = 32 * NKB, DV = 32 * NVB, NE = 8 * NKB; /* NE: key channels per lane */
+    using RL = RecLayout<NKB, 2 * NVB>;
+    __shared__ PrepShared<NKB, NVB> sh;
     const int64_t slot = blockIdx.x / H;
     const int h = (int)(blockIdx.x - slot * H);
     int64_t t0, seq;
     int L;
     if (!locate_chunk(slot, cu, chunk_off, nseq, T, t0, L, seq)) return;
-    unsigned char *rec = rec_base + ((size_t)h * nslots + slot) * KDA_REC_BYTES;
+    unsigned char *rec = rec_base + ((size_t)h * nslots + slot) * RL::BYTES;
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, r16 = l & 15;
     const int r = 16 * w + r16;
@@ -158,28 +161,34 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     /* ---- phase A: load this lane's token row, norms, gate, cumsum ---- */
     /* Token rows past the chunk end fall outside the descriptors' ranges and load
        as zeros, so every lane loads unconditionally (no branch, no early wait). */
-    const size_t act0 = ((size_t)t0 * H + h) * KDA_DK; /* element offset of (t0, h, 0) */
-    const uint32_t row_bytes = (uint32_t)H * KDA_DK * 2;
-    const uint32_t act_bytes = (uint32_t)(L - 1) * row_bytes + KDA_DK * 2;
+    const size_t act0 = ((size_t)t0 * H + h) * DK; /* element offset of (t0, h, 0) in q, k, g */
+    const size_t actv0 = ((size_t)t0 * H + h) * DV; /* ... in v */
+    const uint32_t row_bytes = (uint32_t)H * DK * 2, row_bytes_v = (uint32_t)H * DV * 2;
+    const uint32_t act_bytes = (uint32_t)(L - 1) * row_bytes + DK * 2;
+    const uint32_t act_bytes_v = (uint32_t)(L - 1) * row_bytes_v + DV * 2;
     const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + act0, act_bytes), rk = buf_rsrc(k + act0, act_bytes);
-    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gt + act0, act_bytes), rv = buf_rsrc(v + act0, act_bytes);
+    const __amdgpu_buffer_rsrc_t rg = buf_rsrc(gt + act0, act_bytes), rv = buf_rsrc(v + actv0, act_bytes_v);
     const __amdgpu_buffer_rsrc_t rb = buf_rsrc(beta + (size_t)t0 * H + h, (uint32_t)(L - 1) * H * 2 + 2);
-    const uint32_t voff = (uint32_t)r * row_bytes;
-    float qf[32], kf[32], la[32];
-    bf16x8 vfr[4];
+    const uint32_t voff = (uint32_t)r * row_bytes, voff_v = (uint32_t)r * row_bytes_v;
+    float qf[NE], kf[NE], la[NE];
+    bf16x8 vfr[NVB];
     const float bt = bf2f(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)r * H * 2, 0, 0));
     const float decay_rate = __expf(A_log[h]);
     const float lb2 = lower_bound * LOG2E_F;
     /* 16 bytes per lane and tensor: operand slot i of key block kb holds channel
        32 kb + 8 g + i (natural order) */
-    u32x4 uqa[4], uka[4], uga[4], uva[4];
+    u32x4 uqa[NKB], uka[NKB], uga[NKB], uva[NVB];
+    static_assert(NKB == NVB || NKB == 2 * NVB || NVB == 2 * NKB, "head dims");
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
-        const uint32_t o = voff + (uint32_t)(32 * kb + 8 * g) * 2;
-        uqa[kb] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
-        uka[kb] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
-        uga[kb] = __builtin_amdgcn_raw_buffer_load_b128(rg, o, 0, 0);
-        uva[kb] = __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0);
+    for (int kb = 0; kb < (NKB > NVB ? NKB : NVB); kb++) {
+        if (kb < NKB) {
+            const uint32_t o = voff + (uint32_t)(32 * kb + 8 * g) * 2;
+            uqa[kb] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
+            uka[kb] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
+            uga[kb] = __builtin_amdgcn_raw_buffer_load_b128(rg, o, 0, 0);
+        }
+        if (kb < NVB)
+            uva[kb] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v + (uint32_t)(32 * kb + 8 * g) * 2, 0, 0);
     }
     /* All 17 loads are in flight before any of them is consumed. (The activation
        pointers are deliberately not __restrict__: loads through restrict const
@@ -187,8 +196,8 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
        next to their late first use, which costs a second memory round trip.) */
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
-        const float *dbp = dt_bias + (size_t)h * KDA_DK + 32 * kb + 8 * g;
+    for (int kb = 0; kb < NKB; kb++) {
+        const float *dbp = dt_bias + (size_t)h * DK + 32 * kb + 8 * g;
         const float4 db0 = *(const float4 *)dbp, db1 = *(const float4 *)(dbp + 4);
         const float dbs[8] = {db0.x, db0.y, db0.z, db0.w, db1.x, db1.y, db1.z, db1.w};
 #pragma unroll
@@ -204,21 +213,22 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
             const float l2 = fmaxf(-decay_rate * sp2, lb2);
             la[j] = valid ? l2 : 0.f; /* padded rows: no decay */
         }
-        /* v stays in bf16 */
-        vfr[kb] = __builtin_bit_cast(bf16x8, uva[kb]);
     }
+    /* v stays in bf16 */
+#pragma unroll
+    for (int vb = 0; vb < NVB; vb++) vfr[vb] = __builtin_bit_cast(bf16x8, uva[vb]);
     float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int j = 0; j < 32; j++) { sq += qf[j] * qf[j]; sk += kf[j] * kf[j]; }
+    for (int j = 0; j < NE; j++) { sq += qf[j] * qf[j]; sk += kf[j] * kf[j]; }
     sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
     sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
     const float iq = scale / sqrtf(sq + 1e-6f), ik = 1.f / sqrtf(sk + 1e-6f);
 #pragma unroll
-    for (int j = 0; j < 32; j++) la[j] = row_scan16(la[j]);
+    for (int j = 0; j < NE; j++) la[j] = row_scan16(la[j]);
     if (r16 == 7 || r16 == 15) {
         float *dst = (r16 == 15) ? sh.u.p1.tot[w] : sh.u.p1.mid[w];
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++) {
+        for (int kb = 0; kb < NKB; kb++) {
             *(float4 *)&dst[32 * kb + 8 * g] = make_float4(la[8 * kb], la[8 * kb + 1], la[8 * kb + 2], la[8 * kb + 3]);
             *(float4 *)&dst[32 * kb + 8 * g + 4] =
                 make_float4(la[8 * kb + 4], la[8 * kb + 5], la[8 * kb + 6], la[8 * kb + 7]);
@@ -228,8 +238,8 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     __syncthreads();
 
     /* ---- phase B: per (sub-chunk, channel) factors ---- */
-    for (int p = tid; p < 4 * KDA_DK; p += 256) {
-        const int ww = p >> 7, ch = p & 127;
+    for (int p = tid; p < 4 * DK; p += 256) {
+        const int ww = p / DK, ch = p % DK;
         float B = 0.f, GL = 0.f;
 #pragma unroll
         for (int m = 0; m < 4; m++) {
@@ -246,10 +256,10 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
             sh.u.p1.fk[ww][ch] = exp2_fast(GL - gm);
             sh.u.p1.fm[ww][ch] = exp2_fast(sh.u.p1.mid[ww][ch]);
         }
-        if (ww == 0) ((float *)(rec + KDA_REC_GL))[ch] = exp2_fast(GL);
+        if (ww == 0) ((float *)(rec + RL::GL))[ch] = exp2_fast(GL);
     }
-    for (int p = tid; p < 6 * KDA_DK; p += 256) {
-        const int pp = p >> 7, ch = p & 127;
+    for (int p = tid; p < 6 * DK; p += 256) {
+        const int pp = p / DK, ch = p % DK;
         const int i = pp < 1 ? 1 : (pp < 3 ? 2 : 3);
         const int b = pp - i * (i - 1) / 2;
         float Bi = 0.f, Bb = 0.f;
@@ -264,7 +274,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     __syncthreads();
 
     /* ---- phase C: decay-scaled operands (R-form), transposes ---- */
-    bf16x8 xdk_f[4], xdq_f[4], yd_f[4], qt_f[4], xok_f[4], xoq_f[4];
+    bf16x8 xdk_f[NKB], xdq_f[NKB], yd_f[NKB], qt_f[NKB], xok_f[NKB], xoq_f[NKB];
     bf16x8 sel[2]; /* 0/1 selectors: slot i of lane group g is channel 8 g + i of a 32-wide block */
     {
 #pragma unroll
@@ -273,7 +283,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
             for (int i = 0; i < 8; i++) sel[hh][i] = (__bf16)(8 * g + i == 16 * hh + r16 ? 1.f : 0.f);
         const int jb = w >> 1, jh = w & 1;
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++) {
+        for (int kb = 0; kb < NKB; kb++) {
             bf16x8 rf, kt;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
@@ -310,12 +320,17 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
             /* key tiles 2 kb and 2 kb + 1 of R, V and K~ */
             store_transposed(rf, sel, (uint16_t *)&sh.rt[2 * kb][jb][l] + 4 * jh,
                              (uint16_t *)&sh.rt[2 * kb + 1][jb][l] + 4 * jh);
-            store_transposed(vfr[kb], sel, (uint16_t *)&sh.vt[2 * kb][jb][l] + 4 * jh,
-                             (uint16_t *)&sh.vt[2 * kb + 1][jb][l] + 4 * jh);
+            if (kb < NVB)
+                store_transposed(vfr[kb], sel, (uint16_t *)&sh.vt[2 * kb][jb][l] + 4 * jh,
+                                 (uint16_t *)&sh.vt[2 * kb + 1][jb][l] + 4 * jh);
             store_transposed(kt, sel,
-                             (uint16_t *)(rec + KDA_REC_KT + ((size_t)((2 * kb) * 2 + jb) * 64 + l) * 16 + jh * 8),
-                             (uint16_t *)(rec + KDA_REC_KT + ((size_t)((2 * kb + 1) * 2 + jb) * 64 + l) * 16 + jh * 8));
+                             (uint16_t *)(rec + RL::KT + ((size_t)((2 * kb) * 2 + jb) * 64 + l) * 16 + jh * 8),
+                             (uint16_t *)(rec + RL::KT + ((size_t)((2 * kb + 1) * 2 + jb) * 64 + l) * 16 + jh * 8));
         }
+#pragma unroll
+        for (int vb = NKB; vb < NVB; vb++) /* value tiles past the key tiles (DV > DK) */
+            store_transposed(vfr[vb], sel, (uint16_t *)&sh.vt[2 * vb][jb][l] + 4 * jh,
+                             (uint16_t *)&sh.vt[2 * vb + 1][jb][l] + 4 * jh);
     }
     __syncthreads(); /* yd, rt, vt visible */
 
@@ -333,7 +348,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
 #pragma unroll
             for (int jj = 0; jj < 16; jj++) { sa[jj] = 0.f; sp[jj] = 0.f; }
 #pragma unroll
-            for (int j = 0; j < 32; j++) {
+            for (int j = 0; j < NE; j++) {
                 const float kh = kf[j] * ik, qh = qf[j] * iq, c = la[j];
 #pragma unroll
                 for (int jj = 0; jj < 16; jj++) {
@@ -358,7 +373,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
                     if (jj == 4 * g + e) { ad[e] = sa[jj]; pd[e] = sp[jj]; }
         } else {
 #pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
+            for (int kb = 0; kb < NKB; kb++) {
                 ad = mfma(yd_f[kb], xdk_f[kb], ad);
                 pd = mfma(yd_f[kb], xdq_f[kb], pd);
             }
@@ -368,7 +383,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
             const float *fy = sh.u.p1.fy[w * (w - 1) / 2 + b];
             f32x4 ta = zero4(), tp = zero4();
 #pragma unroll
-            for (int kb = 0; kb < 4; kb++) {
+            for (int kb = 0; kb < NKB; kb++) {
                 const bf16x8 yb = sh.u.p1.yd[b][kb][l];
                 bf16x8 ys;
 #pragma unroll
@@ -404,7 +419,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     pf[0] = pack8(pt[0], pt[1]);
     pf[1] = pack8(pt[2], pt[3]);
     {
-        bf16x8 *pdst = (bf16x8 *)(rec + KDA_REC_P);
+        bf16x8 *pdst = (bf16x8 *)(rec + RL::P);
         if (w < 2) {
             pdst[KDA_PIDX(w, 0) * 64 + l] = pf[0];
         } else {
@@ -499,7 +514,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     }
     /* W (stored negated), lane = token, regs = key channel */
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
+    for (int kb = 0; kb < NKB; kb++) {
         f32x4 d0 = zero4(), d1 = zero4();
 #pragma unroll
         for (int jb = 0; jb < 2; jb++)
@@ -507,11 +522,11 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
                 d0 = mfma(sh.rt[2 * kb][jb][l], tbf[jb], d0);
                 d1 = mfma(sh.rt[2 * kb + 1][jb][l], tbf[jb], d1);
             }
-        ((bf16x8 *)(rec + KDA_REC_W))[(w * 4 + kb) * 64 + l] = pack8(-d0, -d1);
+        ((bf16x8 *)(rec + RL::W))[(w * NKB + kb) * 64 + l] = pack8(-d0, -d1);
     }
     /* U, lane = value column, regs = token */
 #pragma unroll
-    for (int nt = 0; nt < 8; nt++) {
+    for (int nt = 0; nt < 2 * NVB; nt++) {
         f32x4 d = zero4();
 #pragma unroll
         for (int jb = 0; jb < 2; jb++)
@@ -519,7 +534,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
         uint2 u;
         u.x = f2bf_bits(d[0]) | ((uint32_t)f2bf_bits(d[1]) << 16);
         u.y = f2bf_bits(d[2]) | ((uint32_t)f2bf_bits(d[3]) << 16);
-        *(uint2 *)(rec + KDA_REC_U + ((size_t)(nt * 64 + l) * 16 + w * 4) * 2) = u;
+        *(uint2 *)(rec + RL::U + ((size_t)(nt * 64 + l) * 16 + w * 4) * 2) = u;
     }
     /* P TB, lane = token r, regs = j' */
     f32x4 ptt[4];
@@ -538,7 +553,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     ptf[1] = pack8(-ptt[2], -ptt[3]);
     /* Q' = Q~ - (P TB) R, lane = token, regs = key channel */
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
+    for (int kb = 0; kb < NKB; kb++) {
         /* Q~ into the accumulator layout (rows = channels 32 kb + 16 hh + 4 g + e,
            column = token) by 0/1 selector MFMAs (exact) */
         f32x4 d0 = mfma(sel[0], qt_f[kb], zero4()), d1 = mfma(sel[1], qt_f[kb], zero4());
@@ -548,32 +563,27 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
                 d0 = mfma(sh.rt[2 * kb][jb][l], ptf[jb], d0);
                 d1 = mfma(sh.rt[2 * kb + 1][jb][l], ptf[jb], d1);
             }
-        ((bf16x8 *)(rec + KDA_REC_Q))[(w * 4 + kb) * 64 + l] = pack8(d0, d1);
+        ((bf16x8 *)(rec + RL::Q))[(w * NKB + kb) * 64 + l] = pack8(d0, d1);
     }
 }
 
-extern "C" __global__ void __launch_bounds__(256, 2)
-kda_prep_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gt,
-                const uint16_t *beta, const float *__restrict__ A_log,
-                const float *__restrict__ dt_bias, float scale, float lower_bound,
-                const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
-                int64_t nseq, int64_t T, int H, int64_t nslots, unsigned char *__restrict__ rec_base)
-{
-    prep_body<false>(q, k, v, gt, beta, A_log, dt_bias, scale, lower_bound, cu, chunk_off, nseq, T, H, nslots,
-                     rec_base);
-}
+#define KDA_PREP_KERNEL(name, WIDE, NKB, NVB)                                                                      \
+    extern "C" __global__ void __launch_bounds__(256, 2)                                                            \
+        name(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gt, const uint16_t *beta,     \
+             const float *__restrict__ A_log, const float *__restrict__ dt_bias, float scale, float lower_bound,     \
+             const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H,  \
+             int64_t nslots, unsigned char *__restrict__ rec_base)                                                 \
+    {                                                                                                               \
+        prep_body<WIDE, NKB, NVB>(q, k, v, gt, beta, A_log, dt_bias, scale, lower_bound, cu, chunk_off, nseq, T, H, \
+                                  nslots, rec_base);                                                                \
+    }
 
-/* lower_bound below KDA_LOWER_BOUND_NARROW */
-extern "C" __global__ void __launch_bounds__(256, 2)
-kda_prep_wide_kernel(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gt,
-                     const uint16_t *beta, const float *__restrict__ A_log,
-                     const float *__restrict__ dt_bias, float scale, float lower_bound,
-                     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
-                     int64_t nseq, int64_t T, int H, int64_t nslots, unsigned char *__restrict__ rec_base)
-{
-    prep_body<true>(q, k, v, gt, beta, A_log, dt_bias, scale, lower_bound, cu, chunk_off, nseq, T, H, nslots,
-                    rec_base);
-}
+/* K = V = 128; the wide form below lower_bound KDA_LOWER_BOUND_NARROW */
+KDA_PREP_KERNEL(kda_prep_kernel, false, 4, 4)
+KDA_PREP_KERNEL(kda_prep_wide_kernel, true, 4, 4)
+/* K = V = 64 */
+KDA_PREP_KERNEL(kda_prep_k64_kernel, false, 2, 2)
+KDA_PREP_KERNEL(kda_prep_wide_k64_kernel, true, 2, 2)
 
 /* ------------------------------------------------------------------------- */
 /* launchers (called by kda_api.cpp after validation)                          */
@@ -589,10 +599,14 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
                                       const void *beta, const float *A_log, const float *dt_bias,
                                       float scale, float lower_bound, const int32_t *cu,
                                       const int32_t *chunk_off, int64_t nseq, int64_t T, int64_t H,
-                                      int64_t nslots, void *records, hipStream_t st)
+                                      int64_t nslots, int64_t K, int64_t V, void *records, hipStream_t st)
 {
     const int64_t blocks = nslots * H;
-    hipLaunchKernelGGL(lower_bound < KDA_LOWER_BOUND_NARROW ? kda_prep_wide_kernel : kda_prep_kernel,
+    const bool wide = lower_bound < KDA_LOWER_BOUND_NARROW;
+    auto kern = wide ? kda_prep_wide_kernel : kda_prep_kernel;
+    if (K == 64 && V == 64) kern = wide ? kda_prep_wide_k64_kernel : kda_prep_k64_kernel;
+    else if (K != KDA_DK || V != KDA_DV) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern,
                        dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
                        (const uint16_t *)g, (const uint16_t *)beta, A_log, dt_bias, scale,

@@ -572,27 +572,32 @@ kda_seg_chain_kernel(float *seg_area, const void *init_state, int state_fp32, co
  * The state slice is read and written through buffer descriptors whose range is
  * empty when the state pointer is null (loads return 0, stores are dropped).
  */
+template <int DK, int DV>
 __device__ __forceinline__ void state_io_rsrc(const void *state, int state_fp32, int64_t chain, const void *dummy,
                                               __amdgpu_buffer_rsrc_t &r)
 {
-    const uint32_t bytes = (uint32_t)(KDA_DK * KDA_DV * (state_fp32 ? 4 : 2));
+    const uint32_t bytes = (uint32_t)(DK * DV * (state_fp32 ? 4 : 2));
     r = state ? buf_rsrc((const unsigned char *)state + (size_t)chain * bytes, bytes) : buf_rsrc(dummy, 0);
 }
-
-#define KDA_SHARED_PIECES (KDA_REC_U / 16) /* 16-byte pieces of the shared operands */
-#define KDA_FILL_ITERS ((KDA_SHARED_PIECES + 511) / 512)
 
 __device__ __forceinline__ bf16x8 ldsld(const unsigned char *base, int off)
 {
     return *(const bf16x8 *)(base + off);
 }
 
-extern "C" __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
-kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ cu,
-                     const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
-                     uint16_t *out, const void *init_state, void *final_state, int state_fp32, int64_t max_chunks)
+/* One workgroup of NVT waves per chain (wave = 16-column value tile), the
+   chunk's shared operands in LDS; DK = 32 NKB key channels, DV = 16 NVT value
+   columns (record layout RecLayout<NKB, NVT>). */
+template <int NKB, int NVT>
+__device__ __forceinline__ void scan_many_body(const unsigned char *rec_base, const int32_t *__restrict__ cu,
+                                               const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H,
+                                               int64_t nslots, uint16_t *out, const void *init_state,
+                                               void *final_state, int state_fp32, int64_t max_chunks)
 {
-    __shared__ __attribute__((aligned(16))) unsigned char opnd[KDA_REC_U];
+    using RL = RecLayout<NKB, NVT>;
+    constexpr int DK = 32 * NKB, DV = 16 * NVT, NKT = 2 * NKB, NTH = 64 * NVT;
+    constexpr int PIECES = RL::U / 16, FILL_ITERS = (PIECES + NTH - 1) / NTH; /* 16-byte pieces of the shared operands */
+    __shared__ __attribute__((aligned(16))) unsigned char opnd[RL::U];
     const int tid = threadIdx.x;
     const int l = tid & 63, g = l >> 4, n16 = l & 15;
     const int nt = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -612,58 +617,58 @@ kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ 
     }
     const int64_t nchunk = (eos - bos + KDA_CHUNK - 1) / KDA_CHUNK;
     if (nchunk > max_chunks) return; /* left to the three-wave kernel (uniform over the workgroup) */
-    const unsigned char *rec0 = rec_base + ((size_t)h * nslots + slot0) * KDA_REC_BYTES;
-    const int ubase = KDA_REC_U + nt * 2048;
-    const int row_bytes = H * KDA_DV * 2;
+    const unsigned char *rec0 = rec_base + ((size_t)h * nslots + slot0) * RL::BYTES;
+    const int ubase = RL::U + nt * 2048;
+    const int row_bytes = H * DV * 2;
 
     /* element (16 mt + 4 g + e, 16 nt + n16) of the state */
     const int esz = state_fp32 ? 4 : 2;
-    const int soff = ((4 * g) * KDA_DV + 16 * nt + n16) * esz;
+    const int soff = ((4 * g) * DV + 16 * nt + n16) * esz;
     __amdgpu_buffer_rsrc_t ri, rf;
-    state_io_rsrc(init_state, state_fp32, chain, rec_base, ri);
-    state_io_rsrc(final_state, state_fp32, chain, rec_base, rf);
-    f32x4 S[8];
+    state_io_rsrc<DK, DV>(init_state, state_fp32, chain, rec_base, ri);
+    state_io_rsrc<DK, DV>(final_state, state_fp32, chain, rec_base, rf);
+    f32x4 S[NKT];
     if (state_fp32) {
 #pragma unroll
-        for (int mt = 0; mt < 8; mt++)
+        for (int mt = 0; mt < NKT; mt++)
 #pragma unroll
             for (int e = 0; e < 4; e++)
-                S[mt][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ri, soff, (16 * mt + e) * KDA_DV * 4, 0));
+                S[mt][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ri, soff, (16 * mt + e) * DV * 4, 0));
     } else {
 #pragma unroll
-        for (int mt = 0; mt < 8; mt++)
+        for (int mt = 0; mt < NKT; mt++)
 #pragma unroll
             for (int e = 0; e < 4; e++)
-                S[mt][e] = bf2f(__builtin_amdgcn_raw_buffer_load_b16(ri, soff, (16 * mt + e) * KDA_DV * 2, 0));
+                S[mt][e] = bf2f(__builtin_amdgcn_raw_buffer_load_b16(ri, soff, (16 * mt + e) * DV * 2, 0));
     }
 
     for (int64_t c = 0; c < nchunk; c++) {
-        const __amdgpu_buffer_rsrc_t r = rec_rsrc(rec0 + (size_t)c * KDA_REC_BYTES);
+        const __amdgpu_buffer_rsrc_t r = buf_rsrc(rec0 + (size_t)c * RL::BYTES, RL::BYTES);
         const int64_t t0 = bos + c * KDA_CHUNK;
         const int64_t rem = eos - t0;
         const int L = (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
         /* this chunk's shared operands: loads issued before the barrier that
            frees the LDS copy of the previous chunk, stores after it */
-        u32x4 stage[KDA_FILL_ITERS];
+        u32x4 stage[FILL_ITERS];
 #pragma unroll
-        for (int i = 0; i < KDA_FILL_ITERS; i++) {
-            const int p = i * 512 + tid;
-            stage[i] = p < KDA_SHARED_PIECES ? __builtin_amdgcn_raw_buffer_load_b128(r, p * 16, 0, 0) : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < FILL_ITERS; i++) {
+            const int p = i * NTH + tid;
+            stage[i] = p < PIECES ? __builtin_amdgcn_raw_buffer_load_b128(r, p * 16, 0, 0) : u32x4{0, 0, 0, 0};
         }
         bf16x8 U[2];
         U[0] = bufld(r, l * 32, ubase);
         U[1] = bufld(r, l * 32, ubase + 16);
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < KDA_FILL_ITERS; i++) {
-            const int p = i * 512 + tid;
-            if (p < KDA_SHARED_PIECES) *(u32x4 *)(opnd + p * 16) = stage[i];
+        for (int i = 0; i < FILL_ITERS; i++) {
+            const int p = i * NTH + tid;
+            if (p < PIECES) *(u32x4 *)(opnd + p * 16) = stage[i];
         }
         __syncthreads();
 
-        bf16x8 sb[4];
+        bf16x8 sb[NKB];
 #pragma unroll
-        for (int kb = 0; kb < 4; kb++) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
+        for (int kb = 0; kb < NKB; kb++) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
         /* D = U - W S; LDS operands are read in groups of eight fragments */
         f32x4 D[4];
 #pragma unroll
@@ -674,11 +679,11 @@ kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ 
         }
         bf16x8 fr[8];
 #pragma unroll
-        for (int half = 0; half < 2; half++) {
+        for (int half = 0; half < NKB / 2; half++) {
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const int kb = 2 * half + (i >> 2), mt = i & 3;
-                fr[i] = ldsld(opnd, KDA_REC_W + (mt * 4 + kb) * 1024 + l * 16);
+                fr[i] = ldsld(opnd, RL::W + (mt * NKB + kb) * 1024 + l * 16);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -694,11 +699,11 @@ kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ 
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) O[mt] = zero4();
 #pragma unroll
-        for (int half = 0; half < 2; half++) {
+        for (int half = 0; half < NKB / 2; half++) {
 #pragma unroll
             for (int i = 0; i < 8; i++) {
                 const int kb = 2 * half + (i >> 2), mt = i & 3;
-                fr[i] = ldsld(opnd, KDA_REC_Q + (mt * 4 + kb) * 1024 + l * 16);
+                fr[i] = ldsld(opnd, RL::Q + (mt * NKB + kb) * 1024 + l * 16);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -709,7 +714,7 @@ kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ 
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int f = 0; f < 6; f++) fr[f] = ldsld(opnd, KDA_REC_P + f * 1024 + l * 16);
+        for (int f = 0; f < 6; f++) fr[f] = ldsld(opnd, RL::P + f * 1024 + l * 16);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mt = 0; mt < 4; mt++)
@@ -717,7 +722,7 @@ kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ 
             for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(U[jb], fr[KDA_PIDX(mt, jb)], O[mt]);
         __builtin_amdgcn_sched_barrier(0);
         const __amdgpu_buffer_rsrc_t ro =
-            buf_rsrc(out + ((size_t)t0 * H + h) * KDA_DV, (uint32_t)((L - 1) * row_bytes + KDA_DV * 2));
+            buf_rsrc(out + ((size_t)t0 * H + h) * DV, (uint32_t)((L - 1) * row_bytes + DV * 2));
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
             u32x2 u;
@@ -728,34 +733,53 @@ kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ 
 
         /* S <- diag(e^{G_L}) S + K~^T D */
 #pragma unroll
-        for (int mt = 0; mt < 8; mt++) S[mt] *= *(const f32x4 *)(opnd + KDA_REC_GL + mt * 64 + g * 16);
+        for (int mt = 0; mt < NKT; mt++) S[mt] *= *(const f32x4 *)(opnd + RL::GL + mt * 64 + g * 16);
         bf16x8 db[2];
         db[0] = pack8(D[0], D[1]);
         db[1] = pack8(D[2], D[3]);
 #pragma unroll
         for (int jb = 0; jb < 2; jb++) {
 #pragma unroll
-            for (int mt = 0; mt < 8; mt++) fr[mt] = ldsld(opnd, KDA_REC_KT + (mt * 2 + jb) * 1024 + l * 16);
+            for (int mt = 0; mt < NKT; mt++) fr[mt] = ldsld(opnd, RL::KT + (mt * 2 + jb) * 1024 + l * 16);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int mt = 0; mt < 8; mt++) S[mt] = mfma(fr[mt], db[jb], S[mt]);
+            for (int mt = 0; mt < NKT; mt++) S[mt] = mfma(fr[mt], db[jb], S[mt]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 
     if (state_fp32) {
 #pragma unroll
-        for (int mt = 0; mt < 8; mt++)
+        for (int mt = 0; mt < NKT; mt++)
 #pragma unroll
             for (int e = 0; e < 4; e++)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[mt][e]), rf, soff, (16 * mt + e) * KDA_DV * 4, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[mt][e]), rf, soff, (16 * mt + e) * DV * 4, 0);
     } else {
 #pragma unroll
-        for (int mt = 0; mt < 8; mt++)
+        for (int mt = 0; mt < NKT; mt++)
 #pragma unroll
             for (int e = 0; e < 4; e++)
-                __builtin_amdgcn_raw_buffer_store_b16(f2bf_bits(S[mt][e]), rf, soff, (16 * mt + e) * KDA_DV * 2, 0);
+                __builtin_amdgcn_raw_buffer_store_b16(f2bf_bits(S[mt][e]), rf, soff, (16 * mt + e) * DV * 2, 0);
     }
+}
+
+extern "C" __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ cu,
+                     const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
+                     uint16_t *out, const void *init_state, void *final_state, int state_fp32, int64_t max_chunks)
+{
+    scan_many_body<4, 8>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state, state_fp32,
+                         max_chunks);
+}
+
+/* K = V = 64: four waves per chain, every chain of any length */
+extern "C" __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
+kda_scan_many_k64_kernel(const unsigned char *rec_base, const int32_t *__restrict__ cu,
+                         const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
+                         uint16_t *out, const void *init_state, void *final_state, int state_fp32)
+{
+    scan_many_body<2, 4>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state, state_fp32,
+                         INT64_MAX);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -774,12 +798,18 @@ kda_scan_many_kernel(const unsigned char *rec_base, const int32_t *__restrict__ 
 #define KDA_MANY_CHAINS 128
 
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
-                                      int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
-                                      const void *init_state, void *final_state, int state_fp32, int64_t segc,
-                                      void *seg_area, hipStream_t st)
+                                      int64_t nseq, int64_t T, int64_t H, int64_t nslots, int64_t K, int64_t V,
+                                      void *out, const void *init_state, void *final_state, int state_fp32,
+                                      int64_t segc, void *seg_area, hipStream_t st)
 {
     const unsigned char *rec = (const unsigned char *)records;
     const int64_t nchain = nseq * H;
+    if (K == 64 && V == 64) { /* other head dims: the many-chain form for every chain */
+        hipLaunchKernelGGL(kda_scan_many_k64_kernel, dim3((unsigned)nchain), dim3(256), 0, st, rec, cu, chunk_off,
+                           nseq, T, (int)H, nslots, (uint16_t *)out, init_state, final_state, state_fp32);
+        return hipGetLastError();
+    }
+    if (K != KDA_DK || V != KDA_DV) return hipErrorInvalidValue;
     if (segc > 0) { /* segment-parallel (few long chains) */
         const int64_t G = kda_seg_slots(T, segc);
         float *area = (float *)seg_area;

@@ -37,8 +37,9 @@ def run_gpu(d, t=None, final=None, out=None, workspace=None, in_place=False):
     if t is None:
         t = dev_inputs(d)
     B, T, H = d["B"], d["T"], d["H"]
+    K, V = d.get("K", 128), d.get("V", 128)
     if out is None:
-        out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device=DEV)
+        out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=DEV)
     if final is None:
         final = d.get("final", False)
     fin = None
@@ -48,7 +49,7 @@ def run_gpu(d, t=None, final=None, out=None, workspace=None, in_place=False):
         if in_place and t["initial_state"] is not None:
             fin = t["initial_state"]
         else:
-            fin = torch.empty((N, H, 128, 128), dtype=dt, device=DEV)
+            fin = torch.empty((N, H, K, V), dtype=dt, device=DEV)
     kda.fwd(t["q"], t["k"], t["v"], t["g"], t["beta"], d["scale"], out, t["A_log"], t["dt_bias"],
             d["lower_bound"], initial_state=t["initial_state"], final_state=fin,
             cu_seqlens=t["cu_seqlens"], workspace=workspace)

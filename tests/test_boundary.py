@@ -79,9 +79,13 @@ def fb():
 
 
 def test_rejects_head_dims(fb):
+    """kda_fwd takes K = V = 128 and K = V = 64; every other pair is rejected."""
     lib = kda.load_library()
-    assert fb.call(lib, K=64) == 2
-    assert fb.call(lib, V=256) == 2
+    for K, V in ((64, 128), (128, 64), (128, 256), (256, 256), (32, 32), (96, 96), (0, 0)):
+        assert fb.call(lib, K=K, V=V) == 2, (K, V)
+    # K = V = 64 passes the head-dim check: the fake buffers then fail on the
+    # too-small workspace argument (a later check), not on the head dims
+    assert fb.call(lib, K=64, V=64, wsb=0) == 6
 
 
 def test_rejects_shapes(fb):
