@@ -19,6 +19,7 @@ INCLUDES = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
 KERNEL_UNITS = [
     ("kda_prep.hip", []),
     ("kda_scan.hip", ["-mllvm", "-amdgpu-mfma-vgpr-form"]),  # accumulators in VGPRs: no AGPR copies in the chunk loop
+    ("kda_scan_pair.hip", []),
     ("kda_decode.hip", []),
     ("kda_bwd.hip", []),
     ("kda_noalloc.hip", []),

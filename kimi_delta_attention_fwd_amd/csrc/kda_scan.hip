@@ -796,6 +796,21 @@ kda_scan_many_k64_kernel(const unsigned char *rec_base, const int32_t *__restric
  * sequences the chunk-table kernel leaves after chunk_off.
  */
 #define KDA_MANY_CHAINS 128
+/* from this many chains up (and below KDA_MANY_CHAINS) the pair scan
+   (kda_scan_pair.hip, four CUs per chain instead of eight): 32 chains fill the
+   GPU with the three-wave kernel's 256 workgroups (one CU each), beyond that
+   they run in two or more rounds, while the pair scan runs 64 chains in one
+   (dense batch, 64 chains of 32 chunks: scan 0.053 ms against 0.063 ms). With
+   32 chains or fewer the three-wave kernel is faster (long prefill: 1.05 ms
+   against 1.31 ms). */
+#ifndef KDA_PAIR_MIN_CHAINS
+#define KDA_PAIR_MIN_CHAINS 33
+#endif
+
+extern "C" hipError_t kda_launch_scan_pair(const void *records, const int32_t *cu, const int32_t *chunk_off,
+                                           int64_t nseq, int64_t T, int64_t H, int64_t nslots, void *out,
+                                           const void *init_state, void *final_state, int state_fp32,
+                                           int64_t max_chains, const int32_t *long_list, hipStream_t st);
 
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
                                       int64_t nseq, int64_t T, int64_t H, int64_t nslots, int64_t K, int64_t V,
@@ -828,6 +843,9 @@ extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, co
         return hipGetLastError();
     }
     if (nchain < KDA_MANY_CHAINS) {
+        if (nchain >= KDA_PAIR_MIN_CHAINS)
+            return kda_launch_scan_pair(rec, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state,
+                                        state_fp32, nchain, nullptr, st);
         hipLaunchKernelGGL(kda_scan_kernel, dim3((unsigned)((nchain + 7) / 8 * 64)), dim3(192), 0, st, rec, cu,
                            chunk_off, nseq, T, (int)H, nslots, (uint16_t *)out, init_state, final_state, state_fp32,
                            (const int32_t *)nullptr);

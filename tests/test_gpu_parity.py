@@ -511,3 +511,44 @@ print("ok", e)
 """ % root
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and "ok" in r.stdout, r.stdout[-1000:] + r.stderr[-2000:]
+
+
+# From 33 to 127 (sequence, head) chains the scan runs as pairs of value tiles
+# (six waves per workgroup, four CUs per chain); 32 chains or fewer take the
+# three-wave kernel. Both evaluate the same chunk update in the same order, so a
+# head gives the same bits on either.
+@pytest.mark.parametrize("B,T,H,state", [(1, 1000, 33, "fp32"), (3, 333, 16, "bf16"), (2, 129, 50, None),
+                                         (1, 70, 127, "fp32")])
+def test_pair_scan(B, T, H, state):
+    gu = _gpu()
+    assert 33 <= B * H < 128
+    d = ki.make_inputs(B, T, H, seed=40 + H, state=state or "fp32", initial=state is not None, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=d["final"])
+    check("pair B=%d T=%d H=%d out" % (B, T, H), o, ro)
+    if d["final"]:
+        check_state("pair B=%d T=%d H=%d final" % (B, T, H), f, rf)
+    # the first head alone (B chains, the three-wave kernel): the same bits
+    e = gu.subset_heads(d, [0])
+    oe, fe = gu.run_gpu(e)
+    assert np.array_equal(oe[:, :, 0], o[:, :, 0])
+    if d["final"]:
+        assert np.array_equal(fe[:, 0], f[:, 0])
+
+
+def test_pair_scan_packed_and_in_place():
+    """40 packed sequences (with empty and one-token ones) on one head: the pair
+    scan over cu_seqlens, against the oracle and, for an in-place state, against
+    itself."""
+    gu = _gpu()
+    rng = np.random.default_rng(45)
+    lens = [0, 1, 64, 65, 700] + [int(x) for x in rng.integers(1, 400, 35)]
+    d = ki.make_inputs(1, sum(lens), 1, seed=45, lengths=lens, state="bf16", initial=True, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("pair packed out", o, ro)
+    check_state("pair packed final", f, rf)
+    init = ki.bf16_bits_to_f64(d["initial_state"])
+    assert np.array_equal(f[0], init[0])
+    o2, f2 = gu.run_gpu(d, in_place=True)
+    assert np.array_equal(o, o2) and np.array_equal(f, f2)
