@@ -118,8 +118,8 @@ kda_decode_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
 #pragma unroll
         for (int rr = 0; rr < 16; rr++) {
             u32x2 u;
-            u[0] = f2bf_bits(S[rr][0]) | ((uint32_t)f2bf_bits(S[rr][1]) << 16);
-            u[1] = f2bf_bits(S[rr][2]) | ((uint32_t)f2bf_bits(S[rr][3]) << 16);
+            u[0] = pack_bf16x2(S[rr][0], S[rr][1]);
+            u[1] = pack_bf16x2(S[rr][2], S[rr][3]);
             *(u32x2 *)&sp[(16 * cq + rr) * KDA_DV + 4 * jq] = u;
         }
     }
@@ -129,8 +129,8 @@ kda_decode_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k
 #pragma unroll
         for (int i = 0; i < 8; i++) o4 += s_red[i][jq];
         u32x2 u;
-        u[0] = f2bf_bits(o4[0]) | ((uint32_t)f2bf_bits(o4[1]) << 16);
-        u[1] = f2bf_bits(o4[2]) | ((uint32_t)f2bf_bits(o4[3]) << 16);
+        u[0] = pack_bf16x2(o4[0], o4[1]);
+        u[1] = pack_bf16x2(o4[2], o4[3]);
         *(u32x2 *)&out[vec0 + 4 * jq] = u;
     }
 }

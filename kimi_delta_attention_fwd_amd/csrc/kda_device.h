@@ -11,6 +11,7 @@
 #include "kda_internal.h"
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -34,6 +35,16 @@ __device__ __forceinline__ uint16_t f2bf_bits(float x)
 {
     __bf16 b = (__bf16)x; /* round to nearest even */
     return __builtin_bit_cast(uint16_t, b);
+}
+
+/* two floats -> a packed bf16 pair (a in the low half), round to nearest even; one
+   v_cvt_pk_bf16_f32 */
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
+{
+    bf16x2 r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 __device__ __forceinline__ bf16x8 pack8(const f32x4 &a, const f32x4 &b)

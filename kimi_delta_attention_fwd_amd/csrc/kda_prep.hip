@@ -119,10 +119,10 @@ __device__ __forceinline__ void store_transposed(const bf16x8 &fr, const bf16x8 
     const f32x4 d0 = mfma(fr, sel[0], zero4());
     const f32x4 d1 = mfma(fr, sel[1], zero4());
     uint2 u0, u1;
-    u0.x = f2bf_bits(d0[0]) | ((uint32_t)f2bf_bits(d0[1]) << 16);
-    u0.y = f2bf_bits(d0[2]) | ((uint32_t)f2bf_bits(d0[3]) << 16);
-    u1.x = f2bf_bits(d1[0]) | ((uint32_t)f2bf_bits(d1[1]) << 16);
-    u1.y = f2bf_bits(d1[2]) | ((uint32_t)f2bf_bits(d1[3]) << 16);
+    u0.x = pack_bf16x2(d0[0], d0[1]);
+    u0.y = pack_bf16x2(d0[2], d0[3]);
+    u1.x = pack_bf16x2(d1[0], d1[1]);
+    u1.y = pack_bf16x2(d1[2], d1[3]);
     *(uint2 *)dst0 = u0;
     *(uint2 *)dst1 = u1;
 }
@@ -154,7 +154,8 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     if (!locate_chunk(slot, cu, chunk_off, nseq, T, t0, L, seq)) return;
     unsigned char *rec = rec_base + ((size_t)h * nslots + slot) * RL::BYTES;
 
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, r16 = l & 15;
+    const int tid = threadIdx.x, l = tid & 63, g = l >> 4, r16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6); /* wave-uniform: branches on it are scalar */
     const int r = 16 * w + r16;
     const bool valid = r < L;
 
@@ -532,8 +533,8 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
         for (int jb = 0; jb < 2; jb++)
             if (jb < nkb) d = mfma(tbf[jb], sh.vt[nt][jb][l], d);
         uint2 u;
-        u.x = f2bf_bits(d[0]) | ((uint32_t)f2bf_bits(d[1]) << 16);
-        u.y = f2bf_bits(d[2]) | ((uint32_t)f2bf_bits(d[3]) << 16);
+        u.x = pack_bf16x2(d[0], d[1]);
+        u.y = pack_bf16x2(d[2], d[3]);
         *(uint2 *)(rec + RL::U + ((size_t)(nt * 64 + l) * 16 + w * 4) * 2) = u;
     }
     /* P TB, lane = token r, regs = j' */

@@ -154,8 +154,8 @@ __device__ __forceinline__ void output_step(ScanSetO &X, ScanSetO &Y, const unsi
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
         u32x2 u;
-        u[0] = f2bf_bits(O[mt][0]) | ((uint32_t)f2bf_bits(O[mt][1]) << 16);
-        u[1] = f2bf_bits(O[mt][2]) | ((uint32_t)f2bf_bits(O[mt][3]) << 16);
+        u[0] = pack_bf16x2(O[mt][0], O[mt][1]);
+        u[1] = pack_bf16x2(O[mt][2], O[mt][3]);
         __builtin_amdgcn_raw_buffer_store_b64(u, ro, (16 * mt + n16) * row_bytes + (16 * nt + 4 * g) * 2, 0, 0);
     }
 }
@@ -726,8 +726,8 @@ __device__ __forceinline__ void scan_many_body(const unsigned char *rec_base, co
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) {
             u32x2 u;
-            u[0] = f2bf_bits(O[mt][0]) | ((uint32_t)f2bf_bits(O[mt][1]) << 16);
-            u[1] = f2bf_bits(O[mt][2]) | ((uint32_t)f2bf_bits(O[mt][3]) << 16);
+            u[0] = pack_bf16x2(O[mt][0], O[mt][1]);
+            u[1] = pack_bf16x2(O[mt][2], O[mt][3]);
             __builtin_amdgcn_raw_buffer_store_b64(u, ro, (16 * mt + n16) * row_bytes + (16 * nt + 4 * g) * 2, 0, 0);
         }
 

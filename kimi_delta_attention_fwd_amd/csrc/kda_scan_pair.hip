@@ -184,8 +184,8 @@ __device__ __forceinline__ void pair_output_step(const PairNext &X, PairNext &Y,
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
         u32x2 o;
-        o[0] = f2bf_bits(O[mt][0]) | ((uint32_t)f2bf_bits(O[mt][1]) << 16);
-        o[1] = f2bf_bits(O[mt][2]) | ((uint32_t)f2bf_bits(O[mt][3]) << 16);
+        o[0] = pack_bf16x2(O[mt][0], O[mt][1]);
+        o[1] = pack_bf16x2(O[mt][2], O[mt][3]);
         __builtin_amdgcn_raw_buffer_store_b64(o, ro, (16 * mt + n16) * row_bytes + (16 * nt + 4 * g) * 2, 0, 0);
     }
 }
