@@ -41,7 +41,7 @@ SCAN_BYTES_PER_TH = 256
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "kimi_delta_attention_fwd_amd", "csrc")
 KERNEL_SOURCES = {"kda_prep": ("kda_prep.hip", "kda_device.h", "kda_internal.h", "../../include/kda.h"),
-                  "kda_scan": ("kda_scan.hip", "kda_device.h", "kda_internal.h"),
+                  "kda_scan": ("kda_scan.hip", "kda_scan_pair.hip", "kda_device.h", "kda_internal.h"),
                   "kda_decode": ("kda_decode.hip", "kda_device.h", "kda_internal.h"),
                   "kda_bwd_grad": ("kda_bwd.hip", "kda_device.h", "kda_internal.h")}
 # algorithmic MFMA flops per token-head with 16x16 blocks and 64-token chunks:
@@ -64,7 +64,7 @@ MALL_BYTES = 256 << 20
 # the long-prefill scan's kernel time in the committed kernel-stats profile; the
 # bench flags a run where it is more than 3 % slower (its warming loop's place
 # relative to instruction-fetch blocks moved it by up to 6 %)
-SCAN_REF_MS = {"long_prefill": 1.021}
+SCAN_REF_MS = {"long_prefill": 1.071}
 
 
 def cpu_model():
@@ -94,17 +94,21 @@ def kernel_source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, workload, counter=None):
     """HBM bytes per launch of ``kernel`` on ``workload`` from the counter
-    summary, or None if there is none for the current sources."""
+    summary (or, with ``counter``, that counter line's value), or None if there
+    is none for the current sources."""
     if kernel not in KERNEL_SOURCES or not os.path.exists(TRAFFIC_FILE):
         return None
     want = kernel_source_hash(kernel)
     with open(TRAFFIC_FILE) as fh:
         for line in fh:
+            if line.startswith("#"):
+                continue
             f = dict(kv.split("=", 1) for kv in line.split() if "=" in kv)
-            if f.get("kernel") == kernel and f.get("workload") == workload and f.get("src") == want:
-                return float(f["hbm_bytes"])
+            if f.get("kernel") == kernel and f.get("workload") == workload and f.get("src") == want \
+                    and f.get("counter") == counter:
+                return float(f["value" if counter else "hbm_bytes"])
     return None
 
 
@@ -268,6 +272,16 @@ def main():
         traffic += t or 0.0
     achieved = path_bytes / (event_ms * 1e-3) / 1e9
     path_tflops = th * FLOPS_PER_TH / (event_ms * 1e-3) / 1e12
+    # bf16 MFMA flops the counters saw per launch (prep selector MFMAs included)
+    mfma_counted = 0.0
+    for name in kernels:
+        if name == "kda_chunk_map":
+            continue
+        c = measured_traffic(name, d["name"], counter="mfma_bf16_flops")
+        if c is None:
+            mfma_counted = None
+            break
+        mfma_counted += c
 
     res = {
         "metric": METRIC,
@@ -295,7 +309,9 @@ def main():
                      "traffic_ratio": None if traffic is None else traffic / path_bytes,
                      "kernel": "kda_fwd step (%s)" % ", ".join(sorted(kernels)),
                      "launch_ms": event_ms, "alg_bytes_per_launch": path_bytes,
-                     "mfma_frac": path_tflops / PEAK_BF16_TFLOPS},
+                     "mfma_frac": path_tflops / PEAK_BF16_TFLOPS,
+                     "mfma_frac_counter": None if mfma_counted is None else
+                     mfma_counted / (event_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "kernels": per_kernel,
         "dominant_kernel": dom,
         "mall": mall,
