@@ -43,7 +43,10 @@ CSRC = os.path.join(ROOT, "kimi_delta_attention_fwd_amd", "csrc")
 KERNEL_SOURCES = {"kda_prep": ("kda_prep.hip", "kda_device.h", "kda_internal.h", "../../include/kda.h"),
                   "kda_scan": ("kda_scan.hip", "kda_scan_pair.hip", "kda_device.h", "kda_internal.h"),
                   "kda_decode": ("kda_decode.hip", "kda_device.h", "kda_internal.h"),
-                  "kda_bwd_grad": ("kda_bwd.hip", "kda_device.h", "kda_internal.h")}
+                  "kda_bwd_chunk": ("kda_bwd.hip", "kda_device.h", "kda_internal.h"),
+                  "kda_bwd_scan": ("kda_bwd.hip", "kda_device.h", "kda_internal.h"),
+                  "kda_bwd_grad": ("kda_bwd.hip", "kda_device.h", "kda_internal.h"),
+                  "kda_bwd_reduce": ("kda_bwd.hip", "kda_device.h", "kda_internal.h")}
 # algorithmic MFMA flops per token-head with 16x16 blocks and 64-token chunks:
 # state-side 6*K*V + intra-chunk 2*C*(3K + 2V)
 FLOPS_PER_TH = 6 * 128 * 128 + 2 * 64 * (3 * 128 + 2 * 128)
@@ -55,6 +58,9 @@ FLOPS_PER_TH = 6 * 128 * 128 + 2 * 64 * (3 * 128 + 2 * 128)
 # 64x128x64), T^T dT (64^3) and the lower triangle of X1 T^T (64^3 / 2), 2 flops
 # per multiply-add; the two pairwise passes take 17 flops per (i, j <= i, channel)
 PEAK_FP32_TFLOPS = 157.3
+# algorithmic HBM bytes per token-head of the backward: q, k, g, v, dout read in
+# bf16 (5 x 256), beta 2; dq, dk, dg, dv written in fp32 (4 x 512), dbeta 4
+BWD_BYTES_PER_TH = 5 * 256 + 2 + 4 * 512 + 4
 BWD_GRAD_FLOPS_PER_TH = (2 * (5 * 64 * 128 * 128 + 8 * 64 * 64 * 128 + 64 ** 3 + 64 ** 3 // 2)
                          + 17 * (64 * 65 // 2) * 128) / 64.0
 
@@ -388,12 +394,17 @@ def run_decode(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    kda.profile_enable(True)
+    # the timed region: K uninstrumented calls; the kernel time from a second,
+    # instrumented pass
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    kda.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     kda.profile_enable(False)
     prof = kda.profile_read()
     kern_ms = prof["kda_decode"][0] / prof["kda_decode"][1]
@@ -493,12 +504,21 @@ def run_backward(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    kda.profile_enable(True)
+    # the timed region: K uninstrumented calls, synchronised on both sides
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    event_ms = ev0.elapsed_time(ev1) / args.steps
+    # per-kernel times from a second, instrumented pass
+    kda.profile_enable(True)
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     kda.profile_enable(False)
     prof = kda.profile_read()
     kern = {name: ms / n for name, (ms, n) in prof.items()}
@@ -511,7 +531,22 @@ def run_backward(args):
         del src, dst
     units = ki.token_heads(d)
     grad_ms = kern["kda_bwd_grad"]
-    achieved = units * BWD_GRAD_FLOPS_PER_TH / (grad_ms * 1e-3) / 1e12
+    grad_tflops = units * BWD_GRAD_FLOPS_PER_TH / (grad_ms * 1e-3) / 1e12
+    # the step's algorithmic bytes: activations, output gradient and gradients,
+    # plus the initial state read, the final-state gradient read and the
+    # initial-state gradient written
+    sb = 128 * 128
+    state_b = N * H * sb * ((4 if d["state_dtype"] == "fp32" else 2) if init is not None else 0)
+    state_b += N * H * sb * 4 * ((1 if dfin is not None else 0) + 1)
+    step_bytes = units * BWD_BYTES_PER_TH + state_b
+    traffic = 0.0
+    per_kernel = {}
+    for name, ms in kern.items():
+        t = measured_traffic(name, d["name"] + "_backward")
+        per_kernel[name] = {"ms": ms, "traffic": t,
+                            "traffic_frac_hbm": None if t is None else t / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        traffic = None if (traffic is None or t is None) else traffic + t
+    achieved = step_bytes / (event_ms * 1e-3) / 1e9
     res = {
         "metric": "KDA bwd tokens*heads/s (gradients of q, k, v, g, beta, A_log, dt_bias, initial state)",
         "value": units * args.steps / wall, "unit": "token*heads/s", "n_gpus": 1, "steps": args.steps,
@@ -519,16 +554,27 @@ def run_backward(args):
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded numpy draws)",
         "config": {"workload": "%s backward: B=%d T=%d H=%d, bf16 inputs, fp32 gradients" % (d["name"], B, T, H),
                    "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU"},
-        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_TFLOPS,
-                     "traffic": measured_traffic("kda_bwd_grad", d["name"] + "_backward"), "kernel": "kda_bwd_grad",
-                     "kernel_ms": grad_ms, "alg_flops_per_launch": units * BWD_GRAD_FLOPS_PER_TH},
+        # the whole kda_bwd call against the HBM roofline with its algorithmic
+        # bytes; the counters show what the kernels actually move (the gradient
+        # kernel's product operands go through HBM: traffic_ratio), and the
+        # gradient kernel's algorithmic flops against the fp32 vector peak
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "traffic_ratio": None if traffic is None else traffic / step_bytes,
+                     "kernel": "kda_bwd step (%s)" % ", ".join(sorted(kern)), "launch_ms": event_ms,
+                     "alg_bytes_per_launch": step_bytes,
+                     "grad_kernel_fp32": {"achieved": grad_tflops, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                                          "frac": grad_tflops / PEAK_FP32_TFLOPS, "kernel_ms": grad_ms,
+                                          "alg_flops_per_launch": units * BWD_GRAD_FLOPS_PER_TH}},
+        "kernels": per_kernel,
         "kernels_ms": kern,
     }
     if not args.no_cpu:
         from threadpoolctl import threadpool_limits
 
         from oracle import backward as obwd
+        # the numpy reverse pass is single-threaded (per-token steps on small
+        # matrices; threads over heads measured slower, the interpreter lock)
         ts = min(T, 256)
         sub = lambda a: None if a is None else np.ascontiguousarray(a[:, :ts])
         tc, reps = 0.0, 0
