@@ -161,7 +161,8 @@ __device__ __forceinline__ void output_step(ScanSetO &X, ScanSetO &Y, const unsi
 }
 
 /* one 1 KiB LDS-DMA load (64 lanes x 16 bytes) that nobody waits for; m0 is not
-   otherwise used in this kernel (LDS instructions on gfx9 do not read it) */
+   otherwise used in this kernel (LDS instructions on gfx9 do not read it; the
+   generated code is checked for that by tests/test_isa_guards.py) */
 __device__ __forceinline__ void warm_l2(const unsigned char *p, uint32_t lds_addr)
 {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(lds_addr) : "memory", "m0");

@@ -50,7 +50,8 @@ static_assert(4 * KDA_PWARM_RANGE >= KDA_REC_BYTES && KDA_PWARM_RANGE % 128 == 0
 static_assert(2 * KDA_PCP0_TAIL + KDA_PCP_QP < 63, "copies in flight within the vmcnt range");
 
 /* one 1 KiB LDS-DMA copy (lane l: 16 bytes to lds_addr + 16 l); lds_addr is the
-   same in every lane (an SGPR operand) */
+   same in every lane (an SGPR operand). The compiler keeps nothing of its own in
+   m0 in this file (checked on the generated code by tests/test_isa_guards.py). */
 __device__ __forceinline__ void pair_copy(const unsigned char *p, uint32_t lds_addr)
 {
     const uint32_t a = __builtin_amdgcn_readfirstlane(lds_addr);
