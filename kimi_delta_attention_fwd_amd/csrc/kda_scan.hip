@@ -5,7 +5,8 @@
  * kda_internal.h). kda_launch_scan picks one of three forms from the sizes
  * alone (no device data is read on the host):
  *   kda_scan_kernel       3 waves per (chain, 16 value columns): fewer than 128
- *                         chains, and the long sequences of packed batches;
+ *                         chains, and the long sequences of packed batches
+ *                         (kda_scan_k64_kernel: the same at K = V = 64);
  *   kda_scan_many_kernel  8 waves per chain, the chunk's shared operands in
  *                         LDS: 128 chains or more;
  *   kda_seg_map_kernel, kda_seg_chain_kernel, kda_scan_seg_kernel
@@ -37,46 +38,47 @@
  * not track them and no wave ever waits for them, except wave 2 once before it
  * exits (its LDS must not be released with DMA writes in flight).
  */
-struct ScanSetS {
-    bf16x8 W[16], K[16], U[2];
-    f32x4 gl[8]; /* e^{G_L} for key rows 16 mt + 4 g + e */
+/* NKB = DK / 32 key blocks (W, Q', K~^T hold 4 NKB fragments each) */
+template <int NKB> struct ScanSetS {
+    bf16x8 W[4 * NKB], K[4 * NKB], U[2];
+    f32x4 gl[2 * NKB]; /* e^{G_L} for key rows 16 mt + 4 g + e */
 };
-struct ScanSetO {
-    bf16x8 Q[16], P[6], U[2];
+template <int NKB> struct ScanSetO {
+    bf16x8 Q[4 * NKB], P[6], U[2];
 };
-
-/* buffer descriptor over one chunk record: SGPR base, lane offsets in VGPRs */
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const unsigned char *rec)
-{
-    return buf_rsrc(rec, KDA_REC_BYTES);
-}
 
 __device__ __forceinline__ bf16x8 bufld(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-__device__ __forceinline__ void load_set(ScanSetS &X, const unsigned char *rec, int ubase, int l, int g)
+/* one chunk record (layout RecLayout<NKB, NVT>) through a buffer descriptor:
+   SGPR base, lane offsets in VGPRs */
+template <int NKB, int NVT>
+__device__ __forceinline__ void load_set(ScanSetS<NKB> &X, const unsigned char *rec, int ubase, int l, int g)
 {
-    const __amdgpu_buffer_rsrc_t r = rec_rsrc(rec);
+    using RL = RecLayout<NKB, NVT>;
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(rec, RL::BYTES);
 #pragma unroll
-    for (int f = 0; f < 16; f++) X.W[f] = bufld(r, l * 16, KDA_REC_W + f * 1024);
+    for (int f = 0; f < 4 * NKB; f++) X.W[f] = bufld(r, l * 16, RL::W + f * 1024);
     X.U[0] = bufld(r, l * 32, ubase);
     X.U[1] = bufld(r, l * 32, ubase + 16);
 #pragma unroll
-    for (int mt = 0; mt < 8; mt++)
-        X.gl[mt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, g * 16, KDA_REC_GL + mt * 64, 0));
+    for (int mt = 0; mt < 2 * NKB; mt++)
+        X.gl[mt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, g * 16, RL::GL + mt * 64, 0));
 #pragma unroll
-    for (int f = 0; f < 16; f++) X.K[f] = bufld(r, l * 16, KDA_REC_KT + f * 1024);
+    for (int f = 0; f < 4 * NKB; f++) X.K[f] = bufld(r, l * 16, RL::KT + f * 1024);
 }
 
-__device__ __forceinline__ void load_set(ScanSetO &X, const unsigned char *rec, int ubase, int l, int g)
+template <int NKB, int NVT>
+__device__ __forceinline__ void load_set(ScanSetO<NKB> &X, const unsigned char *rec, int ubase, int l, int g)
 {
-    const __amdgpu_buffer_rsrc_t r = rec_rsrc(rec);
+    using RL = RecLayout<NKB, NVT>;
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(rec, RL::BYTES);
 #pragma unroll
-    for (int f = 0; f < 16; f++) X.Q[f] = bufld(r, l * 16, KDA_REC_Q + f * 1024);
+    for (int f = 0; f < 4 * NKB; f++) X.Q[f] = bufld(r, l * 16, RL::Q + f * 1024);
 #pragma unroll
-    for (int f = 0; f < 6; f++) X.P[f] = bufld(r, l * 16, KDA_REC_P + f * 1024);
+    for (int f = 0; f < 6; f++) X.P[f] = bufld(r, l * 16, RL::P + f * 1024);
     X.U[0] = bufld(r, l * 32, ubase);
     X.U[1] = bufld(r, l * 32, ubase + 16);
 }
@@ -89,13 +91,14 @@ __device__ __forceinline__ void chunk_barrier()
 }
 
 /* state wave: X holds chunk c; loads chunk c + 1 (at nrec) into Y */
-__device__ __forceinline__ void state_step(ScanSetS &X, ScanSetS &Y, f32x4 (&S)[8], const unsigned char *nrec,
-                                           int ubase, bf16x8 *slot, int l, int g)
+template <int NKB, int NVT>
+__device__ __forceinline__ void state_step(ScanSetS<NKB> &X, ScanSetS<NKB> &Y, f32x4 (&S)[2 * NKB],
+                                           const unsigned char *nrec, int ubase, bf16x8 *slot, int l, int g)
 {
-    load_set(Y, nrec, ubase, l, g);
-    bf16x8 sb[4];
+    load_set<NKB, NVT>(Y, nrec, ubase, l, g);
+    bf16x8 sb[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
+    for (int kb = 0; kb < NKB; kb++) {
         sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
         slot[kb * 64 + l] = sb[kb];
     }
@@ -109,48 +112,50 @@ __device__ __forceinline__ void state_step(ScanSetS &X, ScanSetS &Y, f32x4 (&S)[
     }
     /* D = U - W S */
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++)
+    for (int kb = 0; kb < NKB; kb++)
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++) D[mt] = mfma(X.W[mt * 4 + kb], sb[kb], D[mt]);
+        for (int mt = 0; mt < 4; mt++) D[mt] = mfma(X.W[mt * NKB + kb], sb[kb], D[mt]);
     /* S <- diag(e^{G_L}) S + K~^T D */
 #pragma unroll
-    for (int mt = 0; mt < 8; mt++) S[mt] *= X.gl[mt];
+    for (int mt = 0; mt < 2 * NKB; mt++) S[mt] *= X.gl[mt];
     bf16x8 db[2];
     db[0] = pack8(D[0], D[1]);
     db[1] = pack8(D[2], D[3]);
 #pragma unroll
     for (int jb = 0; jb < 2; jb++)
 #pragma unroll
-        for (int mt = 0; mt < 8; mt++) S[mt] = mfma(X.K[mt * 2 + jb], db[jb], S[mt]);
+        for (int mt = 0; mt < 2 * NKB; mt++) S[mt] = mfma(X.K[mt * 2 + jb], db[jb], S[mt]);
 }
 
 /* output wave: X holds chunk c (tokens t0 .. t0 + L - 1); loads chunk c + 1 into Y.
    out is written through a buffer descriptor bounded at row L - 1: rows past
    the sequence end fall outside it and the hardware drops their stores. */
-__device__ __forceinline__ void output_step(ScanSetO &X, ScanSetO &Y, const unsigned char *nrec, int ubase,
-                                            const bf16x8 *slot, uint16_t *out, int64_t t0, int L, int H,
-                                            int h, int nt, int l, int g, int n16)
+template <int NKB, int NVT>
+__device__ __forceinline__ void output_step(ScanSetO<NKB> &X, ScanSetO<NKB> &Y, const unsigned char *nrec,
+                                            int ubase, const bf16x8 *slot, uint16_t *out, int64_t t0, int L,
+                                            int H, int h, int nt, int l, int g, int n16)
 {
-    load_set(Y, nrec, ubase, l, g);
+    constexpr int DV = 16 * NVT;
+    load_set<NKB, NVT>(Y, nrec, ubase, l, g);
     chunk_barrier();
-    bf16x8 sb[4];
+    bf16x8 sb[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) sb[kb] = slot[kb * 64 + l];
+    for (int kb = 0; kb < NKB; kb++) sb[kb] = slot[kb * 64 + l];
     /* out^T = S^T Q'^T + U^T P^T   (lane = token, regs = 4 value columns) */
     f32x4 O[4];
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) O[mt] = zero4();
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++)
+    for (int kb = 0; kb < NKB; kb++)
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++) O[mt] = mfma(sb[kb], X.Q[mt * 4 + kb], O[mt]);
+        for (int mt = 0; mt < 4; mt++) O[mt] = mfma(sb[kb], X.Q[mt * NKB + kb], O[mt]);
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
 #pragma unroll
         for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(X.U[jb], X.P[KDA_PIDX(mt, jb)], O[mt]);
-    const int row_bytes = H * KDA_DV * 2;
+    const int row_bytes = H * DV * 2;
     const __amdgpu_buffer_rsrc_t ro =
-        buf_rsrc(out + ((size_t)t0 * H + h) * KDA_DV, (uint32_t)((L - 1) * row_bytes + KDA_DV * 2));
+        buf_rsrc(out + ((size_t)t0 * H + h) * DV, (uint32_t)((L - 1) * row_bytes + DV * 2));
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
         u32x2 u;
@@ -173,9 +178,11 @@ __device__ __forceinline__ void warm_l2(const unsigned char *p, uint32_t lds_add
    8 -> 1.150) */
 #define KDA_WARM_AHEAD 3
 
-/* the scan body; SEG instantiates the segment-parallel rescan (one workgroup per
-   (chain, segment, tile)), which the plain kernel compiles without */
-template <bool SEG>
+/* the scan body over DK = 32 NKB key channels and NVT value tiles of 16 columns
+   (record layout RecLayout<NKB, NVT>); SEG instantiates the segment-parallel
+   rescan (one workgroup per (chain, segment, tile)), which the plain kernel
+   compiles without */
+template <bool SEG, int NKB, int NVT>
 __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
                                           const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H,
                                           int64_t nslots, uint16_t *__restrict__ out,
@@ -183,15 +190,18 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
                                           int state_fp32, const int32_t *__restrict__ long_list, int64_t nseg,
                                           int64_t segc, const float *__restrict__ seg_init)
 {
-    __shared__ bf16x8 ring[2][4 * 64];                          /* 8 KiB: S(c) in bf16 */
+    using RL = RecLayout<NKB, NVT>;
+    constexpr int DK = 32 * NKB, DV = 16 * NVT;
+    static_assert((NVT & (NVT - 1)) == 0, "value tiles: a power of two");
+    __shared__ bf16x8 ring[2][NKB * 64];                        /* S(c) in bf16 (8 KiB at DK = 128) */
     __shared__ __attribute__((aligned(16))) unsigned char warm_sink[1024];
     const int wave = threadIdx.x >> 6;
     const int l = threadIdx.x & 63, g = l >> 4, n16 = l & 15;
-    /* the 8 value tiles of a chain run on one XCD (blockIdx % 8) and share its L2 */
+    /* the NVT value tiles of a chain run on one XCD (blockIdx % 8) and share its L2 */
     const int64_t b = blockIdx.x;
     const int64_t xcd = b & 7, qd = b >> 3;
-    const int nt = (int)(qd & 7);
-    const int64_t cs = (qd >> 3) * 8 + xcd;
+    const int nt = (int)(qd & (NVT - 1));
+    const int64_t cs = (qd / NVT) * 8 + xcd;
     /* cs = ci * nseg + segment; ci is the chain (sequence * H + head), or with a
        long-sequence list (long_list[0] entries, then sequence indices) the list
        slot * H + head */
@@ -229,7 +239,7 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
        it); only the sequence's last segment writes the final state */
     const void *ist = init_state;
     int ist_fp32 = state_fp32;
-    size_t ibase = (size_t)chain * KDA_DK * KDA_DV;
+    size_t ibase = (size_t)chain * DK * DV;
     void *fst = final_state;
     if (SEG) {
         const int64_t nseg_seq = nchunk > segc ? (nchunk + segc - 1) / segc : 1;
@@ -240,22 +250,22 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
         slot0 += c_first;
         ist = seg_init;
         ist_fp32 = 1;
-        ibase = ((size_t)chain * nseg + seg) * KDA_DK * KDA_DV;
+        ibase = ((size_t)chain * nseg + seg) * DK * DV;
         if (seg < nseg_seq - 1) fst = nullptr;
     }
-    const unsigned char *rec0 = rec_base + ((size_t)h * nslots + slot0) * KDA_REC_BYTES;
+    const unsigned char *rec0 = rec_base + ((size_t)h * nslots + slot0) * RL::BYTES;
     /* record of chunk c, clamped to the last one (its reload is harmless) */
-    auto rec_of = [&](int64_t c) { return rec0 + (size_t)(c < nchunk ? c : nchunk - 1) * KDA_REC_BYTES; };
-    const int ubase = KDA_REC_U + nt * 2048; /* this tile's 2 KiB of U; lane l reads 32 bytes */
+    auto rec_of = [&](int64_t c) { return rec0 + (size_t)(c < nchunk ? c : nchunk - 1) * RL::BYTES; };
+    const int ubase = RL::U + nt * 2048; /* this tile's 2 KiB of U; lane l reads 32 bytes */
 
     if (wave == 0) {
         /* ---------------- state wave ---------------- */
-        f32x4 S[8];
+        f32x4 S[2 * NKB];
 #pragma unroll
-        for (int mt = 0; mt < 8; mt++) {
+        for (int mt = 0; mt < 2 * NKB; mt++) {
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                const size_t idx = ibase + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
+                const size_t idx = ibase + (size_t)(16 * mt + 4 * g + e) * DV + vcol;
                 float sv = 0.f;
                 if (ist)
                     sv = ist_fp32 ? ((const float *)ist)[idx] : bf2f(((const uint16_t *)ist)[idx]);
@@ -263,27 +273,27 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
             }
         }
         if (nchunk > 0) {
-            ScanSetS X, Y;
+            ScanSetS<NKB> X, Y;
             int64_t c = 0;
             if (nchunk & 1) {
-                load_set(X, rec_of(0), ubase, l, g);
-                state_step(X, Y, S, rec_of(1), ubase, ring[0], l, g);
+                load_set<NKB, NVT>(X, rec_of(0), ubase, l, g);
+                state_step<NKB, NVT>(X, Y, S, rec_of(1), ubase, ring[0], l, g);
                 c = 1;
             } else {
-                load_set(Y, rec_of(0), ubase, l, g);
+                load_set<NKB, NVT>(Y, rec_of(0), ubase, l, g);
             }
             for (; c < nchunk; c += 2) {
-                state_step(Y, X, S, rec_of(c + 1), ubase, ring[c & 1], l, g);
-                state_step(X, Y, S, rec_of(c + 2), ubase, ring[(c + 1) & 1], l, g);
+                state_step<NKB, NVT>(Y, X, S, rec_of(c + 1), ubase, ring[c & 1], l, g);
+                state_step<NKB, NVT>(X, Y, S, rec_of(c + 2), ubase, ring[(c + 1) & 1], l, g);
             }
         }
         if (fst) {
-            const size_t sbase2 = (size_t)chain * KDA_DK * KDA_DV;
+            const size_t sbase2 = (size_t)chain * DK * DV;
 #pragma unroll
-            for (int mt = 0; mt < 8; mt++)
+            for (int mt = 0; mt < 2 * NKB; mt++)
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
-                    const size_t idx = sbase2 + (size_t)(16 * mt + 4 * g + e) * KDA_DV + vcol;
+                    const size_t idx = sbase2 + (size_t)(16 * mt + 4 * g + e) * DV + vcol;
                     if (state_fp32) ((float *)fst)[idx] = S[mt][e];
                     else ((uint16_t *)fst)[idx] = f2bf_bits(S[mt][e]);
                 }
@@ -291,7 +301,7 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     } else if (wave == 1) {
         /* ---------------- output wave ---------------- */
         if (nchunk > 0) {
-            ScanSetO X, Y;
+            ScanSetO<NKB> X, Y;
             int64_t c = 0;
             auto t0_of = [&](int64_t cc) { return bos + cc * KDA_CHUNK; };
             auto len_of = [&](int64_t cc) {
@@ -299,17 +309,18 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
                 return (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
             };
             if (nchunk & 1) {
-                load_set(X, rec_of(0), ubase, l, g);
-                output_step(X, Y, rec_of(1), ubase, ring[0], out, t0_of(0), len_of(0), H, h, nt, l, g, n16);
+                load_set<NKB, NVT>(X, rec_of(0), ubase, l, g);
+                output_step<NKB, NVT>(X, Y, rec_of(1), ubase, ring[0], out, t0_of(0), len_of(0), H, h, nt, l, g,
+                                      n16);
                 c = 1;
             } else {
-                load_set(Y, rec_of(0), ubase, l, g);
+                load_set<NKB, NVT>(Y, rec_of(0), ubase, l, g);
             }
             for (; c < nchunk; c += 2) {
-                output_step(Y, X, rec_of(c + 1), ubase, ring[c & 1], out, t0_of(c), len_of(c), H, h, nt, l, g,
-                            n16);
-                output_step(X, Y, rec_of(c + 2), ubase, ring[(c + 1) & 1], out, t0_of(c + 1), len_of(c + 1), H,
-                            h, nt, l, g, n16);
+                output_step<NKB, NVT>(Y, X, rec_of(c + 1), ubase, ring[c & 1], out, t0_of(c), len_of(c), H, h, nt,
+                                      l, g, n16);
+                output_step<NKB, NVT>(X, Y, rec_of(c + 2), ubase, ring[(c + 1) & 1], out, t0_of(c + 1),
+                                      len_of(c + 1), H, h, nt, l, g, n16);
             }
         }
     } else {
@@ -325,12 +336,12 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
             asm volatile(".p2align 5\n\ts_nop 0\n\ts_nop 0");
             const int64_t cw = c + KDA_WARM_AHEAD;
             if (cw < nchunk) {
-                const unsigned char *r = rec0 + (size_t)cw * KDA_REC_BYTES;
-                /* this tile's eighth of the shared operands, 1 KiB pieces */
-                for (int i = nt; i < KDA_REC_U / 1024 + 1; i += 8) warm_l2(r + i * 1024 + l * 16, lds);
+                const unsigned char *r = rec0 + (size_t)cw * RL::BYTES;
+                /* this tile's share of the shared operands, 1 KiB pieces */
+                for (int i = nt; i < RL::U / 1024 + 1; i += NVT) warm_l2(r + i * 1024 + l * 16, lds);
                 /* and its own 2 KiB of U */
-                warm_l2(r + KDA_REC_U + nt * 2048 + l * 16, lds);
-                warm_l2(r + KDA_REC_U + nt * 2048 + 1024 + l * 16, lds);
+                warm_l2(r + RL::U + nt * 2048 + l * 16, lds);
+                warm_l2(r + RL::U + nt * 2048 + 1024 + l * 16, lds);
             }
             chunk_barrier();
         }
@@ -344,8 +355,18 @@ kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__res
                 uint16_t *__restrict__ out, const void *init_state,
                 void *final_state, int state_fp32, const int32_t *__restrict__ long_list)
 {
-    scan_body<false>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state, state_fp32, long_list,
-                     1, 0, nullptr);
+    scan_body<false, 4, 8>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state, state_fp32,
+                           long_list, 1, 0, nullptr);
+}
+
+/* K = V = 64: four value tiles per chain */
+extern "C" __global__ void __launch_bounds__(192)
+kda_scan_k64_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
+                    const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
+                    uint16_t *__restrict__ out, const void *init_state, void *final_state, int state_fp32)
+{
+    scan_body<false, 2, 4>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state, state_fp32,
+                           nullptr, 1, 0, nullptr);
 }
 
 /* the rescan of the segment-parallel scan: workgroup (chain, segment slot, tile) */
@@ -355,8 +376,8 @@ kda_scan_seg_kernel(const unsigned char *__restrict__ rec_base, const int32_t *_
                     uint16_t *__restrict__ out, void *final_state, int state_fp32, int64_t nseg,
                     int64_t segc, const float *__restrict__ seg_init)
 {
-    scan_body<true>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, nullptr, final_state, state_fp32, nullptr,
-                    nseg, segc, seg_init);
+    scan_body<true, 4, 8>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, nullptr, final_state, state_fp32, nullptr,
+                          nseg, segc, seg_init);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -378,10 +399,10 @@ kda_scan_seg_kernel(const unsigned char *__restrict__ rec_base, const int32_t *_
  */
 
 /* state-only chunk step: X holds chunk c, loads chunk c + 1 (at nrec) into Y */
-__device__ __forceinline__ void map_step(ScanSetS &X, ScanSetS &Y, f32x4 (&S)[8], const unsigned char *nrec,
+__device__ __forceinline__ void map_step(ScanSetS<4> &X, ScanSetS<4> &Y, f32x4 (&S)[8], const unsigned char *nrec,
                                          int ubase, int l, int g, bool homog)
 {
-    load_set(Y, nrec, ubase, l, g);
+    load_set<4, 8>(Y, nrec, ubase, l, g);
     bf16x8 sb[4];
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) sb[kb] = pack8(S[2 * kb], S[2 * kb + 1]);
@@ -458,14 +479,14 @@ kda_seg_map_kernel(const unsigned char *rec_base, const int32_t *__restrict__ cu
     for (int mt = 0; mt < 8; mt++)
 #pragma unroll
         for (int e = 0; e < 4; e++) S[mt][e] = (homog && 16 * mt + 4 * g + e == 16 * nt + n16) ? 1.f : 0.f;
-    ScanSetS X, Y;
+    ScanSetS<4> X, Y;
     int64_t c = 0;
     if (segc & 1) {
-        load_set(X, rec_of(0), ubase, l, g);
+        load_set<4, 8>(X, rec_of(0), ubase, l, g);
         map_step(X, Y, S, rec_of(1), ubase, l, g, homog);
         c = 1;
     } else {
-        load_set(Y, rec_of(0), ubase, l, g);
+        load_set<4, 8>(Y, rec_of(0), ubase, l, g);
     }
     for (; c < segc; c += 2) {
         map_step(Y, X, S, rec_of(c + 1), ubase, l, g, homog);
@@ -820,9 +841,18 @@ extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, co
 {
     const unsigned char *rec = (const unsigned char *)records;
     const int64_t nchain = nseq * H;
-    if (K == 64 && V == 64) { /* other head dims: the many-chain form for every chain */
-        hipLaunchKernelGGL(kda_scan_many_k64_kernel, dim3((unsigned)nchain), dim3(256), 0, st, rec, cu, chunk_off,
-                           nseq, T, (int)H, nslots, (uint16_t *)out, init_state, final_state, state_fp32);
+    if (K == 64 && V == 64) {
+        /* K = V = 64: the three-wave form (four value tiles per chain) for fewer
+           than KDA_MANY_CHAINS chains, the many-chain form for more; each takes
+           every chain of any length */
+        if (nchain < KDA_MANY_CHAINS)
+            hipLaunchKernelGGL(kda_scan_k64_kernel, dim3((unsigned)((nchain + 7) / 8 * 32)), dim3(192), 0, st, rec,
+                               cu, chunk_off, nseq, T, (int)H, nslots, (uint16_t *)out, init_state, final_state,
+                               state_fp32);
+        else
+            hipLaunchKernelGGL(kda_scan_many_k64_kernel, dim3((unsigned)nchain), dim3(256), 0, st, rec, cu,
+                               chunk_off, nseq, T, (int)H, nslots, (uint16_t *)out, init_state, final_state,
+                               state_fp32);
         return hipGetLastError();
     }
     if (K != KDA_DK || V != KDA_DV) return hipErrorInvalidValue;

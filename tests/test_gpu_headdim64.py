@@ -214,3 +214,28 @@ def test_k64_decode_and_bwd_rejected():
     with pytest.raises(ValueError, match="KDA_ERR_HEAD_DIM"):
         kda.decode(q1, q1, q1, q1, t["beta"][0], d["scale"], torch.empty_like(q1), t["A_log"], t["dt_bias"],
                    d["lower_bound"], st)
+
+
+def test_k64_three_wave_equals_many_chain_bitwise():
+    """Fewer than 128 chains take the three-wave scan (four value tiles per
+    chain), 128 or more the many-chain scan; both evaluate the chunk update in
+    the same order, so a sequence gives the same bits on either. 32 packed
+    sequences x 4 heads (128 chains) run on the many-chain form; the first 31
+    of them alone (124 chains) on the three-wave form."""
+    gu = _gpu()
+    rng = np.random.default_rng(123)
+    lens = [int(x) for x in rng.integers(1, 400, 32)]
+    d = mk(1, sum(lens), 4, seed=123, lengths=lens, state="fp32", initial=True, sigma=0.05)
+    o, f = gu.run_gpu(d)
+    ro, rf = oracle.fwd_inputs(d, want_final=True)
+    check("k64 128 chains out", o, ro)
+    check("k64 128 chains final", f, rf, row_ndim=2)
+    cu = d["cu_seqlens"]
+    t31 = int(cu[31])
+    e = dict(d)
+    for key in ("q", "k", "v", "g", "beta"):
+        e[key] = np.ascontiguousarray(d[key][:, :t31])
+    e.update(T=t31, N=31, cu_seqlens=np.ascontiguousarray(cu[:32]),
+             initial_state=np.ascontiguousarray(d["initial_state"][:31]))
+    o31, f31 = gu.run_gpu(e)
+    assert np.array_equal(o31, o[:, :t31]) and np.array_equal(f31, f[:31])
