@@ -32,9 +32,18 @@ if ROOT not in sys.path:
 METRIC = "KDA fwd tokens*heads/s + % of binding MFMA/HBM roofline, T=64K H=32"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-# algorithmic HBM bytes per token-head: q, k, g, v reads (4 x 256), out write (256), beta (2)
-PREP_BYTES_PER_TH = 4 * 256 + 2
-SCAN_BYTES_PER_TH = 256
+# algorithmic HBM bytes per token-head at K = V = D: q, k, g, v reads (4 x 2 D),
+# out write (2 D), beta (2)
+def prep_bytes_per_th(D=128):
+    return 4 * 2 * D + 2
+
+
+def scan_bytes_per_th(D=128):
+    return 2 * D
+
+
+PREP_BYTES_PER_TH = prep_bytes_per_th()
+SCAN_BYTES_PER_TH = scan_bytes_per_th()
 # HBM bytes per launch read from rocprofv3 FETCH_SIZE / WRITE_SIZE counters,
 # scaled by the same counters' reading for a device copy of known size; valid
 # only while the kernel's sources hash to the recorded value
@@ -49,7 +58,11 @@ KERNEL_SOURCES = {"kda_prep": ("kda_prep.hip", "kda_device.h", "kda_internal.h",
                   "kda_bwd_reduce": ("kda_bwd.hip", "kda_device.h", "kda_internal.h")}
 # algorithmic MFMA flops per token-head with 16x16 blocks and 64-token chunks:
 # state-side 6*K*V + intra-chunk 2*C*(3K + 2V)
-FLOPS_PER_TH = 6 * 128 * 128 + 2 * 64 * (3 * 128 + 2 * 128)
+def flops_per_th(D=128):
+    return 6 * D * D + 2 * 64 * (3 * D + 2 * D)
+
+
+FLOPS_PER_TH = flops_per_th()
 
 
 # backward: published fp32 vector peak of MI355X, and algorithmic flops per
@@ -87,7 +100,8 @@ def cpu_model():
 def state_bytes(d):
     if d["state_dtype"] is None:
         return 0
-    per = 128 * 128 * (4 if d["state_dtype"] == "fp32" else 2)
+    D = d.get("K", 128)
+    per = D * D * (4 if d["state_dtype"] == "fp32" else 2)
     n = (1 if d["initial_state"] is not None else 0) + (1 if d["final"] else 0)
     return n * d["N"] * d["H"] * per
 
@@ -139,6 +153,8 @@ def main():
                     help="keep only the first N heads of the workload (one GPU's share when heads are sharded)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, run 3 device copies of this many MiB (counter calibration)")
+    ap.add_argument("--head-dim", type=int, default=128, choices=(128, 64),
+                    help="K = V of the workload (the forward also takes 64)")
     ap.add_argument("--warm", action="store_true",
                     help="never flush the Infinity Cache between steps (small workloads are flushed by default)")
     args = ap.parse_args()
@@ -155,13 +171,19 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     kda.load_library()
+    if args.head_dim != 128 and (args.decode or args.backward):
+        print("bench.py: --decode and --backward run at K = V = 128 only", file=sys.stderr)
+        sys.exit(2)
     if args.decode:
         return run_decode(args)
     if args.backward:
         return run_backward(args)
     dev = "cuda:0"
     t_gen = time.time()
-    d = ki.config_inputs(args.config)
+    d = ki.config_inputs(args.config, head_dim=args.head_dim)
+    HD = args.head_dim
+    if HD != 128:
+        d["name"] = "%s_k%d" % (d["name"], HD)
     if 0 < args.heads < d["H"]:
         nh = args.heads
         for key in ("q", "k", "v", "g", "beta"):
@@ -185,10 +207,10 @@ def main():
     init = None
     if d["initial_state"] is not None:
         init = torch.from_numpy(d["initial_state"]).to(dev) if sdt == torch.float32 else bf(d["initial_state"])
-    fin = torch.empty((d["N"], d["H"], 128, 128), dtype=sdt, device=dev) if d["final"] else None
+    fin = torch.empty((d["N"], d["H"], HD, HD), dtype=sdt, device=dev) if d["final"] else None
     cu = None if d["cu_seqlens"] is None else torch.from_numpy(d["cu_seqlens"]).to(dev)
     B, T, H = d["B"], d["T"], d["H"]
-    out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((B, T, H, HD), dtype=torch.bfloat16, device=dev)
     nseq = 0 if cu is None else d["N"]
     ws = torch.empty(kda.workspace_size(B, T, H, nseq), dtype=torch.uint8, device=dev)
 
@@ -197,7 +219,7 @@ def main():
                 initial_state=init, final_state=fin, cu_seqlens=cu, workspace=ws)
 
     th = ki.token_heads(d)
-    path_bytes = th * (PREP_BYTES_PER_TH + SCAN_BYTES_PER_TH) + state_bytes(d)
+    path_bytes = th * (prep_bytes_per_th(HD) + scan_bytes_per_th(HD)) + state_bytes(d)
     # The 256 MB Infinity Cache (MALL) keeps a small workload's inputs between
     # steps. Working sets below twice its size are timed one step at a time with
     # a 512 MiB write between steps (outside the timed events), unless --warm.
@@ -258,8 +280,8 @@ def main():
         del src, dst
 
     kernels = {name: tot / cnt for name, (tot, cnt) in prof.items()}
-    alg_bytes = {"kda_prep": th * PREP_BYTES_PER_TH,
-                 "kda_scan": th * SCAN_BYTES_PER_TH + state_bytes(d),
+    alg_bytes = {"kda_prep": th * prep_bytes_per_th(HD),
+                 "kda_scan": th * scan_bytes_per_th(HD) + state_bytes(d),
                  "kda_chunk_map": 0}
     per_kernel = {}
     for name, ms in kernels.items():
@@ -277,7 +299,7 @@ def main():
             break
         traffic += t or 0.0
     achieved = path_bytes / (event_ms * 1e-3) / 1e9
-    path_tflops = th * FLOPS_PER_TH / (event_ms * 1e-3) / 1e12
+    path_tflops = th * flops_per_th(HD) / (event_ms * 1e-3) / 1e12
     # bf16 MFMA flops the counters saw per launch (prep selector MFMAs included)
     mfma_counted = 0.0
     for name in kernels:
@@ -302,8 +324,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded numpy draws, recipe in kda_inputs)",
-        "config": {"workload": "%s: B=%d T=%d H=%d K=V=128 chunk=64 lower_bound=%g state=%s%s" % (
-            d["name"], B, T, H, d["lower_bound"], d["state_dtype"],
+        "config": {"workload": "%s: B=%d T=%d H=%d K=V=%d chunk=64 lower_bound=%g state=%s%s" % (
+            d["name"], B, T, H, HD, d["lower_bound"], d["state_dtype"],
             " varlen N=%d" % d["N"] if cu is not None else ""),
             "global_batch": B, "seq_len": T, "heads": H, "parallelism": "single GPU"},
         # the unit of the roofline is one whole kda_fwd call (all of its kernels):

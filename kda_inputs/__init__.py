@@ -138,8 +138,9 @@ def make_inputs(B: int, T: int, H: int, seed: int = 0, *, lengths=None,
                 cu_seqlens=cu, B=B, T=T, H=H, N=N, K=K, V=V)
 
 
-def config_inputs(i: int, seed: int = 0) -> dict:
-    """Inputs of benchmark workload ``i`` (0..4), drawn from default_rng(seed)."""
+def config_inputs(i: int, seed: int = 0, head_dim: int = HEAD_DIM) -> dict:
+    """Inputs of benchmark workload ``i`` (0..4), drawn from default_rng(seed)
+    (at head dims K = V = ``head_dim``)."""
     c = CONFIGS[i]
     rng = np.random.default_rng(seed)
     lengths = None
@@ -151,7 +152,7 @@ def config_inputs(i: int, seed: int = 0) -> dict:
     d = make_inputs(c["B"], T, c["H"], lengths=lengths,
                     lower_bound=c["lower_bound"], state=c["state"],
                     initial=c["initial"], sigma=c["sigma"],
-                    dt_sigma=c["dt_sigma"], rng=rng)
+                    dt_sigma=c["dt_sigma"], rng=rng, head_dim=head_dim)
     d["config"] = i
     d["name"] = c["name"]
     return d
