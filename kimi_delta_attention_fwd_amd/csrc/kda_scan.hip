@@ -28,7 +28,9 @@
  *                  state that wave 0 leaves in a two-slot LDS ring.
  * wave 2 (L2 warm): touches its eighth of the record three chunks ahead with
  *                  LDS-DMA loads into a scratch LDS buffer, so that the eight
- *                  workgroups of a chain find their records in L2.
+ *                  workgroups of a chain find their records in L2; in the plain
+ *                  128-channel scan it also copies each chunk's K~^T two chunks
+ *                  ahead into a three-slot LDS ring that the state wave reads.
  * The three waves meet at one barrier per chunk. Waves 0 and 1 double-buffer
  * their record operands in registers: all loads for chunk c + 1 are issued at
  * the start of chunk c (two register sets alternate over a two-chunk unroll).
@@ -38,9 +40,10 @@
  * not track them and no wave ever waits for them, except wave 2 once before it
  * exits (its LDS must not be released with DMA writes in flight).
  */
-/* NKB = DK / 32 key blocks (W, Q', K~^T hold 4 NKB fragments each) */
-template <int NKB> struct ScanSetS {
-    bf16x8 W[4 * NKB], K[4 * NKB], U[2];
+/* NKB = DK / 32 key blocks (W, Q', K~^T hold 4 NKB fragments each); KR: K~^T in
+   the register set (else the state wave reads it from an LDS ring) */
+template <int NKB, bool KR = true> struct ScanSetS {
+    bf16x8 W[4 * NKB], K[KR ? 4 * NKB : 1], U[2];
     f32x4 gl[2 * NKB]; /* e^{G_L} for key rows 16 mt + 4 g + e */
 };
 template <int NKB> struct ScanSetO {
@@ -54,8 +57,8 @@ __device__ __forceinline__ bf16x8 bufld(__amdgpu_buffer_rsrc_t r, int voff, int 
 
 /* one chunk record (layout RecLayout<NKB, NVT>) through a buffer descriptor:
    SGPR base, lane offsets in VGPRs */
-template <int NKB, int NVT>
-__device__ __forceinline__ void load_set(ScanSetS<NKB> &X, const unsigned char *rec, int ubase, int l, int g)
+template <int NKB, int NVT, bool KR = true>
+__device__ __forceinline__ void load_set(ScanSetS<NKB, KR> &X, const unsigned char *rec, int ubase, int l, int g)
 {
     using RL = RecLayout<NKB, NVT>;
     const __amdgpu_buffer_rsrc_t r = buf_rsrc(rec, RL::BYTES);
@@ -66,8 +69,10 @@ __device__ __forceinline__ void load_set(ScanSetS<NKB> &X, const unsigned char *
 #pragma unroll
     for (int mt = 0; mt < 2 * NKB; mt++)
         X.gl[mt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, g * 16, RL::GL + mt * 64, 0));
+    if constexpr (KR) {
 #pragma unroll
-    for (int f = 0; f < 4 * NKB; f++) X.K[f] = bufld(r, l * 16, RL::KT + f * 1024);
+        for (int f = 0; f < 4 * NKB; f++) X.K[f] = bufld(r, l * 16, RL::KT + f * 1024);
+    }
 }
 
 template <int NKB, int NVT>
@@ -91,11 +96,12 @@ __device__ __forceinline__ void chunk_barrier()
 }
 
 /* state wave: X holds chunk c; loads chunk c + 1 (at nrec) into Y */
-template <int NKB, int NVT>
-__device__ __forceinline__ void state_step(ScanSetS<NKB> &X, ScanSetS<NKB> &Y, f32x4 (&S)[2 * NKB],
-                                           const unsigned char *nrec, int ubase, bf16x8 *slot, int l, int g)
+template <int NKB, int NVT, bool KR = true>
+__device__ __forceinline__ void state_step(ScanSetS<NKB, KR> &X, ScanSetS<NKB, KR> &Y, f32x4 (&S)[2 * NKB],
+                                           const unsigned char *nrec, int ubase, bf16x8 *slot, int l, int g,
+                                           const bf16x8 *kt_lds = nullptr)
 {
-    load_set<NKB, NVT>(Y, nrec, ubase, l, g);
+    load_set<NKB, NVT, KR>(Y, nrec, ubase, l, g);
     bf16x8 sb[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; kb++) {
@@ -121,10 +127,22 @@ __device__ __forceinline__ void state_step(ScanSetS<NKB> &X, ScanSetS<NKB> &Y, f
     bf16x8 db[2];
     db[0] = pack8(D[0], D[1]);
     db[1] = pack8(D[2], D[3]);
+    if constexpr (KR) {
 #pragma unroll
-    for (int jb = 0; jb < 2; jb++)
+        for (int jb = 0; jb < 2; jb++)
 #pragma unroll
-        for (int mt = 0; mt < 2 * NKB; mt++) S[mt] = mfma(X.K[mt * 2 + jb], db[jb], S[mt]);
+            for (int mt = 0; mt < 2 * NKB; mt++) S[mt] = mfma(X.K[mt * 2 + jb], db[jb], S[mt]);
+    } else {
+        /* K~^T from the chunk's LDS slot, 2 NKB fragments at a time */
+#pragma unroll
+        for (int jb = 0; jb < 2; jb++) {
+            bf16x8 kf[2 * NKB];
+#pragma unroll
+            for (int mt = 0; mt < 2 * NKB; mt++) kf[mt] = kt_lds[(mt * 2 + jb) * 64 + l];
+#pragma unroll
+            for (int mt = 0; mt < 2 * NKB; mt++) S[mt] = mfma(kf[mt], db[jb], S[mt]);
+        }
+    }
 }
 
 /* output wave: X holds chunk c (tokens t0 .. t0 + L - 1); loads chunk c + 1 into Y.
@@ -173,6 +191,13 @@ __device__ __forceinline__ void warm_l2(const unsigned char *p, uint32_t lds_add
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(lds_addr) : "memory", "m0");
 }
 
+/* padding of the LDS-ring warming loop (0-7 nops measured alike) */
+#ifndef KDA_WARM_NOPS
+#define KDA_WARM_NOPS 2
+#endif
+#define KDA_STR2(x) #x
+#define KDA_STR(x) KDA_STR2(x)
+
 /* chunks between the one a workgroup computes and the one its warming wave
    touches (long prefill scan: 2 or 3 -> 1.021 ms, 4 -> 1.038, 6 -> 1.106,
    8 -> 1.150) */
@@ -182,7 +207,7 @@ __device__ __forceinline__ void warm_l2(const unsigned char *p, uint32_t lds_add
    (record layout RecLayout<NKB, NVT>); SEG instantiates the segment-parallel
    rescan (one workgroup per (chain, segment, tile)), which the plain kernel
    compiles without */
-template <bool SEG, int NKB, int NVT>
+template <bool SEG, int NKB, int NVT, bool KLDS = false>
 __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
                                           const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H,
                                           int64_t nslots, uint16_t *__restrict__ out,
@@ -195,6 +220,8 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     static_assert((NVT & (NVT - 1)) == 0, "value tiles: a power of two");
     __shared__ bf16x8 ring[2][NKB * 64];                        /* S(c) in bf16 (8 KiB at DK = 128) */
     __shared__ __attribute__((aligned(16))) unsigned char warm_sink[1024];
+    /* KLDS: K~^T of chunk c in kring[c % 3], copied by the warming wave two chunks ahead */
+    __shared__ __attribute__((aligned(16))) bf16x8 kring[KLDS ? 3 : 1][KLDS ? 4 * NKB * 64 : 1];
     const int wave = threadIdx.x >> 6;
     const int l = threadIdx.x & 63, g = l >> 4, n16 = l & 15;
     /* the NVT value tiles of a chain run on one XCD (blockIdx % 8) and share its L2 */
@@ -273,18 +300,21 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
             }
         }
         if (nchunk > 0) {
-            ScanSetS<NKB> X, Y;
+            constexpr bool KR = !KLDS;
+            ScanSetS<NKB, KR> X, Y;
             int64_t c = 0;
             if (nchunk & 1) {
-                load_set<NKB, NVT>(X, rec_of(0), ubase, l, g);
-                state_step<NKB, NVT>(X, Y, S, rec_of(1), ubase, ring[0], l, g);
+                load_set<NKB, NVT, KR>(X, rec_of(0), ubase, l, g);
+                state_step<NKB, NVT, KR>(X, Y, S, rec_of(1), ubase, ring[0], l, g, kring[0]);
                 c = 1;
             } else {
-                load_set<NKB, NVT>(Y, rec_of(0), ubase, l, g);
+                load_set<NKB, NVT, KR>(Y, rec_of(0), ubase, l, g);
             }
             for (; c < nchunk; c += 2) {
-                state_step<NKB, NVT>(Y, X, S, rec_of(c + 1), ubase, ring[c & 1], l, g);
-                state_step<NKB, NVT>(X, Y, S, rec_of(c + 2), ubase, ring[(c + 1) & 1], l, g);
+                state_step<NKB, NVT, KR>(Y, X, S, rec_of(c + 1), ubase, ring[c & 1], l, g,
+                                         kring[KLDS ? c % 3 : 0]);
+                state_step<NKB, NVT, KR>(X, Y, S, rec_of(c + 2), ubase, ring[(c + 1) & 1], l, g,
+                                         kring[KLDS ? (c + 1) % 3 : 0]);
             }
         }
         if (fst) {
@@ -326,6 +356,44 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     } else {
         /* ---------------- L2-warming wave ---------------- */
         const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)warm_sink;
+        if constexpr (KLDS) {
+            /* Also copies K~^T of chunk c + 2 into kring[(c + 2) % 3] (LDS-DMA) after
+               barrier c, when the state wave is done with chunk c - 1's slot, and
+               waits for chunk c + 1's copy before barrier c + 1. Every trip issues
+               the same number of loads (chunk indices clamped to the last), so the
+               waits count exactly: 7 + 2 touches and 16 copies. */
+            constexpr int NTOUCH = 7 + 2;
+            static_assert(NVT == 8 && (RL::U / 1024 + 1 + 7) / 8 == 7, "touch count");
+            auto kt_copy = [&](int64_t cc) {
+                const int64_t ck = cc < nchunk ? cc : nchunk - 1;
+                const unsigned char *src = rec0 + (size_t)ck * RL::BYTES + RL::KT + l * 16;
+                const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16x8 *)kring[cc % 3];
+#pragma unroll
+                for (int i = 0; i < 4 * NKB; i++) warm_l2(src + i * 1024, dst + i * 1024);
+            };
+            if (nchunk == 0) return; /* no chunk: no barrier, nothing to copy */
+            kt_copy(0);
+            kt_copy(1);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NKB) : "memory"); /* chunk 0's copy has landed */
+            for (int64_t c = 0; c < nchunk; c++) {
+                asm volatile(".p2align 5\n\t.rept " KDA_STR(KDA_WARM_NOPS) "\n\ts_nop 0\n\t.endr");
+                chunk_barrier();
+                const int64_t cw = c + KDA_WARM_AHEAD < nchunk ? c + KDA_WARM_AHEAD : nchunk - 1;
+                const unsigned char *r = rec0 + (size_t)cw * RL::BYTES;
+#pragma unroll
+                for (int j = 0; j < 7; j++) {
+                    const int i = nt + 8 * j <= RL::U / 1024 ? nt + 8 * j : RL::U / 1024;
+                    warm_l2(r + i * 1024 + l * 16, lds);
+                }
+                warm_l2(r + RL::U + nt * 2048 + l * 16, lds);
+                warm_l2(r + RL::U + nt * 2048 + 1024 + l * 16, lds);
+                kt_copy(c + 2);
+                /* chunk c + 1's copy (issued before this trip's touches and copy) has landed */
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NTOUCH + 4 * NKB) : "memory");
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            return;
+        }
         for (int64_t c = 0; c < nchunk; c++) {
             /* Code placement: the chunk time of the whole workgroup was measured
                to depend on where this loop sits relative to 32-byte instruction
@@ -349,14 +417,21 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     }
 }
 
+/* K~^T through the warming wave's LDS ring in the plain 128-channel scan: the
+   state wave then issues 26 loads per chunk instead of 42, so two chunks of its
+   loads fit the 63 a wave can have outstanding (long prefill scan 1.063 ->
+   1.026 ms, and no longer sensitive to the warming loop's code placement) */
+#ifndef KDA_SCAN_KLDS
+#define KDA_SCAN_KLDS true
+#endif
 extern "C" __global__ void __launch_bounds__(192)
 kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
                 const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
                 uint16_t *__restrict__ out, const void *init_state,
                 void *final_state, int state_fp32, const int32_t *__restrict__ long_list)
 {
-    scan_body<false, 4, 8>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state, state_fp32,
-                           long_list, 1, 0, nullptr);
+    scan_body<false, 4, 8, KDA_SCAN_KLDS>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state,
+                                          state_fp32, long_list, 1, 0, nullptr);
 }
 
 /* K = V = 64: four value tiles per chain */
