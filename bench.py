@@ -49,8 +49,8 @@ SCAN_BYTES_PER_TH = scan_bytes_per_th()
 # only while the kernel's sources hash to the recorded value
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 CSRC = os.path.join(ROOT, "kimi_delta_attention_fwd_amd", "csrc")
-KERNEL_SOURCES = {"kda_prep": ("kda_prep.hip", "kda_device.h", "kda_internal.h", "../../include/kda.h"),
-                  "kda_scan": ("kda_scan.hip", "kda_scan_pair.hip", "kda_device.h", "kda_internal.h"),
+KERNEL_SOURCES = {"kda_prep": ("kda_prep.hip", "kda_device.h", "kda_internal.h", "../../include/kda.h", "../build.py"),
+                  "kda_scan": ("kda_scan.hip", "kda_scan_pair.hip", "kda_device.h", "kda_internal.h", "../build.py"),
                   "kda_decode": ("kda_decode.hip", "kda_device.h", "kda_internal.h"),
                   "kda_bwd_chunk": ("kda_bwd.hip", "kda_device.h", "kda_internal.h"),
                   "kda_bwd_scan": ("kda_bwd.hip", "kda_device.h", "kda_internal.h"),
