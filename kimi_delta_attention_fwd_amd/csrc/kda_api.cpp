@@ -24,7 +24,10 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
                                       const void *beta, const float *A_log, const float *dt_bias,
                                       float scale, float lower_bound, const int32_t *cu,
                                       const int32_t *chunk_off, int64_t nseq, int64_t T, int64_t H,
-                                      int64_t nslots, int64_t K, int64_t V, void *records, hipStream_t st);
+                                      int64_t nslots, int64_t K, int64_t V, void *records, int64_t trim_max,
+                                      hipStream_t st);
+extern "C" int64_t kda_scan_many_max_chunks(const int32_t *cu, int64_t nseq, int64_t H, int64_t K, int64_t V,
+                                            int64_t segc);
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
                                       int64_t nseq, int64_t T, int64_t H, int64_t nslots, int64_t K, int64_t V,
                                       void *out, const void *init_state, void *final_state, int state_fp32,
@@ -250,15 +253,16 @@ static int fwd_run(const void *q, const void *k, const void *v, const void *g, c
     }
     void *records = ws + kda_chunk_map_bytes(nseq_arg, T);
     const int64_t nslots = kda_max_chunks(B, T, nseq_arg);
+    /* the segment-parallel scan (few long chains) exists for K = V = 128 only */
+    const int64_t segc = (K == KDA_DK && V == KDA_DV) ? kda_seg_len(B, T, H, nseq_arg) : 0;
     {
         ProfScope ps("kda_prep", st);
         if (kda_launch_prep(q, k, v, g, beta, A_log, dt_bias, scale, lower_bound, cu_seqlens, chunk_off,
-                            N, T, H, nslots, K, V, records, st) != hipSuccess)
+                            N, T, H, nslots, K, V, records,
+                            kda_scan_many_max_chunks(cu_seqlens, N, H, K, V, segc), st) != hipSuccess)
             return KDA_ERR_HIP;
     }
     {
-        /* the segment-parallel scan (few long chains) exists for K = V = 128 only */
-        const int64_t segc = (K == KDA_DK && V == KDA_DV) ? kda_seg_len(B, T, H, nseq_arg) : 0;
         ProfScope ps("kda_scan", st);
         if (kda_launch_scan(records, cu_seqlens, chunk_off, N, T, H, nslots, K, V, out,
                             state_dtype == KDA_STATE_NONE ? nullptr : initial_state, final_state,

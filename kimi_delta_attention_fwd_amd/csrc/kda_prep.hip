@@ -142,7 +142,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
                                           const float *__restrict__ dt_bias, float scale, float lower_bound,
                                           const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
                                           int64_t nseq, int64_t T, int H, int64_t nslots,
-                                          unsigned char *__restrict__ rec_base)
+                                          unsigned char *__restrict__ rec_base, int64_t trim_max)
 {
     constexpr int DK = 32 * NKB, DV = 32 * NVB, NE = 8 * NKB; /* NE: key channels per lane */
     using RL = RecLayout<NKB, 2 * NVB>;
@@ -158,6 +158,21 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6); /* wave-uniform: branches on it are scalar */
     const int r = 16 * w + r16;
     const bool valid = r < L;
+    /* A partial chunk of a sequence of at most trim_max chunks is scanned by
+       the many-chain kernel, which reads the fragments of token tiles past the
+       chunk's tokens as zeros without touching memory. Those fragments are
+       left unwritten: W, Q' and P of row tile w >= nmt (skip_row), and, when
+       L <= 32, K~^T token block 1 and U token tiles 2, 3 (skip_hi). Both
+       flags are wave-uniform. */
+    bool skip_row = false, skip_hi = false;
+    if (L < KDA_CHUNK) {
+        const int64_t len = cu == nullptr ? T : (int64_t)cu[seq + 1] - cu[seq];
+        if ((len + KDA_CHUNK - 1) / KDA_CHUNK <= trim_max) {
+            const int nmt = (L + 15) >> 4;
+            skip_row = w >= nmt;
+            skip_hi = w >= 2 && nmt <= 2;
+        }
+    }
 
     /* ---- phase A: load this lane's token row, norms, gate, cumsum ---- */
     /* Token rows past the chunk end fall outside the descriptors' ranges and load
@@ -324,9 +339,10 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
             if (kb < NVB)
                 store_transposed(vfr[kb], sel, (uint16_t *)&sh.vt[2 * kb][jb][l] + 4 * jh,
                                  (uint16_t *)&sh.vt[2 * kb + 1][jb][l] + 4 * jh);
-            store_transposed(kt, sel,
-                             (uint16_t *)(rec + RL::KT + ((size_t)((2 * kb) * 2 + jb) * 64 + l) * 16 + jh * 8),
-                             (uint16_t *)(rec + RL::KT + ((size_t)((2 * kb + 1) * 2 + jb) * 64 + l) * 16 + jh * 8));
+            if (!skip_hi)
+                store_transposed(kt, sel,
+                                 (uint16_t *)(rec + RL::KT + ((size_t)((2 * kb) * 2 + jb) * 64 + l) * 16 + jh * 8),
+                                 (uint16_t *)(rec + RL::KT + ((size_t)((2 * kb + 1) * 2 + jb) * 64 + l) * 16 + jh * 8));
         }
 #pragma unroll
         for (int vb = NKB; vb < NVB; vb++) /* value tiles past the key tiles (DV > DK) */
@@ -419,7 +435,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     bf16x8 pf[2];
     pf[0] = pack8(pt[0], pt[1]);
     pf[1] = pack8(pt[2], pt[3]);
-    {
+    if (!skip_row) {
         bf16x8 *pdst = (bf16x8 *)(rec + RL::P);
         if (w < 2) {
             pdst[KDA_PIDX(w, 0) * 64 + l] = pf[0];
@@ -516,6 +532,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     /* W (stored negated), lane = token, regs = key channel */
 #pragma unroll
     for (int kb = 0; kb < NKB; kb++) {
+        if (skip_row) break;
         f32x4 d0 = zero4(), d1 = zero4();
 #pragma unroll
         for (int jb = 0; jb < 2; jb++)
@@ -528,6 +545,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
     /* U, lane = value column, regs = token */
 #pragma unroll
     for (int nt = 0; nt < 2 * NVB; nt++) {
+        if (skip_hi) break;
         f32x4 d = zero4();
 #pragma unroll
         for (int jb = 0; jb < 2; jb++)
@@ -537,6 +555,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
         u.y = pack_bf16x2(d[2], d[3]);
         *(uint2 *)(rec + RL::U + ((size_t)(nt * 64 + l) * 16 + w * 4) * 2) = u;
     }
+    if (skip_row) return;
     /* P TB, lane = token r, regs = j' */
     f32x4 ptt[4];
 #pragma unroll
@@ -573,10 +592,10 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
         name(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *gt, const uint16_t *beta,     \
              const float *__restrict__ A_log, const float *__restrict__ dt_bias, float scale, float lower_bound,     \
              const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H,  \
-             int64_t nslots, unsigned char *__restrict__ rec_base)                                                 \
+             int64_t nslots, unsigned char *__restrict__ rec_base, int64_t trim_max)                              \
     {                                                                                                               \
         prep_body<WIDE, NKB, NVB>(q, k, v, gt, beta, A_log, dt_bias, scale, lower_bound, cu, chunk_off, nseq, T, H, \
-                                  nslots, rec_base);                                                                \
+                                  nslots, rec_base, trim_max);                                                      \
     }
 
 /* K = V = 128; the wide form below lower_bound KDA_LOWER_BOUND_NARROW */
@@ -600,7 +619,8 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
                                       const void *beta, const float *A_log, const float *dt_bias,
                                       float scale, float lower_bound, const int32_t *cu,
                                       const int32_t *chunk_off, int64_t nseq, int64_t T, int64_t H,
-                                      int64_t nslots, int64_t K, int64_t V, void *records, hipStream_t st)
+                                      int64_t nslots, int64_t K, int64_t V, void *records, int64_t trim_max,
+                                      hipStream_t st)
 {
     const int64_t blocks = nslots * H;
     const bool wide = lower_bound < KDA_LOWER_BOUND_NARROW;
@@ -611,7 +631,7 @@ extern "C" hipError_t kda_launch_prep(const void *q, const void *k, const void *
                        dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v,
                        (const uint16_t *)g, (const uint16_t *)beta, A_log, dt_bias, scale,
-                       lower_bound, cu, chunk_off, nseq, T, (int)H, nslots, (unsigned char *)records);
+                       lower_bound, cu, chunk_off, nseq, T, (int)H, nslots, (unsigned char *)records, trim_max);
     return hipGetLastError();
 }
 

@@ -744,17 +744,43 @@ __device__ __forceinline__ void scan_many_body(const unsigned char *rec_base, co
         const int64_t t0 = bos + c * KDA_CHUNK;
         const int64_t rem = eos - t0;
         const int L = (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
+        /* In a partial last chunk, the fragments of token tiles past its L tokens
+           hold only the zeros of the prep's padded rows: W, Q' row tiles mt >=
+           nmt, K~^T token blocks jb >= njb, P row tiles mt >= nmt, U rows >= 32
+           when L <= 32. They are read through a descriptor of empty range, which
+           loads the same zeros without a memory request. Piece p of the fill
+           lies in fragment p / 64 = i NVT + nt, so the choice is wave-uniform. */
+        const __amdgpu_buffer_rsrc_t rz = buf_rsrc(rec0, 0);
         /* this chunk's shared operands: loads issued before the barrier that
            frees the LDS copy of the previous chunk, stores after it */
         u32x4 stage[FILL_ITERS];
-#pragma unroll
-        for (int i = 0; i < FILL_ITERS; i++) {
+        /* lanes past the last piece read outside the record's range (zeros, no
+           branch around the load); their LDS stores below are skipped */
+        auto piece_off = [&](int i) {
             const int p = i * NTH + tid;
-            stage[i] = p < PIECES ? __builtin_amdgcn_raw_buffer_load_b128(r, p * 16, 0, 0) : u32x4{0, 0, 0, 0};
+            return (i + 1) * NTH <= PIECES || p < PIECES ? p * 16 : RL::BYTES;
+        };
+        if (L == KDA_CHUNK) {
+#pragma unroll
+            for (int i = 0; i < FILL_ITERS; i++) stage[i] = __builtin_amdgcn_raw_buffer_load_b128(r, piece_off(i), 0, 0);
+        } else {
+            const int nmt = (L + 15) >> 4, njb = (L + 31) >> 5;
+            const int lim_p = nmt <= 2 ? nmt : 2 * nmt - 2;
+            static_assert(3 * RL::NFR + 6 < 64 && (PIECES + 63) / 64 <= 64, "fragment mask");
+            const uint64_t nfr_bits = (1ull << RL::NFR) - 1;
+            const uint64_t wq = (1ull << (nmt * NKB)) - 1; /* W, Q': index mt NKB + kb */
+            const uint64_t kt = njb == 2 ? nfr_bits : nfr_bits & 0x5555555555555555ull; /* ct 2 + jb */
+            const uint64_t need = wq | wq << RL::NFR | kt << (2 * RL::NFR) |
+                                  ((1ull << lim_p) - 1) << (3 * RL::NFR) | ~0ull << (3 * RL::NFR + 6);
+#pragma unroll
+            for (int i = 0; i < FILL_ITERS; i++) {
+                const uint32_t f = __builtin_amdgcn_readfirstlane(i * NVT + nt); /* = piece / 64 */
+                stage[i] = __builtin_amdgcn_raw_buffer_load_b128((need >> f) & 1 ? r : rz, piece_off(i), 0, 0);
+            }
         }
         bf16x8 U[2];
         U[0] = bufld(r, l * 32, ubase);
-        U[1] = bufld(r, l * 32, ubase + 16);
+        U[1] = bufld(L > 32 ? r : rz, l * 32, ubase + 16);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < FILL_ITERS; i++) {
@@ -909,6 +935,19 @@ extern "C" hipError_t kda_launch_scan_pair(const void *records, const int32_t *c
                                            const void *init_state, void *final_state, int state_fp32,
                                            int64_t max_chains, const int32_t *long_list, hipStream_t st);
 
+/* The longest sequence, in chunks, that kda_launch_scan gives to the many-chain
+   kernel for these sizes (0: that kernel does not run). The chunk preparation
+   leaves the padded fragments of those sequences' partial chunks unwritten,
+   since that kernel reads them as zeros without touching memory. */
+extern "C" int64_t kda_scan_many_max_chunks(const int32_t *cu, int64_t nseq, int64_t H, int64_t K, int64_t V,
+                                            int64_t segc)
+{
+    if (nseq * H < KDA_MANY_CHAINS) return 0;
+    if (K == 64 && V == 64) return INT64_MAX;
+    if (segc > 0) return 0;
+    return cu == nullptr ? INT64_MAX : (int64_t)KDA_MANY_MAX_CHUNKS;
+}
+
 extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, const int32_t *chunk_off,
                                       int64_t nseq, int64_t T, int64_t H, int64_t nslots, int64_t K, int64_t V,
                                       void *out, const void *init_state, void *final_state, int state_fp32,
@@ -957,7 +996,7 @@ extern "C" hipError_t kda_launch_scan(const void *records, const int32_t *cu, co
                            (const int32_t *)nullptr);
         return hipGetLastError();
     }
-    const int64_t max_chunks = cu == nullptr ? INT64_MAX : (int64_t)KDA_MANY_MAX_CHUNKS;
+    const int64_t max_chunks = kda_scan_many_max_chunks(cu, nseq, H, K, V, segc);
     hipLaunchKernelGGL(kda_scan_many_kernel, dim3((unsigned)nchain), dim3(512), 0, st, rec, cu, chunk_off, nseq, T,
                        (int)H, nslots, (uint16_t *)out, init_state, final_state, state_fp32, max_chunks);
     const hipError_t e = hipGetLastError();
