@@ -44,7 +44,7 @@
    the register set (else the state wave reads it from an LDS ring) */
 template <int NKB, bool KR = true> struct ScanSetS {
     bf16x8 W[4 * NKB], K[KR ? 4 * NKB : 1], U[2];
-    f32x4 gl[2 * NKB]; /* e^{G_L} for key rows 16 mt + 4 g + e */
+    f32x4 gl[KR ? 2 * NKB : 1]; /* e^{G_L} for key rows 16 mt + 4 g + e (else from the LDS ring) */
 };
 template <int NKB> struct ScanSetO {
     bf16x8 Q[4 * NKB], P[6], U[2];
@@ -66,10 +66,11 @@ __device__ __forceinline__ void load_set(ScanSetS<NKB, KR> &X, const unsigned ch
     for (int f = 0; f < 4 * NKB; f++) X.W[f] = bufld(r, l * 16, RL::W + f * 1024);
     X.U[0] = bufld(r, l * 32, ubase);
     X.U[1] = bufld(r, l * 32, ubase + 16);
-#pragma unroll
-    for (int mt = 0; mt < 2 * NKB; mt++)
-        X.gl[mt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, g * 16, RL::GL + mt * 64, 0));
     if constexpr (KR) {
+#pragma unroll
+        for (int mt = 0; mt < 2 * NKB; mt++)
+            X.gl[mt] =
+                __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, g * 16, RL::GL + mt * 64, 0));
 #pragma unroll
         for (int f = 0; f < 4 * NKB; f++) X.K[f] = bufld(r, l * 16, RL::KT + f * 1024);
     }
@@ -121,9 +122,12 @@ __device__ __forceinline__ void state_step(ScanSetS<NKB, KR> &X, ScanSetS<NKB, K
     for (int kb = 0; kb < NKB; kb++)
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) D[mt] = mfma(X.W[mt * NKB + kb], sb[kb], D[mt]);
-    /* S <- diag(e^{G_L}) S + K~^T D */
+    /* S <- diag(e^{G_L}) S + K~^T D (e^{G_L} after K~^T in the LDS slot, key-channel order) */
 #pragma unroll
-    for (int mt = 0; mt < 2 * NKB; mt++) S[mt] *= X.gl[mt];
+    for (int mt = 0; mt < 2 * NKB; mt++) {
+        if constexpr (KR) S[mt] *= X.gl[mt];
+        else S[mt] *= ((const f32x4 *)(kt_lds + 4 * NKB * 64))[4 * mt + g];
+    }
     bf16x8 db[2];
     db[0] = pack8(D[0], D[1]);
     db[1] = pack8(D[2], D[3]);
@@ -220,8 +224,9 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     static_assert((NVT & (NVT - 1)) == 0, "value tiles: a power of two");
     __shared__ bf16x8 ring[2][NKB * 64];                        /* S(c) in bf16 (8 KiB at DK = 128) */
     __shared__ __attribute__((aligned(16))) unsigned char warm_sink[1024];
-    /* KLDS: K~^T of chunk c in kring[c % 3], copied by the warming wave two chunks ahead */
-    __shared__ __attribute__((aligned(16))) bf16x8 kring[KLDS ? 3 : 1][KLDS ? 4 * NKB * 64 : 1];
+    /* KLDS: K~^T of chunk c, then 1 KiB from e^{G_L} on, in kring[c % 3], copied by
+       the warming wave two chunks ahead */
+    __shared__ __attribute__((aligned(16))) bf16x8 kring[KLDS ? 3 : 1][KLDS ? 4 * NKB * 64 + 64 : 1];
     const int wave = threadIdx.x >> 6;
     const int l = threadIdx.x & 63, g = l >> 4, n16 = l & 15;
     /* the NVT value tiles of a chain run on one XCD (blockIdx % 8) and share its L2 */
@@ -357,12 +362,13 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
         /* ---------------- L2-warming wave ---------------- */
         const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)warm_sink;
         if constexpr (KLDS) {
-            /* Also copies K~^T of chunk c + 2 into kring[(c + 2) % 3] (LDS-DMA) after
-               barrier c, when the state wave is done with chunk c - 1's slot, and
-               waits for chunk c + 1's copy before barrier c + 1. Every trip issues
-               the same number of loads (chunk indices clamped to the last), so the
-               waits count exactly: 7 + 2 touches and 16 copies. */
-            constexpr int NTOUCH = 7 + 2;
+            /* Also copies K~^T and e^{G_L} of chunk c + 2 into kring[(c + 2) % 3]
+               (LDS-DMA) after barrier c, when the state wave is done with chunk
+               c - 1's slot, and waits for chunk c + 1's copy before barrier c + 1.
+               Every trip issues the same number of loads (chunk indices clamped to
+               the last), so the waits count exactly: 7 + 2 touches and 16 + 1
+               copies. */
+            constexpr int NTOUCH = 7 + 2, NCOPY = 4 * NKB + 1;
             static_assert(NVT == 8 && (RL::U / 1024 + 1 + 7) / 8 == 7, "touch count");
             auto kt_copy = [&](int64_t cc) {
                 const int64_t ck = cc < nchunk ? cc : nchunk - 1;
@@ -370,11 +376,12 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
                 const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16x8 *)kring[cc % 3];
 #pragma unroll
                 for (int i = 0; i < 4 * NKB; i++) warm_l2(src + i * 1024, dst + i * 1024);
+                warm_l2(src - RL::KT + RL::GL, dst + 4 * NKB * 1024); /* e^{G_L} and 512 bytes after it */
             };
             if (nchunk == 0) return; /* no chunk: no barrier, nothing to copy */
             kt_copy(0);
             kt_copy(1);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NKB) : "memory"); /* chunk 0's copy has landed */
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY) : "memory"); /* chunk 0's copy has landed */
             for (int64_t c = 0; c < nchunk; c++) {
                 asm volatile(".p2align 5\n\t.rept " KDA_STR(KDA_WARM_NOPS) "\n\ts_nop 0\n\t.endr");
                 chunk_barrier();
@@ -389,7 +396,7 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
                 warm_l2(r + RL::U + nt * 2048 + 1024 + l * 16, lds);
                 kt_copy(c + 2);
                 /* chunk c + 1's copy (issued before this trip's touches and copy) has landed */
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NTOUCH + 4 * NKB) : "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NTOUCH + NCOPY) : "memory");
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             return;
@@ -417,10 +424,12 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     }
 }
 
-/* K~^T through the warming wave's LDS ring in the plain 128-channel scan: the
-   state wave then issues 26 loads per chunk instead of 42, so two chunks of its
-   loads fit the 63 a wave can have outstanding (long prefill scan 1.063 ->
-   1.026 ms, and no longer sensitive to the warming loop's code placement) */
+/* K~^T and e^{G_L} through the warming wave's LDS ring in the plain 128-channel
+   scan: the state wave then issues 18 loads per chunk instead of 42, so two
+   chunks of its loads fit the 63 a wave can have outstanding, and the kernel
+   needs 292 registers (338 with e^{G_L} in registers) (long prefill scan 1.063
+   -> 1.026 ms with K~^T alone, and no longer sensitive to the warming loop's
+   code placement; 1.004 ms with e^{G_L} too) */
 #ifndef KDA_SCAN_KLDS
 #define KDA_SCAN_KLDS true
 #endif

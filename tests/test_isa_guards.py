@@ -50,7 +50,8 @@ def test_m0_only_set_for_lds_dma(name, tmp_path):
     for i, t in enumerate(ins):
         if not re.search(r"\bm0\b", t):
             continue
-        assert re.match(r"^s_mov_b32 m0, s\d+$", t), "compiler-generated use of m0: %r" % t
+        # the asm's SGPR operand: any SGPR, vcc_lo / vcc_hi included
+        assert re.match(r"^s_mov_b32 m0, (s\d+|vcc_lo|vcc_hi)$", t), "compiler-generated use of m0: %r" % t
         assert i + 1 < len(ins) and LDS_DMA.match(ins[i + 1]), "m0 set without its LDS-DMA load: %r" % t
         n_dma += 1
     assert n_dma > 0, "no LDS-DMA sequence found; the guard is checking the wrong file"
