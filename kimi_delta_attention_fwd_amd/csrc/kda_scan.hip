@@ -43,12 +43,17 @@
 /* NKB = DK / 32 key blocks (W, Q', K~^T hold 4 NKB fragments each); KR: K~^T in
    the register set (else the state wave reads it from an LDS ring) */
 template <int NKB, bool KR = true> struct ScanSetS {
-    bf16x8 W[4 * NKB], K[KR ? 4 * NKB : 1], U[2];
-    f32x4 gl[KR ? 2 * NKB : 1]; /* e^{G_L} for key rows 16 mt + 4 g + e (else from the LDS ring) */
+    bf16x8 W[4 * NKB], K[KR ? 4 * NKB : 1], U[KR ? 2 : 1];
+    f32x4 gl[KR ? 2 * NKB : 1]; /* e^{G_L} for key rows 16 mt + 4 g + e */
 };
-template <int NKB> struct ScanSetO {
-    bf16x8 Q[4 * NKB], P[6], U[2];
+/* UR: U in the register set (else read from the LDS ring) */
+template <int NKB, bool UR = true> struct ScanSetO {
+    bf16x8 Q[4 * NKB], P[6], U[UR ? 2 : 1];
 };
+/* KR = false: the chunk's LDS ring slot holds K~^T (4 NKB fragments), then 1 KiB
+   from e^{G_L} on, then this tile's 2 KiB of U (lane l's 32 bytes at 32 l) */
+template <int NKB> __device__ __forceinline__ const bf16x8 *slot_gl(const bf16x8 *slot) { return slot + 4 * NKB * 64; }
+template <int NKB> __device__ __forceinline__ const bf16x8 *slot_u(const bf16x8 *slot) { return slot + 4 * NKB * 64 + 64; }
 
 __device__ __forceinline__ bf16x8 bufld(__amdgpu_buffer_rsrc_t r, int voff, int soff)
 {
@@ -64,9 +69,9 @@ __device__ __forceinline__ void load_set(ScanSetS<NKB, KR> &X, const unsigned ch
     const __amdgpu_buffer_rsrc_t r = buf_rsrc(rec, RL::BYTES);
 #pragma unroll
     for (int f = 0; f < 4 * NKB; f++) X.W[f] = bufld(r, l * 16, RL::W + f * 1024);
-    X.U[0] = bufld(r, l * 32, ubase);
-    X.U[1] = bufld(r, l * 32, ubase + 16);
     if constexpr (KR) {
+        X.U[0] = bufld(r, l * 32, ubase);
+        X.U[1] = bufld(r, l * 32, ubase + 16);
 #pragma unroll
         for (int mt = 0; mt < 2 * NKB; mt++)
             X.gl[mt] =
@@ -76,8 +81,8 @@ __device__ __forceinline__ void load_set(ScanSetS<NKB, KR> &X, const unsigned ch
     }
 }
 
-template <int NKB, int NVT>
-__device__ __forceinline__ void load_set(ScanSetO<NKB> &X, const unsigned char *rec, int ubase, int l, int g)
+template <int NKB, int NVT, bool UR>
+__device__ __forceinline__ void load_set(ScanSetO<NKB, UR> &X, const unsigned char *rec, int ubase, int l, int g)
 {
     using RL = RecLayout<NKB, NVT>;
     const __amdgpu_buffer_rsrc_t r = buf_rsrc(rec, RL::BYTES);
@@ -85,8 +90,10 @@ __device__ __forceinline__ void load_set(ScanSetO<NKB> &X, const unsigned char *
     for (int f = 0; f < 4 * NKB; f++) X.Q[f] = bufld(r, l * 16, RL::Q + f * 1024);
 #pragma unroll
     for (int f = 0; f < 6; f++) X.P[f] = bufld(r, l * 16, RL::P + f * 1024);
-    X.U[0] = bufld(r, l * 32, ubase);
-    X.U[1] = bufld(r, l * 32, ubase + 16);
+    if constexpr (UR) {
+        X.U[0] = bufld(r, l * 32, ubase);
+        X.U[1] = bufld(r, l * 32, ubase + 16);
+    }
 }
 
 __device__ __forceinline__ void chunk_barrier()
@@ -111,10 +118,16 @@ __device__ __forceinline__ void state_step(ScanSetS<NKB, KR> &X, ScanSetS<NKB, K
     }
     chunk_barrier();
     f32x4 D[4];
+    bf16x8 uu[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; jb++) {
+        if constexpr (KR) uu[jb] = X.U[jb];
+        else uu[jb] = slot_u<NKB>(kt_lds)[2 * l + jb];
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
         const int o = (mt & 1) * 4;
-        const bf16x8 &u = X.U[mt >> 1];
+        const bf16x8 &u = uu[mt >> 1];
         D[mt] = f32x4{(float)u[o], (float)u[o + 1], (float)u[o + 2], (float)u[o + 3]};
     }
     /* D = U - W S */
@@ -126,7 +139,7 @@ __device__ __forceinline__ void state_step(ScanSetS<NKB, KR> &X, ScanSetS<NKB, K
 #pragma unroll
     for (int mt = 0; mt < 2 * NKB; mt++) {
         if constexpr (KR) S[mt] *= X.gl[mt];
-        else S[mt] *= ((const f32x4 *)(kt_lds + 4 * NKB * 64))[4 * mt + g];
+        else S[mt] *= ((const f32x4 *)slot_gl<NKB>(kt_lds))[4 * mt + g];
     }
     bf16x8 db[2];
     db[0] = pack8(D[0], D[1]);
@@ -152,10 +165,11 @@ __device__ __forceinline__ void state_step(ScanSetS<NKB, KR> &X, ScanSetS<NKB, K
 /* output wave: X holds chunk c (tokens t0 .. t0 + L - 1); loads chunk c + 1 into Y.
    out is written through a buffer descriptor bounded at row L - 1: rows past
    the sequence end fall outside it and the hardware drops their stores. */
-template <int NKB, int NVT>
-__device__ __forceinline__ void output_step(ScanSetO<NKB> &X, ScanSetO<NKB> &Y, const unsigned char *nrec,
+template <int NKB, int NVT, bool UR = true>
+__device__ __forceinline__ void output_step(ScanSetO<NKB, UR> &X, ScanSetO<NKB, UR> &Y, const unsigned char *nrec,
                                             int ubase, const bf16x8 *slot, uint16_t *out, int64_t t0, int L,
-                                            int H, int h, int nt, int l, int g, int n16)
+                                            int H, int h, int nt, int l, int g, int n16,
+                                            const bf16x8 *kslot = nullptr)
 {
     constexpr int DV = 16 * NVT;
     load_set<NKB, NVT>(Y, nrec, ubase, l, g);
@@ -171,10 +185,16 @@ __device__ __forceinline__ void output_step(ScanSetO<NKB> &X, ScanSetO<NKB> &Y, 
     for (int kb = 0; kb < NKB; kb++)
 #pragma unroll
         for (int mt = 0; mt < 4; mt++) O[mt] = mfma(sb[kb], X.Q[mt * NKB + kb], O[mt]);
+    bf16x8 uu[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; jb++) {
+        if constexpr (UR) uu[jb] = X.U[jb];
+        else uu[jb] = slot_u<NKB>(kslot)[2 * l + jb];
+    }
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-        for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(X.U[jb], X.P[KDA_PIDX(mt, jb)], O[mt]);
+        for (int jb = 0; jb <= (mt >> 1); jb++) O[mt] = mfma(uu[jb], X.P[KDA_PIDX(mt, jb)], O[mt]);
     const int row_bytes = H * DV * 2;
     const __amdgpu_buffer_rsrc_t ro =
         buf_rsrc(out + ((size_t)t0 * H + h) * DV, (uint32_t)((L - 1) * row_bytes + DV * 2));
@@ -224,9 +244,9 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     static_assert((NVT & (NVT - 1)) == 0, "value tiles: a power of two");
     __shared__ bf16x8 ring[2][NKB * 64];                        /* S(c) in bf16 (8 KiB at DK = 128) */
     __shared__ __attribute__((aligned(16))) unsigned char warm_sink[1024];
-    /* KLDS: K~^T of chunk c, then 1 KiB from e^{G_L} on, in kring[c % 3], copied by
-       the warming wave two chunks ahead */
-    __shared__ __attribute__((aligned(16))) bf16x8 kring[KLDS ? 3 : 1][KLDS ? 4 * NKB * 64 + 64 : 1];
+    /* KLDS: K~^T of chunk c, 1 KiB from e^{G_L} on and this tile's U in kring[c % 3]
+       (slot_gl, slot_u), copied by the warming wave two chunks ahead */
+    __shared__ __attribute__((aligned(16))) bf16x8 kring[KLDS ? 3 : 1][KLDS ? 4 * NKB * 64 + 64 + 128 : 1];
     const int wave = threadIdx.x >> 6;
     const int l = threadIdx.x & 63, g = l >> 4, n16 = l & 15;
     /* the NVT value tiles of a chain run on one XCD (blockIdx % 8) and share its L2 */
@@ -336,7 +356,7 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     } else if (wave == 1) {
         /* ---------------- output wave ---------------- */
         if (nchunk > 0) {
-            ScanSetO<NKB> X, Y;
+            ScanSetO<NKB, !KLDS> X, Y;
             int64_t c = 0;
             auto t0_of = [&](int64_t cc) { return bos + cc * KDA_CHUNK; };
             auto len_of = [&](int64_t cc) {
@@ -346,29 +366,30 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
             if (nchunk & 1) {
                 load_set<NKB, NVT>(X, rec_of(0), ubase, l, g);
                 output_step<NKB, NVT>(X, Y, rec_of(1), ubase, ring[0], out, t0_of(0), len_of(0), H, h, nt, l, g,
-                                      n16);
+                                      n16, kring[0]);
                 c = 1;
             } else {
                 load_set<NKB, NVT>(Y, rec_of(0), ubase, l, g);
             }
             for (; c < nchunk; c += 2) {
                 output_step<NKB, NVT>(Y, X, rec_of(c + 1), ubase, ring[c & 1], out, t0_of(c), len_of(c), H, h, nt,
-                                      l, g, n16);
+                                      l, g, n16, kring[KLDS ? c % 3 : 0]);
                 output_step<NKB, NVT>(X, Y, rec_of(c + 2), ubase, ring[(c + 1) & 1], out, t0_of(c + 1),
-                                      len_of(c + 1), H, h, nt, l, g, n16);
+                                      len_of(c + 1), H, h, nt, l, g, n16, kring[KLDS ? (c + 1) % 3 : 0]);
             }
         }
     } else {
         /* ---------------- L2-warming wave ---------------- */
         const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)warm_sink;
         if constexpr (KLDS) {
-            /* Also copies K~^T and e^{G_L} of chunk c + 2 into kring[(c + 2) % 3]
+            /* Also copies K~^T, e^{G_L} and U of chunk c + 2 into kring[(c + 2) % 3]
                (LDS-DMA) after barrier c, when the state wave is done with chunk
                c - 1's slot, and waits for chunk c + 1's copy before barrier c + 1.
                Every trip issues the same number of loads (chunk indices clamped to
-               the last), so the waits count exactly: 7 + 2 touches and 16 + 1
-               copies. */
-            constexpr int NTOUCH = 7 + 2, NCOPY = 4 * NKB + 1;
+               the last), so the waits count exactly: 7 + 2 touches and 16 + 1 + 2
+               copies. The output wave reads U from the same slot, between the same
+               barriers as the state wave. */
+            constexpr int NTOUCH = 7 + 2, NCOPY = 4 * NKB + 3;
             static_assert(NVT == 8 && (RL::U / 1024 + 1 + 7) / 8 == 7, "touch count");
             auto kt_copy = [&](int64_t cc) {
                 const int64_t ck = cc < nchunk ? cc : nchunk - 1;
@@ -377,6 +398,8 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
 #pragma unroll
                 for (int i = 0; i < 4 * NKB; i++) warm_l2(src + i * 1024, dst + i * 1024);
                 warm_l2(src - RL::KT + RL::GL, dst + 4 * NKB * 1024); /* e^{G_L} and 512 bytes after it */
+                warm_l2(src - RL::KT + ubase, dst + (4 * NKB + 1) * 1024); /* this tile's U */
+                warm_l2(src - RL::KT + ubase + 1024, dst + (4 * NKB + 2) * 1024);
             };
             if (nchunk == 0) return; /* no chunk: no barrier, nothing to copy */
             kt_copy(0);
@@ -424,12 +447,12 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     }
 }
 
-/* K~^T and e^{G_L} through the warming wave's LDS ring in the plain 128-channel
-   scan: the state wave then issues 18 loads per chunk instead of 42, so two
-   chunks of its loads fit the 63 a wave can have outstanding, and the kernel
-   needs 292 registers (338 with e^{G_L} in registers) (long prefill scan 1.063
-   -> 1.026 ms with K~^T alone, and no longer sensitive to the warming loop's
-   code placement; 1.004 ms with e^{G_L} too) */
+/* K~^T, e^{G_L} and U through the warming wave's LDS ring in the plain
+   128-channel scan: the state wave then issues 16 loads per chunk instead of 42,
+   so two chunks of its loads fit the 63 a wave can have outstanding, and the
+   kernel needs 280 registers (338 with e^{G_L} and U in registers). Long
+   prefill scan 1.063 -> 1.026 ms with K~^T alone (and no longer sensitive to
+   the warming loop's code placement), 1.004 ms with e^{G_L}, 0.990 ms with U. */
 #ifndef KDA_SCAN_KLDS
 #define KDA_SCAN_KLDS true
 #endif
