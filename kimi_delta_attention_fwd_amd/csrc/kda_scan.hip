@@ -227,6 +227,13 @@ __device__ __forceinline__ void warm_l2(const unsigned char *p, uint32_t lds_add
    8 -> 1.150) */
 #define KDA_WARM_AHEAD 3
 
+/* chunks between the one the state wave computes and the one whose ring slot the
+   warming wave fills (the ring has KDA_KRING_AHEAD + 1 slots) */
+#ifndef KDA_KRING_AHEAD
+#define KDA_KRING_AHEAD 3
+#endif
+#define KDA_KRING_SLOTS (KDA_KRING_AHEAD + 1)
+
 /* the scan body over DK = 32 NKB key channels and NVT value tiles of 16 columns
    (record layout RecLayout<NKB, NVT>); SEG instantiates the segment-parallel
    rescan (one workgroup per (chain, segment, tile)), which the plain kernel
@@ -244,9 +251,11 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     static_assert((NVT & (NVT - 1)) == 0, "value tiles: a power of two");
     __shared__ bf16x8 ring[2][NKB * 64];                        /* S(c) in bf16 (8 KiB at DK = 128) */
     __shared__ __attribute__((aligned(16))) unsigned char warm_sink[1024];
-    /* KLDS: K~^T of chunk c, 1 KiB from e^{G_L} on and this tile's U in kring[c % 3]
-       (slot_gl, slot_u), copied by the warming wave two chunks ahead */
-    __shared__ __attribute__((aligned(16))) bf16x8 kring[KLDS ? 3 : 1][KLDS ? 4 * NKB * 64 + 64 + 128 : 1];
+    /* KLDS: K~^T of chunk c, 1 KiB from e^{G_L} on and this tile's U in
+       kring[c % KDA_KRING_SLOTS] (slot_gl, slot_u), copied by the warming wave
+       KDA_KRING_AHEAD chunks ahead */
+    __shared__ __attribute__((aligned(16)))
+    bf16x8 kring[KLDS ? KDA_KRING_SLOTS : 1][KLDS ? 4 * NKB * 64 + 64 + 128 : 1];
     const int wave = threadIdx.x >> 6;
     const int l = threadIdx.x & 63, g = l >> 4, n16 = l & 15;
     /* the NVT value tiles of a chain run on one XCD (blockIdx % 8) and share its L2 */
@@ -337,9 +346,9 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
             }
             for (; c < nchunk; c += 2) {
                 state_step<NKB, NVT, KR>(Y, X, S, rec_of(c + 1), ubase, ring[c & 1], l, g,
-                                         kring[KLDS ? c % 3 : 0]);
+                                         kring[KLDS ? c % KDA_KRING_SLOTS : 0]);
                 state_step<NKB, NVT, KR>(X, Y, S, rec_of(c + 2), ubase, ring[(c + 1) & 1], l, g,
-                                         kring[KLDS ? (c + 1) % 3 : 0]);
+                                         kring[KLDS ? (c + 1) % KDA_KRING_SLOTS : 0]);
             }
         }
         if (fst) {
@@ -373,42 +382,40 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
             }
             for (; c < nchunk; c += 2) {
                 output_step<NKB, NVT>(Y, X, rec_of(c + 1), ubase, ring[c & 1], out, t0_of(c), len_of(c), H, h, nt,
-                                      l, g, n16, kring[KLDS ? c % 3 : 0]);
+                                      l, g, n16, kring[KLDS ? c % KDA_KRING_SLOTS : 0]);
                 output_step<NKB, NVT>(X, Y, rec_of(c + 2), ubase, ring[(c + 1) & 1], out, t0_of(c + 1),
-                                      len_of(c + 1), H, h, nt, l, g, n16, kring[KLDS ? (c + 1) % 3 : 0]);
+                                      len_of(c + 1), H, h, nt, l, g, n16, kring[KLDS ? (c + 1) % KDA_KRING_SLOTS : 0]);
             }
         }
     } else {
         /* ---------------- L2-warming wave ---------------- */
         const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)warm_sink;
         if constexpr (KLDS) {
-            /* Also copies K~^T, e^{G_L} and U of chunk c + 2 into kring[(c + 2) % 3]
-               (LDS-DMA) after barrier c, when the state wave is done with chunk
-               c - 1's slot, and waits for chunk c + 1's copy before barrier c + 1.
-               Every trip issues the same number of loads (chunk indices clamped to
-               the last), so the waits count exactly: 7 + 2 touches and 16 + 1 + 2
-               copies. The output wave reads U from the same slot, between the same
-               barriers as the state wave. */
+            /* Also copies K~^T, e^{G_L} and U of chunk c + KDA_KRING_AHEAD into its
+               ring slot (LDS-DMA) after barrier c, when the state wave is done with
+               chunk c - 1's slot, and waits for chunk c + 1's copy before barrier
+               c + 1. Every trip issues the same number of loads (chunk indices
+               clamped to the last), so the waits count exactly: 7 + 2 touches and
+               16 + 1 + 2 copies. The output wave reads U from the same slot,
+               between the same barriers as the state wave. */
             constexpr int NTOUCH = 7 + 2, NCOPY = 4 * NKB + 3;
             static_assert(NVT == 8 && (RL::U / 1024 + 1 + 7) / 8 == 7, "touch count");
+            static_assert((KDA_KRING_AHEAD - 1) * (NTOUCH + NCOPY) <= 63 && KDA_KRING_AHEAD >= 2,
+                          "the waits below count at most 63 loads");
             auto kt_copy = [&](int64_t cc) {
                 const int64_t ck = cc < nchunk ? cc : nchunk - 1;
                 const unsigned char *src = rec0 + (size_t)ck * RL::BYTES + RL::KT + l * 16;
-                const uint32_t dst = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16x8 *)kring[cc % 3];
+                const uint32_t dst =
+                    (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16x8 *)kring[cc % KDA_KRING_SLOTS];
 #pragma unroll
                 for (int i = 0; i < 4 * NKB; i++) warm_l2(src + i * 1024, dst + i * 1024);
                 warm_l2(src - RL::KT + RL::GL, dst + 4 * NKB * 1024); /* e^{G_L} and 512 bytes after it */
                 warm_l2(src - RL::KT + ubase, dst + (4 * NKB + 1) * 1024); /* this tile's U */
                 warm_l2(src - RL::KT + ubase + 1024, dst + (4 * NKB + 2) * 1024);
             };
-            if (nchunk == 0) return; /* no chunk: no barrier, nothing to copy */
-            kt_copy(0);
-            kt_copy(1);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NCOPY) : "memory"); /* chunk 0's copy has landed */
-            for (int64_t c = 0; c < nchunk; c++) {
-                asm volatile(".p2align 5\n\t.rept " KDA_STR(KDA_WARM_NOPS) "\n\ts_nop 0\n\t.endr");
-                chunk_barrier();
-                const int64_t cw = c + KDA_WARM_AHEAD < nchunk ? c + KDA_WARM_AHEAD : nchunk - 1;
+            /* this tile's share of chunk cw's record into L2, in 1 KiB pieces */
+            auto touch = [&](int64_t cw) {
+                cw = cw < nchunk ? cw : nchunk - 1;
                 const unsigned char *r = rec0 + (size_t)cw * RL::BYTES;
 #pragma unroll
                 for (int j = 0; j < 7; j++) {
@@ -417,9 +424,24 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
                 }
                 warm_l2(r + RL::U + nt * 2048 + l * 16, lds);
                 warm_l2(r + RL::U + nt * 2048 + 1024 + l * 16, lds);
-                kt_copy(c + 2);
-                /* chunk c + 1's copy (issued before this trip's touches and copy) has landed */
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NTOUCH + NCOPY) : "memory");
+            };
+            if (nchunk == 0) return; /* no chunk: no barrier, nothing to copy */
+            /* units of NTOUCH + NCOPY loads, so that KDA_KRING_AHEAD - 1 units were
+               issued after any copy when the loop waits for it */
+            kt_copy(0);
+#pragma unroll
+            for (int k = 1; k < KDA_KRING_AHEAD; k++) {
+                touch(k);
+                kt_copy(k);
+            }
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((KDA_KRING_AHEAD - 1) * (NTOUCH + NCOPY)) : "memory");
+            for (int64_t c = 0; c < nchunk; c++) {
+                asm volatile(".p2align 5\n\t.rept " KDA_STR(KDA_WARM_NOPS) "\n\ts_nop 0\n\t.endr");
+                chunk_barrier();
+                touch(c + KDA_WARM_AHEAD);
+                kt_copy(c + KDA_KRING_AHEAD);
+                /* chunk c + 1's copy has landed */
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((KDA_KRING_AHEAD - 1) * (NTOUCH + NCOPY)) : "memory");
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             return;
@@ -452,7 +474,9 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
    so two chunks of its loads fit the 63 a wave can have outstanding, and the
    kernel needs 280 registers (338 with e^{G_L} and U in registers). Long
    prefill scan 1.063 -> 1.026 ms with K~^T alone (and no longer sensitive to
-   the warming loop's code placement), 1.004 ms with e^{G_L}, 0.990 ms with U. */
+   the warming loop's code placement), 1.004 ms with e^{G_L}, 0.990 ms with U,
+   0.977 ms with four ring slots filled three chunks ahead instead of three two
+   ahead). */
 #ifndef KDA_SCAN_KLDS
 #define KDA_SCAN_KLDS true
 #endif
