@@ -395,11 +395,13 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
                ring slot (LDS-DMA) after barrier c, when the state wave is done with
                chunk c - 1's slot, and waits for chunk c + 1's copy before barrier
                c + 1. Every trip issues the same number of loads (chunk indices
-               clamped to the last), so the waits count exactly: 7 + 2 touches and
-               16 + 1 + 2 copies. The output wave reads U from the same slot,
-               between the same barriers as the state wave. */
-            constexpr int NTOUCH = 7 + 2, NCOPY = 4 * NKB + 3;
-            static_assert(NVT == 8 && (RL::U / 1024 + 1 + 7) / 8 == 7, "touch count");
+               clamped to the last), so the waits count exactly: NTJ + 2 touches
+               (7 + 2 at 128 key channels) and 4 NKB + 1 + 2 copies. The output wave
+               reads U from the same slot, between the same barriers as the state
+               wave. */
+            /* NPIECE 1 KiB pieces up to e^{G_L}, NTJ of them per tile, and its U */
+            constexpr int NPIECE = RL::U / 1024 + 1, NTJ = (NPIECE + NVT - 1) / NVT;
+            constexpr int NTOUCH = NTJ + 2, NCOPY = 4 * NKB + 3;
             static_assert((KDA_KRING_AHEAD - 1) * (NTOUCH + NCOPY) <= 63 && KDA_KRING_AHEAD >= 2,
                           "the waits below count at most 63 loads");
             auto kt_copy = [&](int64_t cc) {
@@ -418,8 +420,8 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
                 cw = cw < nchunk ? cw : nchunk - 1;
                 const unsigned char *r = rec0 + (size_t)cw * RL::BYTES;
 #pragma unroll
-                for (int j = 0; j < 7; j++) {
-                    const int i = nt + 8 * j <= RL::U / 1024 ? nt + 8 * j : RL::U / 1024;
+                for (int j = 0; j < NTJ; j++) {
+                    const int i = nt + NVT * j < NPIECE ? nt + NVT * j : NPIECE - 1;
                     warm_l2(r + i * 1024 + l * 16, lds);
                 }
                 warm_l2(r + RL::U + nt * 2048 + l * 16, lds);
@@ -496,8 +498,8 @@ kda_scan_k64_kernel(const unsigned char *__restrict__ rec_base, const int32_t *_
                     const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
                     uint16_t *__restrict__ out, const void *init_state, void *final_state, int state_fp32)
 {
-    scan_body<false, 2, 4>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state, state_fp32,
-                           nullptr, 1, 0, nullptr);
+    scan_body<false, 2, 4, true>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state,
+                                 state_fp32, nullptr, 1, 0, nullptr);
 }
 
 /* the rescan of the segment-parallel scan: workgroup (chain, segment slot, tile) */
@@ -507,8 +509,8 @@ kda_scan_seg_kernel(const unsigned char *__restrict__ rec_base, const int32_t *_
                     uint16_t *__restrict__ out, void *final_state, int state_fp32, int64_t nseg,
                     int64_t segc, const float *__restrict__ seg_init)
 {
-    scan_body<true, 4, 8>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, nullptr, final_state, state_fp32, nullptr,
-                          nseg, segc, seg_init);
+    scan_body<true, 4, 8, true>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, nullptr, final_state, state_fp32,
+                                nullptr, nseg, segc, seg_init);
 }
 
 /* ------------------------------------------------------------------------- */
