@@ -40,18 +40,23 @@
  * not track them and no wave ever waits for them, except wave 2 once before it
  * exits (its LDS must not be released with DMA writes in flight).
  */
-/* NKB = DK / 32 key blocks (W, Q', K~^T hold 4 NKB fragments each); KR: K~^T in
-   the register set (else the state wave reads it from an LDS ring) */
-template <int NKB, bool KR = true> struct ScanSetS {
-    bf16x8 W[4 * NKB], K[KR ? 4 * NKB : 1], U[KR ? 2 : 1];
-    f32x4 gl[KR ? 2 * NKB : 1]; /* e^{G_L} for key rows 16 mt + 4 g + e */
+/* NKB = DK / 32 key blocks (W, Q', K~^T hold 4 NKB fragments each). Register
+   sets of one chunk's operands: every operand of the state update (the
+   segment-map kernel); W alone (the scan's state wave, which reads K~^T, e^{G_L}
+   and U from the warming wave's LDS ring); Q' and P (the output wave, U from the
+   ring). */
+template <int NKB> struct ScanSetS {
+    bf16x8 W[4 * NKB], K[4 * NKB], U[2];
+    f32x4 gl[2 * NKB]; /* e^{G_L} for key rows 16 mt + 4 g + e */
 };
-/* UR: U in the register set (else read from the LDS ring) */
-template <int NKB, bool UR = true> struct ScanSetO {
-    bf16x8 Q[4 * NKB], P[6], U[UR ? 2 : 1];
+template <int NKB> struct ScanSetW {
+    bf16x8 W[4 * NKB];
 };
-/* KR = false: the chunk's LDS ring slot holds K~^T (4 NKB fragments), then 1 KiB
-   from e^{G_L} on, then this tile's 2 KiB of U (lane l's 32 bytes at 32 l) */
+template <int NKB> struct ScanSetO {
+    bf16x8 Q[4 * NKB], P[6];
+};
+/* A ring slot holds the chunk's K~^T (4 NKB fragments), then 1 KiB from e^{G_L}
+   on, then this tile's 2 KiB of U (lane l's 32 bytes at 32 l) */
 template <int NKB> __device__ __forceinline__ const bf16x8 *slot_gl(const bf16x8 *slot) { return slot + 4 * NKB * 64; }
 template <int NKB> __device__ __forceinline__ const bf16x8 *slot_u(const bf16x8 *slot) { return slot + 4 * NKB * 64 + 64; }
 
@@ -62,27 +67,33 @@ __device__ __forceinline__ bf16x8 bufld(__amdgpu_buffer_rsrc_t r, int voff, int 
 
 /* one chunk record (layout RecLayout<NKB, NVT>) through a buffer descriptor:
    SGPR base, lane offsets in VGPRs */
-template <int NKB, int NVT, bool KR = true>
-__device__ __forceinline__ void load_set(ScanSetS<NKB, KR> &X, const unsigned char *rec, int ubase, int l, int g)
+template <int NKB, int NVT>
+__device__ __forceinline__ void load_set(ScanSetS<NKB> &X, const unsigned char *rec, int ubase, int l, int g)
 {
     using RL = RecLayout<NKB, NVT>;
     const __amdgpu_buffer_rsrc_t r = buf_rsrc(rec, RL::BYTES);
 #pragma unroll
     for (int f = 0; f < 4 * NKB; f++) X.W[f] = bufld(r, l * 16, RL::W + f * 1024);
-    if constexpr (KR) {
-        X.U[0] = bufld(r, l * 32, ubase);
-        X.U[1] = bufld(r, l * 32, ubase + 16);
+    X.U[0] = bufld(r, l * 32, ubase);
+    X.U[1] = bufld(r, l * 32, ubase + 16);
 #pragma unroll
-        for (int mt = 0; mt < 2 * NKB; mt++)
-            X.gl[mt] =
-                __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, g * 16, RL::GL + mt * 64, 0));
+    for (int mt = 0; mt < 2 * NKB; mt++)
+        X.gl[mt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, g * 16, RL::GL + mt * 64, 0));
 #pragma unroll
-        for (int f = 0; f < 4 * NKB; f++) X.K[f] = bufld(r, l * 16, RL::KT + f * 1024);
-    }
+    for (int f = 0; f < 4 * NKB; f++) X.K[f] = bufld(r, l * 16, RL::KT + f * 1024);
 }
 
-template <int NKB, int NVT, bool UR>
-__device__ __forceinline__ void load_set(ScanSetO<NKB, UR> &X, const unsigned char *rec, int ubase, int l, int g)
+template <int NKB, int NVT>
+__device__ __forceinline__ void load_set(ScanSetW<NKB> &X, const unsigned char *rec, int l)
+{
+    using RL = RecLayout<NKB, NVT>;
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(rec, RL::BYTES);
+#pragma unroll
+    for (int f = 0; f < 4 * NKB; f++) X.W[f] = bufld(r, l * 16, RL::W + f * 1024);
+}
+
+template <int NKB, int NVT>
+__device__ __forceinline__ void load_set(ScanSetO<NKB> &X, const unsigned char *rec, int l)
 {
     using RL = RecLayout<NKB, NVT>;
     const __amdgpu_buffer_rsrc_t r = buf_rsrc(rec, RL::BYTES);
@@ -90,10 +101,6 @@ __device__ __forceinline__ void load_set(ScanSetO<NKB, UR> &X, const unsigned ch
     for (int f = 0; f < 4 * NKB; f++) X.Q[f] = bufld(r, l * 16, RL::Q + f * 1024);
 #pragma unroll
     for (int f = 0; f < 6; f++) X.P[f] = bufld(r, l * 16, RL::P + f * 1024);
-    if constexpr (UR) {
-        X.U[0] = bufld(r, l * 32, ubase);
-        X.U[1] = bufld(r, l * 32, ubase + 16);
-    }
 }
 
 __device__ __forceinline__ void chunk_barrier()
@@ -103,13 +110,14 @@ __device__ __forceinline__ void chunk_barrier()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-/* state wave: X holds chunk c; loads chunk c + 1 (at nrec) into Y */
-template <int NKB, int NVT, bool KR = true>
-__device__ __forceinline__ void state_step(ScanSetS<NKB, KR> &X, ScanSetS<NKB, KR> &Y, f32x4 (&S)[2 * NKB],
-                                           const unsigned char *nrec, int ubase, bf16x8 *slot, int l, int g,
-                                           const bf16x8 *kt_lds = nullptr)
+/* state wave: X holds chunk c's W, kt_lds is chunk c's ring slot; loads chunk
+   c + 1's W (at nrec) into Y */
+template <int NKB, int NVT>
+__device__ __forceinline__ void state_step(ScanSetW<NKB> &X, ScanSetW<NKB> &Y, f32x4 (&S)[2 * NKB],
+                                           const unsigned char *nrec, bf16x8 *slot, int l, int g,
+                                           const bf16x8 *kt_lds)
 {
-    load_set<NKB, NVT, KR>(Y, nrec, ubase, l, g);
+    load_set<NKB, NVT>(Y, nrec, l);
     bf16x8 sb[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; kb++) {
@@ -120,10 +128,7 @@ __device__ __forceinline__ void state_step(ScanSetS<NKB, KR> &X, ScanSetS<NKB, K
     f32x4 D[4];
     bf16x8 uu[2];
 #pragma unroll
-    for (int jb = 0; jb < 2; jb++) {
-        if constexpr (KR) uu[jb] = X.U[jb];
-        else uu[jb] = slot_u<NKB>(kt_lds)[2 * l + jb];
-    }
+    for (int jb = 0; jb < 2; jb++) uu[jb] = slot_u<NKB>(kt_lds)[2 * l + jb];
 #pragma unroll
     for (int mt = 0; mt < 4; mt++) {
         const int o = (mt & 1) * 4;
@@ -137,42 +142,32 @@ __device__ __forceinline__ void state_step(ScanSetS<NKB, KR> &X, ScanSetS<NKB, K
         for (int mt = 0; mt < 4; mt++) D[mt] = mfma(X.W[mt * NKB + kb], sb[kb], D[mt]);
     /* S <- diag(e^{G_L}) S + K~^T D (e^{G_L} after K~^T in the LDS slot, key-channel order) */
 #pragma unroll
-    for (int mt = 0; mt < 2 * NKB; mt++) {
-        if constexpr (KR) S[mt] *= X.gl[mt];
-        else S[mt] *= ((const f32x4 *)slot_gl<NKB>(kt_lds))[4 * mt + g];
-    }
+    for (int mt = 0; mt < 2 * NKB; mt++) S[mt] *= ((const f32x4 *)slot_gl<NKB>(kt_lds))[4 * mt + g];
     bf16x8 db[2];
     db[0] = pack8(D[0], D[1]);
     db[1] = pack8(D[2], D[3]);
-    if constexpr (KR) {
+    /* K~^T from the chunk's LDS slot, 2 NKB fragments at a time */
 #pragma unroll
-        for (int jb = 0; jb < 2; jb++)
+    for (int jb = 0; jb < 2; jb++) {
+        bf16x8 kf[2 * NKB];
 #pragma unroll
-            for (int mt = 0; mt < 2 * NKB; mt++) S[mt] = mfma(X.K[mt * 2 + jb], db[jb], S[mt]);
-    } else {
-        /* K~^T from the chunk's LDS slot, 2 NKB fragments at a time */
+        for (int mt = 0; mt < 2 * NKB; mt++) kf[mt] = kt_lds[(mt * 2 + jb) * 64 + l];
 #pragma unroll
-        for (int jb = 0; jb < 2; jb++) {
-            bf16x8 kf[2 * NKB];
-#pragma unroll
-            for (int mt = 0; mt < 2 * NKB; mt++) kf[mt] = kt_lds[(mt * 2 + jb) * 64 + l];
-#pragma unroll
-            for (int mt = 0; mt < 2 * NKB; mt++) S[mt] = mfma(kf[mt], db[jb], S[mt]);
-        }
+        for (int mt = 0; mt < 2 * NKB; mt++) S[mt] = mfma(kf[mt], db[jb], S[mt]);
     }
 }
 
-/* output wave: X holds chunk c (tokens t0 .. t0 + L - 1); loads chunk c + 1 into Y.
-   out is written through a buffer descriptor bounded at row L - 1: rows past
-   the sequence end fall outside it and the hardware drops their stores. */
-template <int NKB, int NVT, bool UR = true>
-__device__ __forceinline__ void output_step(ScanSetO<NKB, UR> &X, ScanSetO<NKB, UR> &Y, const unsigned char *nrec,
-                                            int ubase, const bf16x8 *slot, uint16_t *out, int64_t t0, int L,
-                                            int H, int h, int nt, int l, int g, int n16,
-                                            const bf16x8 *kslot = nullptr)
+/* output wave: X holds chunk c's Q' and P (tokens t0 .. t0 + L - 1), kslot is its
+   ring slot (U), slot the entering state; loads chunk c + 1 into Y. out is written
+   through a buffer descriptor bounded at row L - 1: rows past the sequence end
+   fall outside it and the hardware drops their stores. */
+template <int NKB, int NVT>
+__device__ __forceinline__ void output_step(ScanSetO<NKB> &X, ScanSetO<NKB> &Y, const unsigned char *nrec,
+                                            const bf16x8 *slot, uint16_t *out, int64_t t0, int L, int H, int h,
+                                            int nt, int l, int g, int n16, const bf16x8 *kslot)
 {
     constexpr int DV = 16 * NVT;
-    load_set<NKB, NVT>(Y, nrec, ubase, l, g);
+    load_set<NKB, NVT>(Y, nrec, l);
     chunk_barrier();
     bf16x8 sb[NKB];
 #pragma unroll
@@ -187,10 +182,7 @@ __device__ __forceinline__ void output_step(ScanSetO<NKB, UR> &X, ScanSetO<NKB, 
         for (int mt = 0; mt < 4; mt++) O[mt] = mfma(sb[kb], X.Q[mt * NKB + kb], O[mt]);
     bf16x8 uu[2];
 #pragma unroll
-    for (int jb = 0; jb < 2; jb++) {
-        if constexpr (UR) uu[jb] = X.U[jb];
-        else uu[jb] = slot_u<NKB>(kslot)[2 * l + jb];
-    }
+    for (int jb = 0; jb < 2; jb++) uu[jb] = slot_u<NKB>(kslot)[2 * l + jb];
 #pragma unroll
     for (int mt = 0; mt < 4; mt++)
 #pragma unroll
@@ -238,7 +230,7 @@ __device__ __forceinline__ void warm_l2(const unsigned char *p, uint32_t lds_add
    (record layout RecLayout<NKB, NVT>); SEG instantiates the segment-parallel
    rescan (one workgroup per (chain, segment, tile)), which the plain kernel
    compiles without */
-template <bool SEG, int NKB, int NVT, bool KLDS = false>
+template <bool SEG, int NKB, int NVT>
 __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
                                           const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H,
                                           int64_t nslots, uint16_t *__restrict__ out,
@@ -251,11 +243,10 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     static_assert((NVT & (NVT - 1)) == 0, "value tiles: a power of two");
     __shared__ bf16x8 ring[2][NKB * 64];                        /* S(c) in bf16 (8 KiB at DK = 128) */
     __shared__ __attribute__((aligned(16))) unsigned char warm_sink[1024];
-    /* KLDS: K~^T of chunk c, 1 KiB from e^{G_L} on and this tile's U in
+    /* the ring: K~^T of chunk c, 1 KiB from e^{G_L} on and this tile's U in
        kring[c % KDA_KRING_SLOTS] (slot_gl, slot_u), copied by the warming wave
        KDA_KRING_AHEAD chunks ahead */
-    __shared__ __attribute__((aligned(16)))
-    bf16x8 kring[KLDS ? KDA_KRING_SLOTS : 1][KLDS ? 4 * NKB * 64 + 64 + 128 : 1];
+    __shared__ __attribute__((aligned(16))) bf16x8 kring[KDA_KRING_SLOTS][4 * NKB * 64 + 64 + 128];
     const int wave = threadIdx.x >> 6;
     const int l = threadIdx.x & 63, g = l >> 4, n16 = l & 15;
     /* the NVT value tiles of a chain run on one XCD (blockIdx % 8) and share its L2 */
@@ -334,21 +325,19 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
             }
         }
         if (nchunk > 0) {
-            constexpr bool KR = !KLDS;
-            ScanSetS<NKB, KR> X, Y;
+            ScanSetW<NKB> X, Y;
             int64_t c = 0;
             if (nchunk & 1) {
-                load_set<NKB, NVT, KR>(X, rec_of(0), ubase, l, g);
-                state_step<NKB, NVT, KR>(X, Y, S, rec_of(1), ubase, ring[0], l, g, kring[0]);
+                load_set<NKB, NVT>(X, rec_of(0), l);
+                state_step<NKB, NVT>(X, Y, S, rec_of(1), ring[0], l, g, kring[0]);
                 c = 1;
             } else {
-                load_set<NKB, NVT, KR>(Y, rec_of(0), ubase, l, g);
+                load_set<NKB, NVT>(Y, rec_of(0), l);
             }
             for (; c < nchunk; c += 2) {
-                state_step<NKB, NVT, KR>(Y, X, S, rec_of(c + 1), ubase, ring[c & 1], l, g,
-                                         kring[KLDS ? c % KDA_KRING_SLOTS : 0]);
-                state_step<NKB, NVT, KR>(X, Y, S, rec_of(c + 2), ubase, ring[(c + 1) & 1], l, g,
-                                         kring[KLDS ? (c + 1) % KDA_KRING_SLOTS : 0]);
+                state_step<NKB, NVT>(Y, X, S, rec_of(c + 1), ring[c & 1], l, g, kring[c % KDA_KRING_SLOTS]);
+                state_step<NKB, NVT>(X, Y, S, rec_of(c + 2), ring[(c + 1) & 1], l, g,
+                                     kring[(c + 1) % KDA_KRING_SLOTS]);
             }
         }
         if (fst) {
@@ -365,7 +354,7 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
     } else if (wave == 1) {
         /* ---------------- output wave ---------------- */
         if (nchunk > 0) {
-            ScanSetO<NKB, !KLDS> X, Y;
+            ScanSetO<NKB> X, Y;
             int64_t c = 0;
             auto t0_of = [&](int64_t cc) { return bos + cc * KDA_CHUNK; };
             auto len_of = [&](int64_t cc) {
@@ -373,123 +362,97 @@ __device__ __forceinline__ void scan_body(const unsigned char *__restrict__ rec_
                 return (int)(rem < KDA_CHUNK ? rem : KDA_CHUNK);
             };
             if (nchunk & 1) {
-                load_set<NKB, NVT>(X, rec_of(0), ubase, l, g);
-                output_step<NKB, NVT>(X, Y, rec_of(1), ubase, ring[0], out, t0_of(0), len_of(0), H, h, nt, l, g,
-                                      n16, kring[0]);
+                load_set<NKB, NVT>(X, rec_of(0), l);
+                output_step<NKB, NVT>(X, Y, rec_of(1), ring[0], out, t0_of(0), len_of(0), H, h, nt, l, g, n16,
+                                      kring[0]);
                 c = 1;
             } else {
-                load_set<NKB, NVT>(Y, rec_of(0), ubase, l, g);
+                load_set<NKB, NVT>(Y, rec_of(0), l);
             }
             for (; c < nchunk; c += 2) {
-                output_step<NKB, NVT>(Y, X, rec_of(c + 1), ubase, ring[c & 1], out, t0_of(c), len_of(c), H, h, nt,
-                                      l, g, n16, kring[KLDS ? c % KDA_KRING_SLOTS : 0]);
-                output_step<NKB, NVT>(X, Y, rec_of(c + 2), ubase, ring[(c + 1) & 1], out, t0_of(c + 1),
-                                      len_of(c + 1), H, h, nt, l, g, n16, kring[KLDS ? (c + 1) % KDA_KRING_SLOTS : 0]);
+                output_step<NKB, NVT>(Y, X, rec_of(c + 1), ring[c & 1], out, t0_of(c), len_of(c), H, h, nt, l, g,
+                                      n16, kring[c % KDA_KRING_SLOTS]);
+                output_step<NKB, NVT>(X, Y, rec_of(c + 2), ring[(c + 1) & 1], out, t0_of(c + 1), len_of(c + 1), H,
+                                      h, nt, l, g, n16, kring[(c + 1) % KDA_KRING_SLOTS]);
             }
         }
     } else {
         /* ---------------- L2-warming wave ---------------- */
         const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)warm_sink;
-        if constexpr (KLDS) {
-            /* Also copies K~^T, e^{G_L} and U of chunk c + KDA_KRING_AHEAD into its
-               ring slot (LDS-DMA) after barrier c, when the state wave is done with
-               chunk c - 1's slot, and waits for chunk c + 1's copy before barrier
-               c + 1. Every trip issues the same number of loads (chunk indices
-               clamped to the last), so the waits count exactly: NTJ + 2 touches
-               (7 + 2 at 128 key channels) and 4 NKB + 1 + 2 copies. The output wave
-               reads U from the same slot, between the same barriers as the state
-               wave. */
-            /* NPIECE 1 KiB pieces up to e^{G_L}, NTJ of them per tile, and its U */
-            constexpr int NPIECE = RL::U / 1024 + 1, NTJ = (NPIECE + NVT - 1) / NVT;
-            constexpr int NTOUCH = NTJ + 2, NCOPY = 4 * NKB + 3;
-            static_assert((KDA_KRING_AHEAD - 1) * (NTOUCH + NCOPY) <= 63 && KDA_KRING_AHEAD >= 2,
-                          "the waits below count at most 63 loads");
-            auto kt_copy = [&](int64_t cc) {
-                const int64_t ck = cc < nchunk ? cc : nchunk - 1;
-                const unsigned char *src = rec0 + (size_t)ck * RL::BYTES + RL::KT + l * 16;
-                const uint32_t dst =
-                    (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16x8 *)kring[cc % KDA_KRING_SLOTS];
+        /* After barrier c: touches this tile's share of chunk c + KDA_WARM_AHEAD's
+           record into L2 and copies K~^T, e^{G_L} and U of chunk c +
+           KDA_KRING_AHEAD into its ring slot (LDS-DMA), the state wave being done
+           with chunk c - 1's slot; then waits for chunk c + 1's copy before
+           barrier c + 1. Every trip issues the same number of loads (chunk indices
+           clamped to the last), so the waits count exactly: NTJ + 2 touches
+           (7 + 2 at 128 key channels) and 4 NKB + 1 + 2 copies. The output wave
+           reads U from the same slot, between the same barriers as the state
+           wave. */
+        /* NPIECE 1 KiB pieces up to e^{G_L}, NTJ of them per tile, and its U */
+        constexpr int NPIECE = RL::U / 1024 + 1, NTJ = (NPIECE + NVT - 1) / NVT;
+        constexpr int NTOUCH = NTJ + 2, NCOPY = 4 * NKB + 3;
+        static_assert((KDA_KRING_AHEAD - 1) * (NTOUCH + NCOPY) <= 63 && KDA_KRING_AHEAD >= 2,
+                      "the waits below count at most 63 loads");
+        auto kt_copy = [&](int64_t cc) {
+            const int64_t ck = cc < nchunk ? cc : nchunk - 1;
+            const unsigned char *src = rec0 + (size_t)ck * RL::BYTES + RL::KT + l * 16;
+            const uint32_t dst =
+                (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16x8 *)kring[cc % KDA_KRING_SLOTS];
 #pragma unroll
-                for (int i = 0; i < 4 * NKB; i++) warm_l2(src + i * 1024, dst + i * 1024);
-                warm_l2(src - RL::KT + RL::GL, dst + 4 * NKB * 1024); /* e^{G_L} and 512 bytes after it */
-                warm_l2(src - RL::KT + ubase, dst + (4 * NKB + 1) * 1024); /* this tile's U */
-                warm_l2(src - RL::KT + ubase + 1024, dst + (4 * NKB + 2) * 1024);
-            };
-            /* this tile's share of chunk cw's record into L2, in 1 KiB pieces */
-            auto touch = [&](int64_t cw) {
-                cw = cw < nchunk ? cw : nchunk - 1;
-                const unsigned char *r = rec0 + (size_t)cw * RL::BYTES;
+            for (int i = 0; i < 4 * NKB; i++) warm_l2(src + i * 1024, dst + i * 1024);
+            warm_l2(src - RL::KT + RL::GL, dst + 4 * NKB * 1024); /* e^{G_L} and 512 bytes after it */
+            warm_l2(src - RL::KT + ubase, dst + (4 * NKB + 1) * 1024); /* this tile's U */
+            warm_l2(src - RL::KT + ubase + 1024, dst + (4 * NKB + 2) * 1024);
+        };
+        /* this tile's share of chunk cw's record into L2, in 1 KiB pieces */
+        auto touch = [&](int64_t cw) {
+            cw = cw < nchunk ? cw : nchunk - 1;
+            const unsigned char *r = rec0 + (size_t)cw * RL::BYTES;
 #pragma unroll
-                for (int j = 0; j < NTJ; j++) {
-                    const int i = nt + NVT * j < NPIECE ? nt + NVT * j : NPIECE - 1;
-                    warm_l2(r + i * 1024 + l * 16, lds);
-                }
-                warm_l2(r + RL::U + nt * 2048 + l * 16, lds);
-                warm_l2(r + RL::U + nt * 2048 + 1024 + l * 16, lds);
-            };
-            if (nchunk == 0) return; /* no chunk: no barrier, nothing to copy */
-            /* units of NTOUCH + NCOPY loads, so that KDA_KRING_AHEAD - 1 units were
-               issued after any copy when the loop waits for it */
-            kt_copy(0);
-#pragma unroll
-            for (int k = 1; k < KDA_KRING_AHEAD; k++) {
-                touch(k);
-                kt_copy(k);
+            for (int j = 0; j < NTJ; j++) {
+                const int i = nt + NVT * j < NPIECE ? nt + NVT * j : NPIECE - 1;
+                warm_l2(r + i * 1024 + l * 16, lds);
             }
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((KDA_KRING_AHEAD - 1) * (NTOUCH + NCOPY)) : "memory");
-            for (int64_t c = 0; c < nchunk; c++) {
-                asm volatile(".p2align 5\n\t.rept " KDA_STR(KDA_WARM_NOPS) "\n\ts_nop 0\n\t.endr");
-                chunk_barrier();
-                touch(c + KDA_WARM_AHEAD);
-                kt_copy(c + KDA_KRING_AHEAD);
-                /* chunk c + 1's copy has landed */
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"((KDA_KRING_AHEAD - 1) * (NTOUCH + NCOPY)) : "memory");
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            return;
+            warm_l2(r + RL::U + nt * 2048 + l * 16, lds);
+            warm_l2(r + RL::U + nt * 2048 + 1024 + l * 16, lds);
+        };
+        if (nchunk == 0) return; /* no chunk: no barrier, nothing to copy */
+        /* units of NTOUCH + NCOPY loads, so that KDA_KRING_AHEAD - 1 units were
+           issued after any copy when the loop waits for it */
+        kt_copy(0);
+#pragma unroll
+        for (int k = 1; k < KDA_KRING_AHEAD; k++) {
+            touch(k);
+            kt_copy(k);
         }
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((KDA_KRING_AHEAD - 1) * (NTOUCH + NCOPY)) : "memory");
         for (int64_t c = 0; c < nchunk; c++) {
-            /* Code placement: the chunk time of the whole workgroup was measured
-               to depend on where this loop sits relative to 32-byte instruction
-               fetch blocks (1.035 to 1.112 ms per long-prefill launch over the
-               eight offsets; the other two loops showed no such effect). The
-               loop is pinned to a 32-byte boundary plus two s_nop, the fastest
-               offset; an edit of this loop needs the offset measured again. */
-            asm volatile(".p2align 5\n\ts_nop 0\n\ts_nop 0");
-            const int64_t cw = c + KDA_WARM_AHEAD;
-            if (cw < nchunk) {
-                const unsigned char *r = rec0 + (size_t)cw * RL::BYTES;
-                /* this tile's share of the shared operands, 1 KiB pieces */
-                for (int i = nt; i < RL::U / 1024 + 1; i += NVT) warm_l2(r + i * 1024 + l * 16, lds);
-                /* and its own 2 KiB of U */
-                warm_l2(r + RL::U + nt * 2048 + l * 16, lds);
-                warm_l2(r + RL::U + nt * 2048 + 1024 + l * 16, lds);
-            }
+            asm volatile(".p2align 5\n\t.rept " KDA_STR(KDA_WARM_NOPS) "\n\ts_nop 0\n\t.endr");
             chunk_barrier();
+            touch(c + KDA_WARM_AHEAD);
+            kt_copy(c + KDA_KRING_AHEAD);
+            /* chunk c + 1's copy has landed */
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"((KDA_KRING_AHEAD - 1) * (NTOUCH + NCOPY)) : "memory");
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 }
 
-/* K~^T, e^{G_L} and U through the warming wave's LDS ring in the plain
-   128-channel scan: the state wave then issues 16 loads per chunk instead of 42,
-   so two chunks of its loads fit the 63 a wave can have outstanding, and the
-   kernel needs 280 registers (338 with e^{G_L} and U in registers). Long
-   prefill scan 1.063 -> 1.026 ms with K~^T alone (and no longer sensitive to
-   the warming loop's code placement), 1.004 ms with e^{G_L}, 0.990 ms with U,
-   0.977 ms with four ring slots filled three chunks ahead instead of three two
-   ahead). */
-#ifndef KDA_SCAN_KLDS
-#define KDA_SCAN_KLDS true
-#endif
+/* K~^T, e^{G_L} and U through the warming wave's LDS ring: the state wave then
+   issues 16 loads per chunk instead of 42, so two chunks of its loads fit the 63
+   a wave can have outstanding, and the kernel needs 280 registers (338 with
+   e^{G_L} and U in registers). Long prefill scan 1.063 -> 1.026 ms with K~^T
+   alone (and no longer sensitive to the warming loop's code placement), 1.004 ms
+   with e^{G_L}, 0.990 ms with U, 0.977 ms with four ring slots filled three
+   chunks ahead instead of three two ahead. */
 extern "C" __global__ void __launch_bounds__(192)
 kda_scan_kernel(const unsigned char *__restrict__ rec_base, const int32_t *__restrict__ cu,
                 const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
                 uint16_t *__restrict__ out, const void *init_state,
                 void *final_state, int state_fp32, const int32_t *__restrict__ long_list)
 {
-    scan_body<false, 4, 8, KDA_SCAN_KLDS>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state,
-                                          state_fp32, long_list, 1, 0, nullptr);
+    scan_body<false, 4, 8>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state, state_fp32,
+                           long_list, 1, 0, nullptr);
 }
 
 /* K = V = 64: four value tiles per chain */
@@ -498,8 +461,8 @@ kda_scan_k64_kernel(const unsigned char *__restrict__ rec_base, const int32_t *_
                     const int32_t *__restrict__ chunk_off, int64_t nseq, int64_t T, int H, int64_t nslots,
                     uint16_t *__restrict__ out, const void *init_state, void *final_state, int state_fp32)
 {
-    scan_body<false, 2, 4, true>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state,
-                                 state_fp32, nullptr, 1, 0, nullptr);
+    scan_body<false, 2, 4>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, init_state, final_state, state_fp32,
+                           nullptr, 1, 0, nullptr);
 }
 
 /* the rescan of the segment-parallel scan: workgroup (chain, segment slot, tile) */
@@ -509,8 +472,8 @@ kda_scan_seg_kernel(const unsigned char *__restrict__ rec_base, const int32_t *_
                     uint16_t *__restrict__ out, void *final_state, int state_fp32, int64_t nseg,
                     int64_t segc, const float *__restrict__ seg_init)
 {
-    scan_body<true, 4, 8, true>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, nullptr, final_state, state_fp32,
-                                nullptr, nseg, segc, seg_init);
+    scan_body<true, 4, 8>(rec_base, cu, chunk_off, nseq, T, H, nslots, out, nullptr, final_state, state_fp32, nullptr,
+                          nseg, segc, seg_init);
 }
 
 /* ------------------------------------------------------------------------- */
