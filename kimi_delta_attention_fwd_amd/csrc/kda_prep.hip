@@ -106,6 +106,30 @@ template <int NKB, int NVB> struct PrepShared {
    nonzero */
 __device__ __forceinline__ int kda_tbt_idx(int jt, int jb) { return jt < 2 ? 2 * jt + jb : 2 + jt; }
 
+/* lane N of each 16-lane row of the wave, to the whole row (DPP row_newbcast) */
+template <int N> __device__ __forceinline__ float row_bcast(float x)
+{
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xf, 0xf, false));
+}
+
+/* wide form's diagonal block: this lane's partial sums over its channels against
+   partner token JJ .. 15 of its row (lane 16 g + JJ holds the partner's values of
+   the same channels), the decay exp2 of a clamped log2 difference */
+template <int JJ> struct WidePartners {
+    static __device__ __forceinline__ void add(float kh, float qh, float c, float (&sa)[16], float (&sp)[16])
+    {
+        const float kp = row_bcast<JJ>(kh), cp = row_bcast<JJ>(c);
+        const float t = kp * exp2_fast(fminf(c - cp, 0.f));
+        sa[JJ] += kh * t;
+        sp[JJ] += qh * t;
+        WidePartners<JJ + 1>::add(kh, qh, c, sa, sp);
+    }
+};
+template <> struct WidePartners<16> {
+    static __device__ __forceinline__ void add(float, float, float, float (&)[16], float (&)[16]) {}
+};
+
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -365,17 +389,7 @@ __device__ __forceinline__ void prep_body(const uint16_t *q, const uint16_t *k, 
 #pragma unroll
             for (int jj = 0; jj < 16; jj++) { sa[jj] = 0.f; sp[jj] = 0.f; }
 #pragma unroll
-            for (int j = 0; j < NE; j++) {
-                const float kh = kf[j] * ik, qh = qf[j] * iq, c = la[j];
-#pragma unroll
-                for (int jj = 0; jj < 16; jj++) {
-                    const int src = (l & 48) | jj;
-                    const float kp = __shfl(kh, src), cp = __shfl(c, src);
-                    const float t = kp * exp2_fast(fminf(c - cp, 0.f));
-                    sa[jj] += kh * t;
-                    sp[jj] += qh * t;
-                }
-            }
+            for (int j = 0; j < NE; j++) WidePartners<0>::add(kf[j] * ik, qf[j] * iq, la[j], sa, sp);
 #pragma unroll
             for (int jj = 0; jj < 16; jj++) {
                 sa[jj] += __shfl_xor(sa[jj], 16);
